@@ -1,0 +1,232 @@
+"""Seeded synthetic inputs for the fused KV-cache step.
+
+This module draws random tensors and index sets only; it holds none of the
+step's arithmetic (no projection, rotary, scatter or attention), so both the
+HIP path and the CPU oracle can be fed from it.
+
+The shapes follow the workloads the Flash-dLLM pages describe: a draft pass
+whose query set is the tracked rows plus the front masked positions (jaehun.me
+review, "Flash-Verify" and "How It Works: A Concrete Example"), and a
+verification pass laid out as [tracked | confident | draft view | mask view]
+where the two views share positions (same sections, Fig. 2).  The pages
+measure LLaDA-1.5 on public benchmarks; no weights or data are used here, the
+seeded tensors below stand in for them.
+
+All tensors are created on the CPU with a seeded ``torch.Generator`` in fp32
+and cast once (round to nearest even) to the layer's storage dtype.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Optional
+
+import torch
+
+
+@dataclass(frozen=True)
+class LayerShape:
+    B: int
+    N: int
+    d_model: int
+    H: int
+    Hkv: int
+    dh: int
+    rope_base: float = 10000.0
+    dtype: torch.dtype = torch.bfloat16
+
+    @property
+    def cols(self) -> int:
+        return (self.H + 2 * self.Hkv) * self.dh
+
+
+@dataclass
+class Workload:
+    name: str
+    shape: LayerShape
+    nq: int
+    x_rows: int
+    seed: int
+    X_pre: torch.Tensor          # [B, N, d]: hidden states the cache is built from
+    X: torch.Tensor              # [B, x_rows, d]: hidden states of this step
+    W: torch.Tensor              # [(H + 2 Hkv) dh, d]
+    Q_idx: torch.Tensor          # [B, nq] int32: X row of each query
+    pos_ids: torch.Tensor        # [B, nq] int32: position of each query
+    vis: Optional[torch.Tensor]  # [B, nq, nq] uint8 or None (all visible)
+    meta: dict = field(default_factory=dict)
+
+
+SHAPES = {
+    1: LayerShape(B=1, N=64, d_model=128, H=4, Hkv=4, dh=32, dtype=torch.float32),
+    2: LayerShape(B=1, N=1024, d_model=4096, H=32, Hkv=32, dh=128),
+    3: LayerShape(B=8, N=2048, d_model=4096, H=32, Hkv=32, dh=128),
+    4: LayerShape(B=4, N=8192, d_model=3584, H=28, Hkv=4, dh=128),
+    5: LayerShape(B=64, N=2048, d_model=4096, H=32, Hkv=8, dh=128),
+}
+
+NAMES = {
+    1: "tiny fp32 layer B=1 N=64 d=128 H=Hkv=4 dh=32 |Q|=4",
+    2: "8B-class layer draft pass B=1 N=1024 d=4096 H=Hkv=32 dh=128 |Q|=33",
+    3: "8B-class layer Flash-Verify pass B=8 N=2048 d=4096 H=Hkv=32 dh=128 |Q|=44",
+    4: "long-context GQA layer B=4 N=8192 d=3584 H=28 Hkv=4 dh=128 |Q|=32",
+    5: "large-batch GQA layer B=64 N=2048 d=4096 H=32 Hkv=8 dh=128 |Q|=16",
+}
+
+BASE_SEED = 20260
+
+
+def _randn(g, shape, std, dtype):
+    return (torch.randn(shape, generator=g, dtype=torch.float32) * std).to(dtype)
+
+
+def _randint(g, lo, hi_incl):
+    return int(torch.randint(lo, hi_incl + 1, (1,), generator=g).item())
+
+
+def _perm(g, n):
+    return torch.randperm(n, generator=g).tolist()
+
+
+def hidden_and_weights(shape: LayerShape, x_rows: int, g: torch.Generator, w_std: float = 0.02):
+    X_pre = _randn(g, (shape.B, shape.N, shape.d_model), 1.0, shape.dtype)
+    W = _randn(g, (shape.cols, shape.d_model), w_std, shape.dtype)
+    return X_pre, W
+
+
+def step_hidden(shape: LayerShape, X_pre, Q_idx, x_rows, g):
+    """Hidden states of the step: the prefill states with the query rows (and
+    any rows past N) redrawn, so that the step's cache writes are observable."""
+    B, N, d = X_pre.shape
+    X = torch.empty((B, x_rows, d), dtype=shape.dtype)
+    X[:, :N] = X_pre
+    if x_rows > N:
+        X[:, N:] = _randn(g, (B, x_rows - N, d), 1.0, shape.dtype)
+    for b in range(B):
+        rows = sorted(set(int(r) for r in Q_idx[b].tolist() if r < N))
+        if rows:
+            X[b, rows] = _randn(g, (len(rows), d), 1.0, shape.dtype)
+    return X
+
+
+def view_block_mask(groups: List[List[str]]) -> torch.Tensor:
+    """[B, nq, nq] uint8: zero exactly on the draft-view x mask-view pairs."""
+    B, nq = len(groups), len(groups[0])
+    vis = torch.ones((B, nq, nq), dtype=torch.uint8)
+    for b in range(B):
+        gr = groups[b]
+        d_rows = [i for i, t in enumerate(gr) if t == "draft"]
+        m_rows = [i for i, t in enumerate(gr) if t == "mask"]
+        for i in d_rows:
+            for j in m_rows:
+                vis[b, i, j] = 0
+                vis[b, j, i] = 0
+    return vis
+
+
+def make_workload(cid: int, layer: int = 0, w_std: float = 0.02) -> Workload:
+    """The five layer configurations, seeded with 20260 + id (+1000 per layer)."""
+    shape = SHAPES[cid]
+    seed = BASE_SEED + cid + 1000 * layer
+    g = torch.Generator().manual_seed(seed)
+    B, N = shape.B, shape.N
+    meta = {}
+    vis = None
+    if cid == 1:
+        nq, x_rows = 4, N
+        Q = torch.tensor([[33, 34, 35, 36]], dtype=torch.int32)
+        P = Q.clone()
+    elif cid == 2:
+        nq, x_rows = 33, N
+        L = _randint(g, 512, 992)
+        t = _randint(g, 0, L - 1)
+        Q = torch.tensor([[t] + list(range(L, L + 32))], dtype=torch.int32)
+        P = Q.clone()
+        meta["decoded_prefix"] = [L]
+    elif cid == 3:
+        n_t, n_d, n_s = 4, 8, 16
+        nq = n_t + n_d + 2 * n_s
+        x_rows = N + n_s
+        prompt, gen = N // 2, N - N // 2
+        Qs, Ps, groups = [], [], []
+        for b in range(B):
+            r = float(torch.empty(1).uniform_(0.2, 0.8, generator=g).item())
+            n_mask = max(n_d + n_s, int(round(r * gen)))
+            first_mask = N - n_mask
+            tv = sorted(_perm(g, first_mask)[:n_t])
+            front = list(range(first_mask, first_mask + n_d + n_s))
+            order = _perm(g, n_d + n_s)
+            Dset = sorted(front[i] for i in order[:n_d])
+            Sset = sorted(front[i] for i in order[n_d:])
+            q_idx = tv + Dset + Sset + [N + k for k in range(n_s)]
+            pos = tv + Dset + Sset + Sset
+            Qs.append(q_idx)
+            Ps.append(pos)
+            groups.append(["track"] * n_t + ["confident"] * n_d + ["draft"] * n_s + ["mask"] * n_s)
+            meta.setdefault("masked_from", []).append(first_mask)
+        Q = torch.tensor(Qs, dtype=torch.int32)
+        P = torch.tensor(Ps, dtype=torch.int32)
+        vis = view_block_mask(groups)
+        meta["groups"] = groups
+    elif cid == 4:
+        nq, x_rows = 32, N
+        Ls = [_randint(g, 2048, 7000) for _ in range(B)]
+        Q = torch.tensor([list(range(L, L + nq)) for L in Ls], dtype=torch.int32)
+        P = Q.clone()
+        meta["decoded_prefix"] = Ls
+    elif cid == 5:
+        nq, x_rows = 16, N
+        # the query sets are shared by every layer of the stack
+        gq = torch.Generator().manual_seed(BASE_SEED + cid)
+        Ls = [_randint(gq, 512, 2000) for _ in range(B)]
+        Q = torch.tensor([list(range(L, L + nq)) for L in Ls], dtype=torch.int32)
+        P = Q.clone()
+        meta["decoded_prefix"] = Ls
+    else:
+        raise ValueError("unknown configuration %r" % cid)
+    X_pre, W = hidden_and_weights(shape, x_rows, g, w_std)
+    X = step_hidden(shape, X_pre, Q, x_rows, g)
+    return Workload(NAMES[cid], shape, nq, x_rows, seed, X_pre, X, W, Q.contiguous(),
+                    P.contiguous(), vis, meta)
+
+
+def make_random_case(shape: LayerShape, nq: int, seed: int, *, n_extra_rows: int = 0,
+                     dup_frac: float = 0.0, masked_vis: bool = False, w_std: float = 0.02,
+                     positions: Optional[List[List[int]]] = None) -> Workload:
+    """Small generic case for parity tests: random distinct positions per
+    sequence, optionally some rows duplicated at an earlier row's position
+    (reading from X rows past N, like a second view), and an optional random
+    visibility mask."""
+    g = torch.Generator().manual_seed(seed)
+    B, N = shape.B, shape.N
+    x_rows = N + n_extra_rows
+    Qs, Ps = [], []
+    for b in range(B):
+        if positions is not None:
+            pos = list(positions[b])
+        else:
+            n_dup = int(round(dup_frac * nq)) if nq > 1 else 0
+            n_dup = min(n_dup, n_extra_rows, nq - 1) if nq > 1 else 0
+            base = _perm(g, N)[: nq - n_dup]
+            pos = list(base)
+            for k in range(n_dup):
+                pos.append(base[_randint(g, 0, len(base) - 1)])
+        q_idx = []
+        seen = set()
+        extra = 0
+        for p in pos:
+            if p in seen and extra < n_extra_rows:
+                q_idx.append(N + extra)
+                extra += 1
+            else:
+                q_idx.append(p)
+            seen.add(p)
+        Qs.append(q_idx)
+        Ps.append(pos)
+    Q = torch.tensor(Qs, dtype=torch.int32).reshape(B, nq)
+    P = torch.tensor(Ps, dtype=torch.int32).reshape(B, nq)
+    vis = None
+    if masked_vis and nq > 0:
+        vis = (torch.rand((B, nq, nq), generator=g) < 0.7).to(torch.uint8)
+    X_pre, W = hidden_and_weights(shape, x_rows, g, w_std)
+    X = step_hidden(shape, X_pre, Q, x_rows, g)
+    return Workload("random", shape, nq, x_rows, seed, X_pre, X, W, Q.contiguous(),
+                    P.contiguous(), vis, {})
