@@ -118,7 +118,8 @@ def round_store(x, mode: int) -> np.ndarray:
 
 
 def project(shape: Shape, X, Q_idx, pos_ids, W, round_mode: int):
-    """Gather + projection + rotary + rounding.  Returns q [B,nq,H,dh], k, v [B,nq,Hkv,dh]."""
+    """Gather + projection + rotary; k and v rounded to the storage type (q is
+    an on-chip value and stays unrounded).  Returns q [B,nq,H,dh], k, v [B,nq,Hkv,dh]."""
     X = _f64(X)
     Qi, Pi, W = _i32(Q_idx), _i32(pos_ids), _f64(W)
     B, x_rows = X.shape[0], X.shape[1]
@@ -138,7 +139,7 @@ def step(shape: Shape, X, Q_idx, pos_ids, vis, W, Kc, Vc, round_mode: int):
     """One fused step.  Kc/Vc are copied (the caller's arrays are not touched).
 
     Returns dict with O [B,nq,H,dh], LSE [B,nq,H], Kc, Vc (updated copies) and
-    the rounded q, k, v of the query rows.
+    the query rows' q (unrounded) and k, v (rounded to the storage type).
     """
     X = _f64(X)
     Qi, Pi, W = _i32(Q_idx), _i32(pos_ids), _f64(W)

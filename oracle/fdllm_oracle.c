@@ -32,8 +32,11 @@
  *   - W_qkv is [(H + 2 Hkv) dh, d_model], rows = output features ordered
  *     [q heads | k heads | v heads], each head dh contiguous; no bias.
  *   - query head h uses kv head g = floor(h * Hkv / H).
- *   - q, k, v are rounded once to the storage type after the rotation
- *     (round_mode), O is rounded once at the end; LSE stays unrounded.
+ *   - k and v are rounded once to the storage type after the rotation
+ *     (round_mode): they are what the cache stores.  q never leaves the chip
+ *     in the fused step (it is built on chip and consumed there), so it has
+ *     no storage type and is not rounded.  O is rounded once at the end;
+ *     LSE stays unrounded.
  *   - first occurrence of a position in Q order owns the cache write; later
  *     rows at the same position are attended as extra keys, never written.
  *   - key set of query row (b,i): every cache position not written by this
@@ -104,7 +107,7 @@ static void rope_rotate(double* v, int dh, int64_t pos, double base)
     }
 }
 
-/* a1-a3: gather, project, rotate, round.
+/* a1-a3: gather, project, rotate; k and v rounded to the storage type.
  * q_out [B,nq,H,dh], k_out/v_out [B,nq,Hkv,dh]. */
 int fdllm_oracle_project(const fdllm_oracle_cfg_t* cfg, const double* X, int32_t x_rows,
                          const int32_t* Q_idx, const int32_t* pos_ids, int32_t nq,
@@ -135,7 +138,7 @@ int fdllm_oracle_project(const fdllm_oracle_cfg_t* cfg, const double* X, int32_t
         for (int h = 0; h < H; ++h) rope_rotate(y + h * dh, dh, pos_ids[t], cfg->rope_base);
         for (int g = 0; g < Hkv; ++g) rope_rotate(y + (H + g) * dh, dh, pos_ids[t], cfg->rope_base);
         for (int o = 0; o < H * dh; ++o)
-            q_out[t * H * dh + o] = round_store(y[o], cfg->round_mode);
+            q_out[t * H * dh + o] = y[o];  /* on-chip value: not rounded */
         for (int o = 0; o < Hkv * dh; ++o) {
             k_out[t * Hkv * dh + o] = round_store(y[H * dh + o], cfg->round_mode);
             v_out[t * Hkv * dh + o] = round_store(y[(H + Hkv) * dh + o], cfg->round_mode);

@@ -352,9 +352,12 @@ def test_rounding_points_change_results_only_slightly_and_deterministically():
     b = oracle.step(sh, wl.X, wl.Q_idx, wl.pos_ids, None, wl.W, Kc, Kc, ROUND_BF16)
     e = oracle.step(sh, wl.X, wl.Q_idx, wl.pos_ids, None, wl.W, Kc, Kc, ROUND_EXACT)
     np.testing.assert_array_equal(a["O"], b["O"])
-    # rounded outputs are bf16 values
+    # stored values (O, k, v) are bf16 values; q is the unrounded on-chip value
     np.testing.assert_array_equal(oracle.round_store(a["O"], ROUND_BF16), a["O"])
     np.testing.assert_array_equal(oracle.round_store(a["k"], ROUND_BF16), a["k"])
+    np.testing.assert_array_equal(oracle.round_store(a["v"], ROUND_BF16), a["v"])
+    np.testing.assert_array_equal(a["q"], e["q"])
+    assert not np.array_equal(oracle.round_store(a["q"], ROUND_BF16), a["q"])
     assert np.abs(a["O"] - e["O"]).max() < 2e-2 * np.abs(e["O"]).max()
     assert np.abs(a["LSE"] - e["LSE"]).max() < 5e-3
 
