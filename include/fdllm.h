@@ -1,0 +1,156 @@
+/*
+ * fdllm.h -- C ABI of the IO-aware fused KV-cache step of a diffusion LLM
+ * attention layer (Flash-dLLM), hand-written HIP for MI355X (gfx950).
+ *
+ * The operation (Flash-dLLM review on jaehun.me, "How It Works: A Concrete
+ * Example", Step 1: Draft and Step 1: Verification; alanhou.org summary,
+ * "Core Mechanism", item 1): for every sequence b, read only the hidden
+ * states of the query rows Q (tracked set plus the first beta_m masked
+ * positions, or the verification layout [tracked | confident | draft view |
+ * mask view]), project them to q, k, v on chip, rotate q and k by position,
+ * write k and v straight into the persistent flat bidirectional cache at
+ * those positions, and attend the query rows over the whole cache under a
+ * visibility mask that keeps the draft view and the [MASK] view apart.
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are caller-owned, row-major, contiguous device pointers
+ *     (hipMalloc / PyTorch allocations), 16-byte aligned.  Element type of
+ *     X, W_qkv, Kc, Vc and O is the configuration's dtype (fp32 or bf16);
+ *     LSE is fp32; index arrays are int32; the mask is uint8.
+ *   - Shapes (notation of the pages): B sequences, cache length N, model
+ *     width d_model, H query heads, Hkv key/value heads (H % Hkv == 0), head
+ *     width dh, nq = |Q| query rows per sequence.
+ *       X        [B, x_rows, d_model]   hidden states, addressed by Q_idx
+ *       W_qkv    [(H + 2 Hkv) dh, d_model]  rows ordered [q heads | k heads |
+ *                v heads], head-major, dh contiguous (y = W_qkv x, no bias)
+ *       Kc, Vc   [B, Hkv, N, dh]        persistent cache, updated in place;
+ *                the cached k is post-rotation
+ *       Q_idx    [B, nq]  X row of each query row, 0 <= Q_idx < x_rows
+ *       pos_ids  [B, nq]  position of each query row, 0 <= pos_ids < N; two
+ *                rows may share a position (the two verification views)
+ *       vis_mask [B, nq, nq] or NULL; vis_mask[b,i,j] != 0 lets query row i
+ *                see the new key of row j; NULL means all visible
+ *       O        [B, nq, H, dh], LSE [B, nq, H] (natural log)
+ *   - Rotary embedding: rotate-half pairs (e, e + dh/2), phase
+ *     pos * base^(-2e/dh).  Query head h reads kv head h * Hkv / H.
+ *     Softmax scale 1/sqrt(dh).
+ *   - Write rule: the first row (in Q order) at a position owns the cache
+ *     write; later rows at the same position are attended as extra keys and
+ *     never written.  Cache rows at positions not in pos_ids[b] are never
+ *     touched.
+ *   - Key set of query row (b,i): every cache position not in pos_ids[b]
+ *     (old content), plus each new row j with vis_mask[b,i,j] != 0.  The old
+ *     content at positions in pos_ids[b] is never attended.  An empty key set
+ *     gives O = 0 and LSE = -inf.
+ *   - Rounding: q, k, v are rounded once to the dtype after the rotation
+ *     (nearest even); accumulation is fp32; O is rounded once at the end.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *     asynchronous on that stream and never synchronise, except that
+ *     FDLLM_VALIDATE=1 in the environment makes fdllm_fused_step copy the
+ *     index arrays to the host and range-check them first.
+ *   - Return value: FDLLM_OK or a negative status; on any error nothing has
+ *     been launched.  Indices out of range are undefined behaviour unless
+ *     FDLLM_VALIDATE=1.  A handle serves one stream at a time; concurrent
+ *     calls on one handle race on its workspace.
+ */
+#ifndef FDLLM_H
+#define FDLLM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FDLLM_F32 = 0, FDLLM_BF16 = 1 } fdllm_dtype_t;
+
+enum {
+    FDLLM_OK = 0,
+    FDLLM_ERR_ARG = -1,      /* null pointer, null handle or invalid configuration */
+    FDLLM_ERR_SHAPE = -2,    /* nq > q_max, x_rows < 1, nq < 0 */
+    FDLLM_ERR_ALIGN = -3,    /* a tensor pointer not 16-byte aligned */
+    FDLLM_ERR_INDEX = -4,    /* index out of range (only with FDLLM_VALIDATE=1) */
+    FDLLM_ERR_ALLOC = -5,    /* device workspace allocation failed */
+    FDLLM_ERR_HIP = -6,      /* a HIP runtime call or launch failed */
+    FDLLM_ERR_UNSUPPORTED = -7 /* shape outside what the kernels implement */
+};
+
+typedef struct {
+    int32_t B, N, d_model, H, Hkv, dh;
+    int32_t q_max;          /* largest nq any fused step of this handle will use */
+    double rope_base;       /* rotary base, e.g. 10000 */
+    int32_t dtype;          /* fdllm_dtype_t */
+} fdllm_config_t;
+
+/* Launch-shape overrides for sweeps; 0 keeps the library's choice. */
+typedef struct {
+    int32_t attn_splits;    /* cache splits per (sequence, kv head) in the attention */
+    int32_t gemm_splitk;    /* d_model splits of the projection */
+    int32_t kernel_family;  /* 0 auto, 1 tiled MFMA (bf16 only), 2 generic scalar */
+} fdllm_tuning_t;
+
+typedef struct fdllm_ctx* fdllm_handle_t;
+
+/* Host-only check of a configuration (no HIP call).  Returns FDLLM_OK,
+ * FDLLM_ERR_ARG or FDLLM_ERR_UNSUPPORTED. */
+int fdllm_validate_config(const fdllm_config_t* cfg);
+
+/* Create a handle: validates cfg, allocates the handle's workspace on the
+ * current device (rotary table, q staging, duplicate-row side buffer, split
+ * partials and counters) and, if X_full is not NULL, builds the cache from
+ * the full sequence (see fdllm_prefill with x_rows = N).  W_qkv, Kc, Vc may
+ * be NULL when X_full is NULL.  *out receives the handle, or NULL on error.
+ * Statuses: ARG, UNSUPPORTED, ALIGN, ALLOC, HIP. */
+int fdllm_cache_init(fdllm_handle_t* out, const fdllm_config_t* cfg, const void* X_full,
+                     const void* W_qkv, void* Kc, void* Vc, void* stream);
+
+/* Cache build from a full sequence ("cache prefilled from full-sequence
+ * projection"): for every b and position p < N, row p of X[b] is projected,
+ * k is rotated at position p, and k, v are rounded and stored at
+ * Kc/Vc[b, :, p, :].  X is [B, x_rows, d_model] with x_rows >= N.
+ * Statuses: ARG, SHAPE, ALIGN, HIP. */
+int fdllm_prefill(fdllm_handle_t h, const void* X, int32_t x_rows, const void* W_qkv,
+                  void* Kc, void* Vc, void* stream);
+
+/* One fused step (gather X[Q] -> q,k,v -> rotary -> in-place k/v write ->
+ * attention over the whole cache under vis_mask), see the conventions above.
+ * 0 <= nq <= q_max; nq == 0 launches nothing.
+ * Statuses: ARG, SHAPE, ALIGN, INDEX (FDLLM_VALIDATE=1 only), HIP. */
+int fdllm_fused_step(fdllm_handle_t h, const void* X, int32_t x_rows, const int32_t* Q_idx,
+                     const int32_t* pos_ids, int32_t nq, const uint8_t* vis_mask,
+                     const void* W_qkv, void* Kc, void* Vc, void* O, float* LSE, void* stream);
+
+/* The two launches of fdllm_fused_step, callable separately (same arguments
+ * and statuses; used to time the phases or to run work between them).
+ * fdllm_step_project runs gather + projection + rotary + k/v write and leaves
+ * the step's rounded q rows and duplicate-position k/v rows in the handle's
+ * workspace; fdllm_step_attend consumes them (it must follow the project call
+ * of the same step on the same stream, with the same nq and pos_ids). */
+int fdllm_step_project(fdllm_handle_t h, const void* X, int32_t x_rows, const int32_t* Q_idx,
+                       const int32_t* pos_ids, int32_t nq, const void* W_qkv, void* Kc, void* Vc,
+                       void* stream);
+int fdllm_step_attend(fdllm_handle_t h, const int32_t* pos_ids, int32_t nq, const uint8_t* vis_mask,
+                      const void* Kc, const void* Vc, void* O, float* LSE, void* stream);
+
+/* Set (tuning != NULL) or reset (NULL) the launch-shape overrides of h.
+ * Statuses: ARG. */
+int fdllm_set_tuning(fdllm_handle_t h, const fdllm_tuning_t* tuning);
+
+/* Report the launch shapes fdllm_fused_step would use for nq: attention
+ * splits, projection d_model splits and the kernel family (1 tiled MFMA,
+ * 2 generic).  Any output pointer may be NULL.  Statuses: ARG, SHAPE. */
+int fdllm_get_plan(fdllm_handle_t h, int32_t nq, int32_t* attn_splits, int32_t* gemm_splitk,
+                   int32_t* kernel_family);
+
+/* Free the handle and its workspace (synchronises the device first).
+ * NULL is accepted.  Statuses: HIP. */
+int fdllm_cache_destroy(fdllm_handle_t h);
+
+/* Static, human-readable name of a status code. */
+const char* fdllm_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FDLLM_H */

@@ -1,0 +1,210 @@
+"""ctypes binding of libfdllm (include/fdllm.h): argument marshalling only.
+
+Every step of the fused KV-cache step runs in the library's HIP kernels; this
+module checks tensor devices, dtypes and shapes, passes raw device pointers
+and the current HIP stream, and turns status codes into exceptions.  It
+raises if the library has not been built: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfdllm.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "fdllm.h")
+
+FDLLM_F32, FDLLM_BF16 = 0, 1
+STATUS = {0: "FDLLM_OK", -1: "FDLLM_ERR_ARG", -2: "FDLLM_ERR_SHAPE", -3: "FDLLM_ERR_ALIGN",
+          -4: "FDLLM_ERR_INDEX", -5: "FDLLM_ERR_ALLOC", -6: "FDLLM_ERR_HIP", -7: "FDLLM_ERR_UNSUPPORTED"}
+
+
+class FdllmError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (what, STATUS.get(status, "?"), status))
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("N", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("H", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("dh", ctypes.c_int32),
+                ("q_max", ctypes.c_int32), ("rope_base", ctypes.c_double), ("dtype", ctypes.c_int32)]
+
+
+class Tuning(ctypes.Structure):
+    _fields_ = [("attn_splits", ctypes.c_int32), ("gemm_splitk", ctypes.c_int32),
+                ("kernel_family", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def declared_symbols():
+    """Function names declared in include/fdllm.h."""
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(fdllm_\w+)\s*\(", txt, re.M)))
+
+
+def load():
+    """Load libfdllm.so (built by io_aware_kv_amd.build); raises if missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libfdllm.so is not built (%s); run __graft_entry__.build()" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32 = ctypes.c_void_p, ctypes.c_int32
+    lib.fdllm_validate_config.argtypes = [ctypes.POINTER(Config)]
+    lib.fdllm_cache_init.argtypes = [ctypes.POINTER(P), ctypes.POINTER(Config), P, P, P, P, P]
+    lib.fdllm_prefill.argtypes = [P, P, i32, P, P, P, P]
+    lib.fdllm_fused_step.argtypes = [P, P, i32, P, P, i32, P, P, P, P, P, P, P]
+    lib.fdllm_step_project.argtypes = [P, P, i32, P, P, i32, P, P, P, P]
+    lib.fdllm_step_attend.argtypes = [P, P, i32, P, P, P, P, P, P]
+    lib.fdllm_set_tuning.argtypes = [P, ctypes.POINTER(Tuning)]
+    lib.fdllm_get_plan.argtypes = [P, i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.fdllm_cache_destroy.argtypes = [P]
+    lib.fdllm_status_str.argtypes = [ctypes.c_int]
+    lib.fdllm_status_str.restype = ctypes.c_char_p
+    for name in ("fdllm_validate_config", "fdllm_cache_init", "fdllm_prefill", "fdllm_fused_step",
+                 "fdllm_step_project", "fdllm_step_attend",
+                 "fdllm_set_tuning", "fdllm_get_plan", "fdllm_cache_destroy"):
+        getattr(lib, name).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise FdllmError(rc, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(dtype: torch.dtype) -> int:
+    if dtype == torch.bfloat16:
+        return FDLLM_BF16
+    if dtype == torch.float32:
+        return FDLLM_F32
+    raise ValueError("dtype must be bfloat16 or float32")
+
+
+def make_config(B, N, d_model, H, Hkv, dh, q_max, dtype=torch.bfloat16, rope_base=10000.0) -> Config:
+    return Config(B, N, d_model, H, Hkv, dh, q_max, float(rope_base), _dtype_code(dtype))
+
+
+def validate_config(cfg: Config) -> int:
+    """Host-only configuration check; returns the status code."""
+    return load().fdllm_validate_config(ctypes.byref(cfg))
+
+
+class FusedKVCache:
+    """A library handle for one layer shape: workspace plus the fused step."""
+
+    def __init__(self, B, N, d_model, H, Hkv, dh, q_max, dtype=torch.bfloat16, rope_base=10000.0,
+                 X_full=None, W=None, Kc=None, Vc=None, stream=None):
+        lib = load()
+        self.cfg = make_config(B, N, d_model, H, Hkv, dh, q_max, dtype, rope_base)
+        self.dtype = dtype
+        h = ctypes.c_void_p()
+        if X_full is not None:
+            self._check_layer(X_full, W, Kc, Vc)
+        rc = lib.fdllm_cache_init(ctypes.byref(h), ctypes.byref(self.cfg), _ptr(X_full), _ptr(W),
+                                  _ptr(Kc), _ptr(Vc), _stream(stream))
+        _check(rc, "fdllm_cache_init")
+        self._h = h
+
+    def _check_layer(self, X, W, Kc, Vc):
+        c = self.cfg
+        for name, t in (("X", X), ("W", W), ("Kc", Kc), ("Vc", Vc)):
+            if t is None or t.dtype != self.dtype:
+                raise ValueError("%s must be a %s tensor" % (name, self.dtype))
+        if X.dim() != 3 or X.shape[0] != c.B or X.shape[2] != c.d_model:
+            raise ValueError("X must be [B, x_rows, d_model]")
+        if tuple(W.shape) != ((c.H + 2 * c.Hkv) * c.dh, c.d_model):
+            raise ValueError("W must be [(H + 2 Hkv) dh, d_model]")
+        for t in (Kc, Vc):
+            if tuple(t.shape) != (c.B, c.Hkv, c.N, c.dh):
+                raise ValueError("Kc/Vc must be [B, Hkv, N, dh]")
+
+    @property
+    def handle(self):
+        return self._h
+
+    def prefill(self, X, W, Kc, Vc, stream=None):
+        self._check_layer(X, W, Kc, Vc)
+        rc = load().fdllm_prefill(self._h, _ptr(X), X.shape[1], _ptr(W), _ptr(Kc), _ptr(Vc), _stream(stream))
+        _check(rc, "fdllm_prefill")
+
+    def step(self, X, Q_idx, pos_ids, vis, W, Kc, Vc, O, LSE, stream=None):
+        """One fused step.  O [B,nq,H,dh] and LSE [B,nq,H] (fp32) are written."""
+        c = self.cfg
+        self._check_layer(X, W, Kc, Vc)
+        nq = Q_idx.shape[1]
+        if Q_idx.dtype != torch.int32 or pos_ids.dtype != torch.int32:
+            raise ValueError("Q_idx and pos_ids must be int32")
+        if tuple(Q_idx.shape) != (c.B, nq) or tuple(pos_ids.shape) != (c.B, nq):
+            raise ValueError("Q_idx and pos_ids must be [B, nq]")
+        if vis is not None and (vis.dtype != torch.uint8 or tuple(vis.shape) != (c.B, nq, nq)):
+            raise ValueError("vis must be uint8 [B, nq, nq]")
+        if O.dtype != self.dtype or tuple(O.shape) != (c.B, nq, c.H, c.dh):
+            raise ValueError("O must be [B, nq, H, dh] of the layer dtype")
+        if LSE.dtype != torch.float32 or tuple(LSE.shape) != (c.B, nq, c.H):
+            raise ValueError("LSE must be fp32 [B, nq, H]")
+        rc = load().fdllm_fused_step(self._h, _ptr(X), X.shape[1], _ptr(Q_idx), _ptr(pos_ids), nq,
+                                     _ptr(vis), _ptr(W), _ptr(Kc), _ptr(Vc), _ptr(O), _ptr(LSE),
+                                     _stream(stream))
+        _check(rc, "fdllm_fused_step")
+
+    def project(self, X, Q_idx, pos_ids, W, Kc, Vc, stream=None):
+        """First launch of the step (gather, projection, rotary, k/v write)."""
+        self._check_layer(X, W, Kc, Vc)
+        nq = Q_idx.shape[1]
+        rc = load().fdllm_step_project(self._h, _ptr(X), X.shape[1], _ptr(Q_idx), _ptr(pos_ids), nq,
+                                       _ptr(W), _ptr(Kc), _ptr(Vc), _stream(stream))
+        _check(rc, "fdllm_step_project")
+
+    def attend(self, pos_ids, vis, Kc, Vc, O, LSE, stream=None):
+        """Second launch of the step (attention over the cache, split combine)."""
+        nq = pos_ids.shape[1]
+        rc = load().fdllm_step_attend(self._h, _ptr(pos_ids), nq, _ptr(vis), _ptr(Kc), _ptr(Vc), _ptr(O),
+                                      _ptr(LSE), _stream(stream))
+        _check(rc, "fdllm_step_attend")
+
+    def set_tuning(self, attn_splits=0, gemm_splitk=0, kernel_family=0):
+        t = Tuning(attn_splits, gemm_splitk, kernel_family)
+        _check(load().fdllm_set_tuning(self._h, ctypes.byref(t)), "fdllm_set_tuning")
+
+    def plan(self, nq):
+        a, g, f = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+        _check(load().fdllm_get_plan(self._h, nq, ctypes.byref(a), ctypes.byref(g), ctypes.byref(f)),
+               "fdllm_get_plan")
+        return {"attn_splits": a.value, "gemm_splitk": g.value, "kernel_family": f.value}
+
+    def close(self):
+        if getattr(self, "_h", None):
+            _check(load().fdllm_cache_destroy(self._h), "fdllm_cache_destroy")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

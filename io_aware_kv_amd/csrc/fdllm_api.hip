@@ -1,0 +1,394 @@
+// fdllm_api.hip -- the C ABI of libfdllm (declared in include/fdllm.h):
+// argument checks, the handle's workspace, the rotary table, launch planning
+// and the launch sequence of the fused step.  No arithmetic of the step runs
+// here: every step runs in the HIP kernels.
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "fdllm.h"
+#include "fdllm_common.h"
+
+using namespace fdllm;
+
+struct fdllm_ctx {
+    fdllm_config_t cfg;
+    int device = 0;
+    int G = 1;
+    size_t elt = 2;
+    float2* rope = nullptr;
+    float* qbuf = nullptr;
+    void* sideK = nullptr;
+    void* sideV = nullptr;
+    float* gpart = nullptr;
+    size_t gpart_bytes = 0;
+    uint32_t* gticket = nullptr;
+    size_t gticket_n = 0;
+    float* apart = nullptr;
+    float* aml = nullptr;
+    size_t apart_rows = 0;        // (B*Hkv) * splits * Rpad rows available
+    uint32_t* aticket = nullptr;
+    fdllm_tuning_t tune{0, 0, 0};
+};
+
+namespace {
+
+enum { FAMILY_MFMA = 1, FAMILY_GENERIC = 2 };
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int env_int(const char* name, int dflt)
+{
+    const char* v = getenv(name);
+    return (v && *v) ? atoi(v) : dflt;
+}
+
+struct Plan {
+    int proj_family, attn_family;
+    int splitk, proj_tiles, bm;
+    int splits, keys_per_split, R, Rpad;
+};
+
+Plan make_plan(const fdllm_ctx* h, int nq)
+{
+    const fdllm_config_t& c = h->cfg;
+    Plan p{};
+    int fam = h->tune.kernel_family;
+    const bool mfma_ok = c.dtype == FDLLM_BF16 && c.dh == 128 && c.d_model % 64 == 0;
+    if (fam == 0) fam = mfma_ok ? FAMILY_MFMA : FAMILY_GENERIC;
+    if (fam == FAMILY_MFMA && !mfma_ok) fam = FAMILY_GENERIC;
+    p.proj_family = fam;
+    p.R = nq * h->G;
+    p.Rpad = ((p.R + 15) / 16) * 16;
+    p.attn_family = (fam == FAMILY_MFMA && (p.R + 15) / 16 <= 16) ? FAMILY_MFMA : FAMILY_GENERIC;
+
+    // projection: tiles of BM rows x one head; split d_model until ~512 workgroups
+    const int M = c.B * nq;
+    p.splitk = 1;
+    if (p.proj_family == FAMILY_MFMA && M > 0) {
+        p.bm = proj_mfma_block_m(M);
+        const int m_tiles = (M + p.bm - 1) / p.bm;
+        p.proj_tiles = m_tiles * (c.H + 2 * c.Hkv);
+        const int nk = c.d_model / 64;
+        int sk = h->tune.gemm_splitk > 0 ? h->tune.gemm_splitk : env_int("FDLLM_SPLITK", 0);
+        if (sk <= 0) {
+            sk = (512 + p.proj_tiles - 1) / p.proj_tiles;
+            sk = std::min(sk, std::max(1, nk / 4));
+        }
+        p.splitk = std::max(1, std::min(sk, nk));
+    }
+
+    // attention: (sequence, kv head) pairs x cache splits, ~512 workgroups
+    p.splits = 1;
+    p.keys_per_split = c.N;
+    if (p.attn_family == FAMILY_MFMA && nq > 0) {
+        const int tk = attn_mfma_tile_keys(p.R);
+        const int bgs = c.B * c.Hkv;
+        const int max_splits = (c.N + tk - 1) / tk;
+        int sp = h->tune.attn_splits > 0 ? h->tune.attn_splits : env_int("FDLLM_SPLITS", 0);
+        if (sp <= 0) sp = (512 + bgs - 1) / bgs;
+        sp = std::max(1, std::min(sp, max_splits));
+        int kps = (c.N + sp - 1) / sp;
+        kps = ((kps + tk - 1) / tk) * tk;
+        // the per-split slot table lives in LDS: keep a split under 8192 keys
+        while (kps > 8192) kps -= tk;
+        p.keys_per_split = kps;
+        p.splits = (c.N + kps - 1) / kps;
+    }
+    return p;
+}
+
+int hip_status(hipError_t e)
+{
+    if (e == hipSuccess) return FDLLM_OK;
+    if (getenv("FDLLM_LOG")) fprintf(stderr, "fdllm: HIP error %s\n", hipGetErrorString(e));
+    return FDLLM_ERR_HIP;
+}
+
+void free_ws(fdllm_ctx* h)
+{
+    void* ptrs[] = {h->rope, h->qbuf, h->sideK, h->sideV, h->gpart, h->gticket, h->apart, h->aml, h->aticket};
+    for (void* p : ptrs)
+        if (p) (void)hipFree(p);
+    h->rope = nullptr; h->qbuf = nullptr; h->sideK = h->sideV = nullptr;
+    h->gpart = nullptr; h->gticket = nullptr; h->apart = h->aml = nullptr; h->aticket = nullptr;
+}
+
+// Size the split buffers for every nq the handle may see.
+int ensure_split_ws(fdllm_ctx* h)
+{
+    const fdllm_config_t& c = h->cfg;
+    size_t gbytes = 0, gtickets = 0, arows = 0;
+    for (int nq = 1; nq <= c.q_max; ++nq) {
+        const Plan p = make_plan(h, nq);
+        if (p.proj_family == FAMILY_MFMA && p.splitk > 1) {
+            gbytes = std::max(gbytes, (size_t)p.proj_tiles * p.splitk * p.bm * 128 * sizeof(float));
+            gtickets = std::max(gtickets, (size_t)p.proj_tiles);
+        }
+        if (p.attn_family == FAMILY_MFMA && p.splits > 1)
+            arows = std::max(arows, (size_t)c.B * c.Hkv * p.splits * p.Rpad);
+    }
+    if (gbytes > h->gpart_bytes) {
+        if (h->gpart) (void)hipFree(h->gpart);
+        h->gpart = nullptr;
+        if (hipMalloc(&h->gpart, gbytes) != hipSuccess) { h->gpart_bytes = 0; return FDLLM_ERR_ALLOC; }
+        h->gpart_bytes = gbytes;
+    }
+    if (gtickets > h->gticket_n) {
+        if (h->gticket) (void)hipFree(h->gticket);
+        h->gticket = nullptr;
+        if (hipMalloc(&h->gticket, gtickets * sizeof(uint32_t)) != hipSuccess) { h->gticket_n = 0; return FDLLM_ERR_ALLOC; }
+        if (hipMemset(h->gticket, 0, gtickets * sizeof(uint32_t)) != hipSuccess) return FDLLM_ERR_HIP;
+        h->gticket_n = gtickets;
+    }
+    if (arows > h->apart_rows) {
+        if (h->apart) (void)hipFree(h->apart);
+        if (h->aml) (void)hipFree(h->aml);
+        h->apart = h->aml = nullptr;
+        if (hipMalloc(&h->apart, arows * c.dh * sizeof(float)) != hipSuccess ||
+            hipMalloc(&h->aml, arows * 2 * sizeof(float)) != hipSuccess) {
+            h->apart_rows = 0;
+            return FDLLM_ERR_ALLOC;
+        }
+        h->apart_rows = arows;
+    }
+    return FDLLM_OK;
+}
+
+int set_device(const fdllm_ctx* h)
+{
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return FDLLM_ERR_HIP;
+    if (cur != h->device && hipSetDevice(h->device) != hipSuccess) return FDLLM_ERR_HIP;
+    return FDLLM_OK;
+}
+
+ProjArgs proj_args(const fdllm_ctx* h, const void* X, int x_rows, const int32_t* Q_idx, const int32_t* pos,
+                   int rows_per_seq, const void* W, void* Kc, void* Vc, int prefill, int splitk)
+{
+    const fdllm_config_t& c = h->cfg;
+    ProjArgs a{};
+    a.X = X; a.W = W; a.Q_idx = Q_idx; a.pos_ids = pos; a.rope = h->rope;
+    a.Kc = Kc; a.Vc = Vc; a.qbuf = h->qbuf; a.sideK = h->sideK; a.sideV = h->sideV;
+    a.gpart = h->gpart; a.gticket = h->gticket;
+    a.B = c.B; a.N = c.N; a.d = c.d_model; a.H = c.H; a.Hkv = c.Hkv; a.dh = c.dh; a.G = h->G;
+    a.x_rows = x_rows; a.rows_per_seq = rows_per_seq; a.q_max = c.q_max;
+    a.prefill = prefill; a.splitk = splitk;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fdllm_status_str(int status)
+{
+    switch (status) {
+        case FDLLM_OK: return "FDLLM_OK";
+        case FDLLM_ERR_ARG: return "FDLLM_ERR_ARG: null or invalid argument";
+        case FDLLM_ERR_SHAPE: return "FDLLM_ERR_SHAPE: size out of range (nq > q_max, nq < 0, x_rows too small)";
+        case FDLLM_ERR_ALIGN: return "FDLLM_ERR_ALIGN: tensor pointer not 16-byte aligned";
+        case FDLLM_ERR_INDEX: return "FDLLM_ERR_INDEX: Q_idx or pos_ids out of range";
+        case FDLLM_ERR_ALLOC: return "FDLLM_ERR_ALLOC: device workspace allocation failed";
+        case FDLLM_ERR_HIP: return "FDLLM_ERR_HIP: HIP runtime or launch error";
+        case FDLLM_ERR_UNSUPPORTED: return "FDLLM_ERR_UNSUPPORTED: shape not implemented";
+        default: return "FDLLM: unknown status";
+    }
+}
+
+int fdllm_validate_config(const fdllm_config_t* c)
+{
+    if (!c) return FDLLM_ERR_ARG;
+    if (c->B < 1 || c->N < 1 || c->d_model < 1 || c->H < 1 || c->Hkv < 1 || c->dh < 2 || c->q_max < 1)
+        return FDLLM_ERR_ARG;
+    if (c->H % c->Hkv != 0 || (c->dh & 1) || !(c->rope_base > 0.0)) return FDLLM_ERR_ARG;
+    if (c->dtype != FDLLM_F32 && c->dtype != FDLLM_BF16) return FDLLM_ERR_ARG;
+    const int elt = c->dtype == FDLLM_BF16 ? 2 : 4;
+    // 16-byte rows everywhere: head width and model width in whole 16 B chunks
+    if ((c->dh * elt) % 16 != 0 || (c->d_model * elt) % 16 != 0) return FDLLM_ERR_UNSUPPORTED;
+    if (c->dh > 256) return FDLLM_ERR_UNSUPPORTED;           // scalar kernels keep dh <= 256
+    if (c->q_max > 32767) return FDLLM_ERR_UNSUPPORTED;      // row slots are int16 in LDS
+    if ((int64_t)c->B * c->Hkv * c->N > ((int64_t)1 << 40)) return FDLLM_ERR_UNSUPPORTED;
+    return FDLLM_OK;
+}
+
+int fdllm_prefill(fdllm_handle_t h, const void* X, int32_t x_rows, const void* W, void* Kc, void* Vc,
+                  void* stream)
+{
+    if (!h || !X || !W || !Kc || !Vc) return FDLLM_ERR_ARG;
+    if (x_rows < h->cfg.N) return FDLLM_ERR_SHAPE;
+    if (!aligned16(X) || !aligned16(W) || !aligned16(Kc) || !aligned16(Vc)) return FDLLM_ERR_ALIGN;
+    int st = set_device(h);
+    if (st) return st;
+    const Plan p = make_plan(h, 1);
+    hipStream_t s = (hipStream_t)stream;
+    ProjArgs a = proj_args(h, X, x_rows, nullptr, nullptr, h->cfg.N, W, Kc, Vc, 1, 1);
+    hipError_t e = p.proj_family == FAMILY_MFMA ? launch_proj_mfma(a, s)
+                                                : launch_proj_generic(a, h->cfg.dtype, s);
+    return hip_status(e);
+}
+
+int fdllm_cache_init(fdllm_handle_t* out, const fdllm_config_t* cfg, const void* X_full, const void* W,
+                     void* Kc, void* Vc, void* stream)
+{
+    if (!out) return FDLLM_ERR_ARG;
+    *out = nullptr;
+    int st = fdllm_validate_config(cfg);
+    if (st) return st;
+    if (X_full && (!W || !Kc || !Vc)) return FDLLM_ERR_ARG;
+    fdllm_ctx* h = new (std::nothrow) fdllm_ctx();
+    if (!h) return FDLLM_ERR_ALLOC;
+    h->cfg = *cfg;
+    h->G = cfg->H / cfg->Hkv;
+    h->elt = cfg->dtype == FDLLM_BF16 ? 2 : 4;
+    if (hipGetDevice(&h->device) != hipSuccess) { delete h; return FDLLM_ERR_HIP; }
+
+    const fdllm_config_t& c = h->cfg;
+    const size_t half = c.dh / 2;
+    const size_t qrows = (size_t)c.B * c.Hkv * c.q_max * h->G;
+    const size_t srows = (size_t)c.B * c.Hkv * c.q_max;
+    bool ok = hipMalloc(&h->rope, (size_t)c.N * half * sizeof(float2)) == hipSuccess &&
+              hipMalloc(&h->qbuf, qrows * c.dh * sizeof(float)) == hipSuccess &&
+              hipMalloc(&h->sideK, srows * c.dh * h->elt) == hipSuccess &&
+              hipMalloc(&h->sideV, srows * c.dh * h->elt) == hipSuccess &&
+              hipMalloc(&h->aticket, (size_t)c.B * c.Hkv * sizeof(uint32_t)) == hipSuccess;
+    if (!ok) { free_ws(h); delete h; return FDLLM_ERR_ALLOC; }
+    if (hipMemset(h->aticket, 0, (size_t)c.B * c.Hkv * sizeof(uint32_t)) != hipSuccess) {
+        free_ws(h); delete h; return FDLLM_ERR_HIP;
+    }
+    st = ensure_split_ws(h);
+    if (st) { free_ws(h); delete h; return st; }
+
+    // rotary table: phase pos * base^(-2e/dh), evaluated in double, stored fp32
+    std::vector<float2> tab((size_t)c.N * half);
+    for (int p = 0; p < c.N; ++p)
+        for (size_t e = 0; e < half; ++e) {
+            const double theta = std::pow(c.rope_base, -2.0 * (double)e / (double)c.dh);
+            const double phi = (double)p * theta;
+            tab[(size_t)p * half + e] = make_float2((float)std::cos(phi), (float)std::sin(phi));
+        }
+    if (hipMemcpy(h->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice) != hipSuccess) {
+        free_ws(h); delete h; return FDLLM_ERR_HIP;
+    }
+    if (X_full) {
+        st = fdllm_prefill(h, X_full, c.N, W, Kc, Vc, stream);
+        if (st) { free_ws(h); delete h; return st; }
+    }
+    *out = h;
+    return FDLLM_OK;
+}
+
+int fdllm_set_tuning(fdllm_handle_t h, const fdllm_tuning_t* t)
+{
+    if (!h) return FDLLM_ERR_ARG;
+    if (t && (t->attn_splits < 0 || t->gemm_splitk < 0 || t->kernel_family < 0 || t->kernel_family > 2))
+        return FDLLM_ERR_ARG;
+    h->tune = t ? *t : fdllm_tuning_t{0, 0, 0};
+    int st = set_device(h);
+    if (st) return st;
+    return ensure_split_ws(h);
+}
+
+int fdllm_get_plan(fdllm_handle_t h, int32_t nq, int32_t* attn_splits, int32_t* gemm_splitk, int32_t* family)
+{
+    if (!h) return FDLLM_ERR_ARG;
+    if (nq < 0 || nq > h->cfg.q_max) return FDLLM_ERR_SHAPE;
+    const Plan p = make_plan(h, nq);
+    if (attn_splits) *attn_splits = p.splits;
+    if (gemm_splitk) *gemm_splitk = p.splitk;
+    if (family) *family = p.proj_family;
+    return FDLLM_OK;
+}
+
+int fdllm_step_project(fdllm_handle_t h, const void* X, int32_t x_rows, const int32_t* Q_idx,
+                       const int32_t* pos_ids, int32_t nq, const void* W, void* Kc, void* Vc, void* stream)
+{
+    if (!h) return FDLLM_ERR_ARG;
+    const fdllm_config_t& c = h->cfg;
+    if (nq < 0 || nq > c.q_max || x_rows < 1) return FDLLM_ERR_SHAPE;
+    if (nq == 0) return FDLLM_OK;
+    if (!X || !Q_idx || !pos_ids || !W || !Kc || !Vc) return FDLLM_ERR_ARG;
+    if (!aligned16(X) || !aligned16(W) || !aligned16(Kc) || !aligned16(Vc) ||
+        (reinterpret_cast<uintptr_t>(Q_idx) & 3u) || (reinterpret_cast<uintptr_t>(pos_ids) & 3u))
+        return FDLLM_ERR_ALIGN;
+    int st = set_device(h);
+    if (st) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (env_int("FDLLM_VALIDATE", 0)) {
+        std::vector<int32_t> qi((size_t)c.B * nq), pi((size_t)c.B * nq);
+        if (hipMemcpyAsync(qi.data(), Q_idx, qi.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipMemcpyAsync(pi.data(), pos_ids, pi.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess)
+            return FDLLM_ERR_HIP;
+        for (size_t t = 0; t < qi.size(); ++t)
+            if (qi[t] < 0 || qi[t] >= x_rows || pi[t] < 0 || pi[t] >= c.N) return FDLLM_ERR_INDEX;
+    }
+    const Plan p = make_plan(h, nq);
+    if (p.proj_family == FAMILY_MFMA && p.splitk > 1 &&
+        (size_t)p.proj_tiles * p.splitk * p.bm * 128 * sizeof(float) > h->gpart_bytes)
+        return FDLLM_ERR_ALLOC;   // not reached: the workspace is sized for every nq
+    ProjArgs pa = proj_args(h, X, x_rows, Q_idx, pos_ids, nq, W, Kc, Vc, 0, p.splitk);
+    hipError_t e = p.proj_family == FAMILY_MFMA ? launch_proj_mfma(pa, s) : launch_proj_generic(pa, c.dtype, s);
+    return hip_status(e);
+}
+
+int fdllm_step_attend(fdllm_handle_t h, const int32_t* pos_ids, int32_t nq, const uint8_t* vis,
+                      const void* Kc, const void* Vc, void* O, float* LSE, void* stream)
+{
+    if (!h) return FDLLM_ERR_ARG;
+    const fdllm_config_t& c = h->cfg;
+    if (nq < 0 || nq > c.q_max) return FDLLM_ERR_SHAPE;
+    if (nq == 0) return FDLLM_OK;
+    if (!pos_ids || !Kc || !Vc || !O || !LSE) return FDLLM_ERR_ARG;
+    if (!aligned16(Kc) || !aligned16(Vc) || !aligned16(O) || (reinterpret_cast<uintptr_t>(LSE) & 3u) ||
+        (reinterpret_cast<uintptr_t>(pos_ids) & 3u))
+        return FDLLM_ERR_ALIGN;
+    int st = set_device(h);
+    if (st) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const Plan p = make_plan(h, nq);
+    if (p.attn_family == FAMILY_MFMA && p.splits > 1 && (size_t)c.B * c.Hkv * p.splits * p.Rpad > h->apart_rows)
+        return FDLLM_ERR_ALLOC;   // not reached: the workspace is sized for every nq
+    AttnArgs aa{};
+    aa.qbuf = h->qbuf; aa.Kc = Kc; aa.Vc = Vc; aa.sideK = h->sideK; aa.sideV = h->sideV;
+    aa.pos_ids = pos_ids; aa.vis = vis; aa.O = O; aa.LSE = LSE;
+    aa.apart = h->apart; aa.aml = h->aml; aa.aticket = h->aticket;
+    aa.B = c.B; aa.N = c.N; aa.H = c.H; aa.Hkv = c.Hkv; aa.dh = c.dh; aa.G = h->G; aa.nq = nq; aa.q_max = c.q_max;
+    aa.R = p.R; aa.Rpad = p.Rpad; aa.splits = p.splits; aa.keys_per_split = p.keys_per_split;
+    aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.dh));
+    hipError_t e = p.attn_family == FAMILY_MFMA ? launch_attn_mfma(aa, s) : launch_attn_generic(aa, c.dtype, s);
+    return hip_status(e);
+}
+
+int fdllm_fused_step(fdllm_handle_t h, const void* X, int32_t x_rows, const int32_t* Q_idx,
+                     const int32_t* pos_ids, int32_t nq, const uint8_t* vis, const void* W, void* Kc,
+                     void* Vc, void* O, float* LSE, void* stream)
+{
+    if (!h) return FDLLM_ERR_ARG;
+    if (nq < 0 || nq > h->cfg.q_max || x_rows < 1) return FDLLM_ERR_SHAPE;
+    if (nq == 0) return FDLLM_OK;
+    // check every argument of both phases before launching either
+    if (!X || !Q_idx || !pos_ids || !W || !Kc || !Vc || !O || !LSE) return FDLLM_ERR_ARG;
+    if (!aligned16(O) || (reinterpret_cast<uintptr_t>(LSE) & 3u)) return FDLLM_ERR_ALIGN;
+    int st = fdllm_step_project(h, X, x_rows, Q_idx, pos_ids, nq, W, Kc, Vc, stream);
+    if (st) return st;
+    return fdllm_step_attend(h, pos_ids, nq, vis, Kc, Vc, O, LSE, stream);
+}
+
+int fdllm_cache_destroy(fdllm_handle_t h)
+{
+    if (!h) return FDLLM_OK;
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(h->device);
+    hipError_t e = hipDeviceSynchronize();
+    free_ws(h);
+    if (cur >= 0) (void)hipSetDevice(cur);
+    delete h;
+    return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,86 @@
+// fdllm_common.h -- internal declarations shared by the HIP kernels and the
+// C-ABI host code of libfdllm.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fdllm {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Everything a launch of the projection kernels needs.  Rows of the
+// projection are m = b * rows_per_seq + j.
+struct ProjArgs {
+    const void* X;          // [B, x_rows, d]
+    const void* W;          // [(H + 2 Hkv) dh, d]
+    const int32_t* Q_idx;   // [B, nq]  (NULL in prefill mode: row j is X row j)
+    const int32_t* pos_ids; // [B, nq]  (NULL in prefill mode: position j)
+    const float2* rope;     // [N, dh/2] (cos, sin) of pos * base^(-2e/dh)
+    void* Kc;               // [B, Hkv, N, dh]
+    void* Vc;
+    float* qbuf;            // [B, Hkv, q_max * G, dh] fp32, row j * G + hl  (unused in prefill)
+    void* sideK;            // [B, Hkv, q_max, dh]: rows whose position an earlier row owns
+    void* sideV;
+    float* gpart;           // split-d partial sums
+    uint32_t* gticket;      // one counter per output tile, zero between launches
+    int B, N, d, H, Hkv, dh, G;
+    int x_rows;
+    int rows_per_seq;       // nq, or N in prefill mode
+    int q_max;
+    int prefill;            // 1: k/v heads only, no q, no side buffer
+    int splitk;
+};
+
+struct AttnArgs {
+    const float* qbuf;      // [B, Hkv, q_max * G, dh] fp32 (q is not rounded to storage)
+    const void* Kc;         // [B, Hkv, N, dh]
+    const void* Vc;
+    const void* sideK;      // [B, Hkv, q_max, dh]
+    const void* sideV;
+    const int32_t* pos_ids; // [B, nq]
+    const uint8_t* vis;     // [B, nq, nq] or NULL
+    void* O;                // [B, nq, H, dh]
+    float* LSE;             // [B, nq, H]
+    float* apart;           // [B * Hkv, splits, Rpad, dh]  unnormalised partial outputs
+    float* aml;             // [B * Hkv, splits, Rpad, 2]    (max in log2 units, sum)
+    uint32_t* aticket;      // [B * Hkv], zero between launches
+    int B, N, H, Hkv, dh, G, nq, q_max;
+    int R;                  // nq * G query rows per (sequence, kv head)
+    int Rpad;               // R rounded up for the partial buffers
+    int splits;
+    int keys_per_split;     // multiple of the kernel's tile width
+    float scale_log2;       // log2(e) / sqrt(dh)
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_proj_generic(const ProjArgs& a, int dtype, hipStream_t s);
+hipError_t launch_attn_generic(const AttnArgs& a, int dtype, hipStream_t s);
+hipError_t launch_proj_mfma(const ProjArgs& a, hipStream_t s);
+hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
+
+// Tile geometry of the MFMA kernels, needed by the host planner.
+int proj_mfma_block_m(int M);
+int attn_mfma_tile_keys(int R);
+
+// Conversions between storage types and fp32.
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return (bf16)x; }  // RNE
+
+// XCD-aware workgroup order: consecutive workgroup ids are dispatched round
+// robin over the 8 XCDs, so logical tile t runs on XCD t / per.  The grid is
+// padded to a multiple of 8; ids past `total` return -1.
+__device__ __forceinline__ int xcd_remap(int bid, int total)
+{
+    const int per = (total + 7) >> 3;
+    const int logical = (bid & 7) * per + (bid >> 3);
+    return logical < total ? logical : -1;
+}
+
+}  // namespace fdllm

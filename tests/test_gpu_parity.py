@@ -1,0 +1,180 @@
+"""GPU parity of the fused KV-cache step (HIP path through the C ABI) against
+the fp64 oracle, on seeded inputs: the five layer workloads at full size in
+the launch configuration the bench times, small cases that span several
+tiles with ragged tails, duplicates and masks, forced split counts, the
+scalar kernel family, determinism, the views' mutual invisibility, edge
+positions and empty key sets."""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+from io_aware_kv_amd.workloads import LayerShape, make_random_case, make_workload
+from parity_util import compare, log, run_gpu, run_oracle
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+def test_layer_workload_full_size(cid):
+    log("case: workload %d full size" % cid)
+    wl = make_workload(cid)
+    g = run_gpu(wl)
+    r = run_oracle(wl, g["K0"], g["V0"])
+    compare(wl, g, r, "workload%d" % cid)
+
+
+@pytest.mark.parametrize("layer", [0, 31])
+def test_large_batch_stack_layers(layer):
+    log("case: workload 5 layer %d" % layer)
+    wl = make_workload(5, layer=layer)
+    g = run_gpu(wl)
+    r = run_oracle(wl, g["K0"], g["V0"])
+    compare(wl, g, r, "workload5-layer%d" % layer)
+
+
+SMALL = [
+    # (label, shape kwargs, nq, case kwargs)
+    ("mha-ragged", dict(B=2, N=300, d_model=256, H=4, Hkv=4, dh=128), 13, dict()),
+    ("gqa-dups-mask", dict(B=2, N=333, d_model=192, H=8, Hkv=2, dh=128), 21,
+     dict(n_extra_rows=6, dup_frac=0.25, masked_vis=True)),
+    ("gqa-dups-nomask", dict(B=3, N=129, d_model=128, H=6, Hkv=3, dh=128), 9,
+     dict(n_extra_rows=4, dup_frac=0.4)),
+    ("many-rows", dict(B=1, N=257, d_model=256, H=16, Hkv=2, dh=128), 20, dict(masked_vis=True)),
+    ("single-row", dict(B=2, N=70, d_model=128, H=2, Hkv=1, dh=128), 1, dict()),
+    ("fp32-generic", dict(B=2, N=50, d_model=64, H=4, Hkv=2, dh=32, dtype=torch.float32), 7,
+     dict(n_extra_rows=2, dup_frac=0.3, masked_vis=True)),
+    ("fp32-dh64", dict(B=1, N=90, d_model=96, H=2, Hkv=2, dh=64, dtype=torch.float32), 5, dict()),
+]
+
+
+@pytest.mark.parametrize("label,shape,nq,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_small_cases(label, shape, nq, kw):
+    log("case: small %s" % label)
+    ls = LayerShape(**shape)
+    wl = make_random_case(ls, nq, seed=zlib.crc32(label.encode()) % 10000, w_std=0.05, **kw)
+    g = run_gpu(wl)
+    r = run_oracle(wl, g["K0"], g["V0"])
+    compare(wl, g, r, label)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 8])
+@pytest.mark.parametrize("splitk", [1, 3])
+def test_forced_splits(splits, splitk):
+    log("case: splits %d splitk %d" % (splits, splitk))
+    ls = LayerShape(B=2, N=1000, d_model=384, H=4, Hkv=2, dh=128)
+    wl = make_random_case(ls, 11, seed=77, n_extra_rows=3, dup_frac=0.2, masked_vis=True, w_std=0.05)
+    g = run_gpu(wl, tuning={"attn_splits": splits, "gemm_splitk": splitk})
+    assert g["plan"]["attn_splits"] == splits and g["plan"]["gemm_splitk"] == splitk
+    r = run_oracle(wl, g["K0"], g["V0"])
+    compare(wl, g, r, "splits%d-splitk%d" % (splits, splitk))
+
+
+def test_generic_family_on_bf16():
+    log("case: generic family bf16")
+    ls = LayerShape(B=2, N=200, d_model=256, H=4, Hkv=2, dh=128)
+    wl = make_random_case(ls, 10, seed=5, n_extra_rows=3, dup_frac=0.3, masked_vis=True, w_std=0.05)
+    g = run_gpu(wl, tuning={"kernel_family": 2})
+    assert g["plan"]["kernel_family"] == 2
+    r = run_oracle(wl, g["K0"], g["V0"])
+    compare(wl, g, r, "generic-bf16")
+
+
+def test_q_max_larger_than_nq_and_edge_positions():
+    log("case: edge positions")
+    ls = LayerShape(B=2, N=160, d_model=128, H=2, Hkv=2, dh=128)
+    wl = make_random_case(ls, 4, seed=6, positions=[[0, 159, 1, 158], [159, 0, 80, 81]], w_std=0.05)
+    g = run_gpu(wl, q_max=40)
+    r = run_oracle(wl, g["K0"], g["V0"])
+    compare(wl, g, r, "edges")
+
+
+def test_determinism_bit_identical_reruns():
+    log("case: determinism")
+    wl = make_workload(3)
+    g = run_gpu(wl, repeat=3)
+    (O1, L1, K1, V1), (O2, L2, K2, V2) = g["runs"][1], g["runs"][2]
+    assert torch.equal(O1.view(torch.int16), O2.view(torch.int16))
+    assert torch.equal(L1.view(torch.int32), L2.view(torch.int32))
+    assert torch.equal(K1.view(torch.int16), K2.view(torch.int16))
+    assert torch.equal(V1.view(torch.int16), V2.view(torch.int16))
+
+
+def test_views_mutually_invisible_on_gpu():
+    """Perturbing the draft view's hidden states leaves the [MASK] view's O
+    and LSE bit-identical (and the other way round)."""
+    log("case: view invisibility")
+    wl = make_workload(3)
+    groups = wl.meta["groups"]
+    base = run_gpu(wl)
+    for view, other, delta in (("draft", "mask", 3.0), ("mask", "draft", -2.0)):
+        X2 = wl.X.clone()
+        for b in range(wl.shape.B):
+            rows = [int(wl.Q_idx[b, i]) for i, t in enumerate(groups[b]) if t == view]
+            X2[b, rows] = (X2[b, rows].float() + delta).to(X2.dtype)
+        pert = run_gpu(wl, X=X2)
+        for b in range(wl.shape.B):
+            idx = [i for i, t in enumerate(groups[b]) if t == other]
+            assert torch.equal(pert["O"][b, idx].view(torch.int16), base["O"][b, idx].view(torch.int16))
+            assert torch.equal(pert["LSE"][b, idx].view(torch.int32), base["LSE"][b, idx].view(torch.int32))
+            moved = [i for i, t in enumerate(groups[b]) if t == view]
+            assert not torch.equal(pert["O"][b, moved], base["O"][b, moved])
+
+
+def test_empty_key_set_gives_zero_and_minus_inf():
+    log("case: empty key set")
+    ls = LayerShape(B=1, N=3, d_model=128, H=2, Hkv=1, dh=128)
+    wl = make_random_case(ls, 3, seed=8, positions=[[2, 0, 1]], w_std=0.05)
+    wl.vis = torch.zeros((1, 3, 3), dtype=torch.uint8)
+    wl.vis[0, 1, 1] = 1
+    g = run_gpu(wl)
+    r = run_oracle(wl, g["K0"], g["V0"])
+    assert torch.all(g["O"][0, [0, 2]].float() == 0)
+    assert torch.all(torch.isneginf(g["LSE"][0, [0, 2]]))
+    compare(wl, g, r, "empty-keys")
+
+
+def test_prefill_matches_oracle():
+    import oracle
+    from parity_util import rel_err, shape_of, round_mode
+    log("case: prefill")
+    for ls in (LayerShape(B=1, N=64, d_model=128, H=4, Hkv=4, dh=32, dtype=torch.float32),
+               LayerShape(B=2, N=200, d_model=256, H=4, Hkv=2, dh=128)):
+        wl = make_random_case(ls, 1, seed=9, w_std=0.05)
+        g = run_gpu(wl)
+        Kr, Vr = oracle.prefill(shape_of(ls), wl.X_pre, wl.W, round_mode(ls.dtype))
+        tol = 1e-4 if ls.dtype == torch.float32 else 2e-2
+        assert rel_err(g["K0"].double().numpy(), Kr) <= tol
+        assert rel_err(g["V0"].double().numpy(), Vr) <= tol
+
+
+def test_status_codes_on_gpu():
+    from io_aware_kv_amd.binding import FdllmError, FusedKVCache
+    log("case: status codes")
+    import os
+    ls = LayerShape(B=1, N=64, d_model=128, H=2, Hkv=2, dh=128)
+    wl = make_random_case(ls, 4, seed=10)
+    dev = "cuda"
+    W = wl.W.to(dev)
+    X = wl.X.to(dev)
+    Kc = torch.zeros((1, 2, 64, 128), dtype=torch.bfloat16, device=dev)
+    Vc = torch.zeros_like(Kc)
+    fk = FusedKVCache(1, 64, 128, 2, 2, 128, 4)
+    O = torch.empty((1, 5, 2, 128), dtype=torch.bfloat16, device=dev)
+    LSE = torch.empty((1, 5, 2), dtype=torch.float32, device=dev)
+    Q5 = torch.zeros((1, 5), dtype=torch.int32, device=dev)
+    with pytest.raises(FdllmError) as e:
+        fk.step(X, Q5, Q5, None, W, Kc, Vc, O, LSE)
+    assert e.value.status == -2
+    bad = torch.tensor([[0, 1, 2, 64]], dtype=torch.int32, device=dev)
+    O4 = torch.empty((1, 4, 2, 128), dtype=torch.bfloat16, device=dev)
+    L4 = torch.empty((1, 4, 2), dtype=torch.float32, device=dev)
+    os.environ["FDLLM_VALIDATE"] = "1"
+    try:
+        with pytest.raises(FdllmError) as e:
+            fk.step(X, bad - 1, bad, None, W, Kc, Vc, O4, L4)
+        assert e.value.status == -4
+    finally:
+        del os.environ["FDLLM_VALIDATE"]
+    fk.close()
