@@ -85,7 +85,7 @@ typedef struct {
 /* Launch-shape overrides for sweeps; 0 keeps the library's choice. */
 typedef struct {
     int32_t attn_splits;    /* cache splits per (sequence, kv head) in the attention */
-    int32_t gemm_splitk;    /* d_model splits of the projection */
+    int32_t gemm_splitk;    /* reserved: the projection does not split d_model (plan reports 1) */
     int32_t kernel_family;  /* 0 auto, 1 tiled MFMA (bf16 only), 2 generic scalar */
 } fdllm_tuning_t;
 

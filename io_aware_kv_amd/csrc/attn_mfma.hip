@@ -6,31 +6,37 @@
 // review, "How It Works: A Concrete Example", Step 1: Draft; alanhou.org,
 // "Core Mechanism" item 1), and in the verification pass the draft view and
 // the [MASK] view share positions but cannot see each other (jaehun.me,
-// "Flash-Verify", Fig. 2).  The pages' kernel targets SRAM and tensor cores of
-// another GPU; this one is laid out for CDNA4:
+// "Flash-Verify", Fig. 2).  The pages' kernel targets the SRAM and tensor
+// cores of another GPU; this one is laid out for CDNA4:
 //
 //  * one workgroup per (sequence, kv head, cache split): all nq * H/Hkv query
 //    rows that share a kv head are packed as the MFMA N dimension, so every
-//    K/V byte is read from HBM exactly once per step;
-//  * K and V tiles are streamed with coalesced 16 B loads into registers
-//    (prefetch of the next tile overlaps the current tile's math), then
-//    stored row-major into padded LDS;
+//    K/V byte is read from HBM once per step;
+//  * one producer wave streams K/V tiles straight into a ring of LDS stages
+//    with global_load_lds (16 B per lane, no registers), keeping up to three
+//    tiles (~96 KB) in flight per CU; it waits on its own vmcnt and releases
+//    each stage with a barrier.  The consumer waves never issue global loads
+//    in the loop, they only read LDS and run MFMAs;
+//  * LDS rows are 256 B with their 16 B chunks XOR-swizzled by the row index,
+//    which makes both fragment read patterns below bank-conflict free;
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 leaves each lane with one query
 //    row, so the row max needs two cross-lane steps and the rescale of the
-//    output accumulators is lane-local;
-//  * O^T += V^T P^T takes V^T fragments straight from the row-major LDS tile
-//    with ds_read_b64_tr_b16 (gfx950 transpose read) and P^T from the score
-//    registers, so P never touches LDS;
-//  * waves split either the keys of a tile (few query rows; partial softmax
-//    states are merged through LDS at the end) or the query rows (many rows);
-//  * the last workgroup of a (sequence, kv head) to finish (atomic ticket)
-//    merges the splits' (max, sum, output) partials into O and LSE.
+//    output accumulators is lane-local; q enters as bf16 hi + lo parts so the
+//    scores keep q's fp32 accumulation precision;
+//  * O^T += V^T P^T takes V^T fragments from the row-major tile with
+//    ds_read_b64_tr_b16 (gfx950 transpose read) and P^T from the score
+//    registers, so P never goes through LDS;
+//  * consumer waves split the query rows and the keys of a tile; key-split
+//    waves merge their softmax states through LDS at the end;
+//  * with several cache splits, each writes its (max, sum, output) partial
+//    state and a small second kernel merges them into O and LSE (a kernel
+//    boundary is far cheaper than a device-scope fence per workgroup).
 //
 // Key set of query row i (same definition as the CPU oracle): every cache
-// position not written by this step, plus each new row j that i may see.
-// A position written by its first row j is reached through the cache (the
+// position not written by this step, plus each new row j that i may see.  A
+// position written by its first row j is reached through the cache (the
 // projection kernel stored it there) and gated by vis[i][j]; later rows at a
-// shared position live in the side buffer and are attended as an extra tile.
+// shared position live in the side buffer and are attended as extra tiles.
 #include "fdllm_common.h"
 
 namespace fdllm {
@@ -38,12 +44,50 @@ namespace fdllm {
 namespace {
 
 constexpr int kDH = 128;
-constexpr int kRowPad = kDH + 8;     // LDS row of K/V tiles (bf16): 272 B
+constexpr int kRowB = kDH * 2;   // bytes of one K or V row
 
 typedef __bf16 bf16x4g __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef __attribute__((address_space(3))) bf16x4g lds_bf16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
 
-__device__ __forceinline__ bf16x8 read_vt_frag(const bf16* p0, const bf16* p1)
+template <int RG, int NWR, int NWK>
+struct AttnCfg {
+    static constexpr int NC = NWR * NWK;            // consumer waves
+    static constexpr int NT = (NC + 1) * 64;        // + one producer wave
+    static constexpr int KW = 32;                   // keys per consumer wave per tile
+    static constexpr int TK = KW * NWK;             // keys per tile
+    static constexpr int STAGE = TK * 2 * kRowB;    // K rows then V rows
+    static constexpr int NS = (128 * 1024) / STAGE; // ring of 128 KB
+    static constexpr int DMA = STAGE / 1024;        // producer instructions per stage
+    static constexpr int MERGE = (NWK / 2) * NWR * RG * 64 * (32 + 2) * 4;
+    static constexpr int SCRATCH = NS * STAGE > MERGE ? NS * STAGE : MERGE;
+    static_assert(NS >= 2 && NS * STAGE == 128 * 1024, "stage ring");
+};
+
+// Producer wait: stage `it` has landed once at most `younger` * DMA of this
+// wave's loads are outstanding; then release the stage to the consumers.
+template <int DMA>
+__device__ __forceinline__ void producer_sync(int younger)
+{
+#define FDLLM_PSYNC(N) asm volatile("s_waitcnt vmcnt(" #N ")\n\ts_barrier" ::: "memory")
+    const int n = younger * DMA;
+    if (n >= 63) FDLLM_PSYNC(63);
+    else if (n >= 48) FDLLM_PSYNC(48);
+    else if (n >= 32) FDLLM_PSYNC(32);
+    else if (n >= 16) FDLLM_PSYNC(16);
+    else FDLLM_PSYNC(0);
+#undef FDLLM_PSYNC
+}
+
+// Consumer side of the same barrier: its LDS reads of the previous stage have
+// returned (so the producer may overwrite that stage).
+__device__ __forceinline__ void consumer_sync()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ bf16x8 read_vt_frag(const unsigned char* p0, const unsigned char* p1)
 {
     const bf16x4g a = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p0));
     const bf16x4g b = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p1));
@@ -53,69 +97,84 @@ __device__ __forceinline__ bf16x8 read_vt_frag(const bf16* p0, const bf16* p1)
     return r;
 }
 
-// RG row groups of 16 query rows per wave; NWR waves split the rows, NWK waves
-// split the keys of a tile; KW keys per wave per tile.
-template <int RG, int NWR, int NWK, int KW>
-struct AttnCfg {
-    static constexpr int NW = NWR * NWK;
-    static constexpr int NT = NW * 64;
-    static constexpr int TK = KW * NWK;         // keys per tile
-    static constexpr int KB = KW / 16;          // 16-key blocks per wave
-    static constexpr int CHUNKS = TK * 2 * (kDH / 8);   // 16 B chunks of K+V per tile
-    static constexpr int CPT = (CHUNKS + NT - 1) / NT;
-    static constexpr int TILE_BYTES = 2 * TK * kRowPad * 2;
-    static constexpr int MERGE_BYTES = (NWK / 2) * NWR * RG * 64 * (32 + 2) * 4;
-    static constexpr int SCRATCH = TILE_BYTES > MERGE_BYTES ? TILE_BYTES : MERGE_BYTES;
-    static_assert(KW % 32 == 0, "PV consumes 32 keys per MFMA");
-};
+// One stage of the ring: TK cache rows from `base` (or side-buffer rows
+// sDup[base ...] for the duplicate tiles), K then V, as 1 KB DMA blocks of 4
+// rows; chunk c of row r lands in slot c ^ (r & 15).
+template <int TK, int DMA>
+__device__ __forceinline__ void issue_stage(unsigned char* st, bool dup, int base, int k1, int ndup,
+                                            const int* sDup, const unsigned char* Kg, const unsigned char* Vg,
+                                            const unsigned char* SKg, const unsigned char* SVg, int lane)
+{
+    const int srow = lane >> 4, slot = lane & 15;
+#pragma unroll
+    for (int i = 0; i < DMA / 2; ++i) {
+        const int row = 4 * i + srow;
+        const int chunk = slot ^ (row & 15);
+        size_t src;
+        if (!dup) {
+            const int key = min(base + row, k1 - 1);   // rows past the split are masked later
+            src = (size_t)key * kRowB + chunk * 16;
+        } else {
+            const int kk = base + row;
+            const int j = kk < ndup ? sDup[kk] : sDup[0];
+            src = (size_t)j * kRowB + chunk * 16;
+        }
+        __builtin_amdgcn_global_load_lds((glb_void*)((dup ? SKg : Kg) + src), (lds_void*)(st + i * 1024), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((glb_void*)((dup ? SVg : Vg) + src),
+                                         (lds_void*)(st + TK * kRowB + i * 1024), 16, 0, 0);
+    }
+}
 
-struct StepInfo {
-    int b, g, bg, s, k0, k1;
-};
-
-template <int RG, int NWR, int NWK, int KW>
-__global__ void __launch_bounds__(NWR * NWK * 64)
+template <int RG, int NWR, int NWK>
+__global__ void __launch_bounds__((NWR * NWK + 1) * 64)
 attn_mfma_kernel(AttnArgs a)
 {
-    using C = AttnCfg<RG, NWR, NWK, KW>;
+    using C = AttnCfg<RG, NWR, NWK>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    bf16* sK = (bf16*)smem;                         // [TK][kRowPad]
-    bf16* sV = sK + C::TK * kRowPad;                // [TK][kRowPad]
-    int16_t* sSlot = (int16_t*)(smem + C::SCRATCH); // [keys_per_split] owner row of written positions
-    int* sInt = (int*)(sSlot + ((a.keys_per_split + 1) & ~1));
-    int* sPos = sInt;                               // [nq]
-    int* sOwn = sPos + a.q_max;                     // [nq] 1 if the row owns its position
-    int* sDup = sOwn + a.q_max;                     // [nq] rows that do not own their position
-    int* sMisc = sDup + a.q_max;                    // [0] dup count, [1] last flag, [2..] tile flags
+    const int kps = a.keys_per_split;
+    const int nq = a.nq;
+    const int VW = (nq + 31) >> 5;                  // 32-bit words per visibility row
+    int16_t* sSlot = (int16_t*)(smem + C::SCRATCH); // [kps] owner row of written positions, -1
+    uint32_t* sVis = (uint32_t*)(smem + C::SCRATCH + 2 * ((kps + 1) & ~1));   // [nq][VW]
+    int* sPos = (int*)(sVis + (size_t)nq * VW);     // [nq]
+    int* sOwn = sPos + nq;                          // [nq] 1 if the row owns its position
+    int* sDup = sOwn + nq;                          // [nq] rows that do not own their position
+    int* sMisc = sDup + nq;                         // [0] dup count, [2..] tile flags
 
     const int total = a.B * a.Hkv * a.splits;
     const int logical = xcd_remap(blockIdx.x, total);
     if (logical < 0) return;
-    StepInfo si;
-    si.bg = logical / a.splits;
-    si.s = logical - si.bg * a.splits;
-    si.b = si.bg / a.Hkv;
-    si.g = si.bg - si.b * a.Hkv;
-    si.k0 = si.s * a.keys_per_split;
-    si.k1 = min(a.N, si.k0 + a.keys_per_split);
+    const int bg = logical / a.splits;
+    const int split = logical - bg * a.splits;
+    const int b = bg / a.Hkv;
+    const int g = bg - b * a.Hkv;
+    const int k0 = split * kps;
+    const int k1 = min(a.N, k0 + kps);
+    const int nkeys = k1 - k0;
+    const int n_main = (nkeys + C::TK - 1) / C::TK;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wk = wave % NWK, wr = wave / NWK;
+    // wave-uniform in an SGPR, so branches on it stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
-    const int nq = a.nq;
     const int G = a.G;
-    const int nkeys = si.k1 - si.k0;
-    const int ntiles = (nkeys + C::TK - 1) / C::TK;
     int* sTileFlag = sMisc + 2;
 
-    // --- per-sequence bookkeeping: positions, ownership, duplicates, gating slots
-    const int32_t* pos_b = a.pos_ids + (size_t)si.b * nq;
+    // ---- per-sequence bookkeeping: positions, ownership, duplicates, gating
+    const int32_t* pos_b = a.pos_ids + (size_t)b * nq;
     for (int j = tid; j < nq; j += C::NT) sPos[j] = pos_b[j];
     if (a.vis) {
         for (int k = tid; k < nkeys; k += C::NT) sSlot[k] = -1;
-        for (int t = tid; t < ntiles; t += C::NT) sTileFlag[t] = 0;
+        for (int t = tid; t < n_main; t += C::NT) sTileFlag[t] = 0;
+        const uint8_t* vb = a.vis + (size_t)b * nq * nq;
+        for (int w = tid; w < nq * VW; w += C::NT) {
+            const int i = w / VW, j0 = (w - i * VW) * 32;
+            uint32_t bits = 0;
+            for (int j = j0; j < min(nq, j0 + 32); ++j)
+                bits |= (vb[(size_t)i * nq + j] ? 1u : 0u) << (j - j0);
+            sVis[w] = bits;
+        }
     }
     __syncthreads();
     for (int j = tid; j < nq; j += C::NT) {
@@ -124,9 +183,9 @@ attn_mfma_kernel(AttnArgs a)
             if (sPos[q] == sPos[j]) { own = 0; break; }
         sOwn[j] = own;
         const int p = sPos[j];
-        if (own && a.vis && p >= si.k0 && p < si.k1) {
-            sSlot[p - si.k0] = (int16_t)j;
-            sTileFlag[(p - si.k0) / C::TK] = 1;
+        if (own && a.vis && p >= k0 && p < k1) {
+            sSlot[p - k0] = (int16_t)j;
+            sTileFlag[(p - k0) / C::TK] = 1;
         }
     }
     __syncthreads();
@@ -137,40 +196,14 @@ attn_mfma_kernel(AttnArgs a)
         sMisc[0] = n;
     }
     __syncthreads();
-    const int ndup = (si.s == 0) ? sMisc[0] : 0;
+    const int ndup = (split == 0) ? sMisc[0] : 0;
+    const int ntot = n_main + (ndup + C::TK - 1) / C::TK;
 
-    // --- query fragments: lane holds row (wr*RG + rg)*16 + lr, dims 32c + 8lg .. +7.
-    // q arrives in fp32 and is split into bf16 hi + lo parts (q = hi + lo to
-    // 16 significant bits), so the scores keep q's accumulation precision.
-    const float* qbase = a.qbuf + (size_t)si.bg * a.q_max * G * kDH;
-    bf16x8 qf[RG][4], ql[RG][4];
-    int qrow_query[RG];   // query index of the lane's row, -1 for padding rows
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-        const int row = (wr * RG + rg) * 16 + lr;
-        qrow_query[rg] = row < a.R ? row / G : -1;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            float x[8];
-            if (row < a.R) {
-                const float4 u = *(const float4*)(qbase + (size_t)row * kDH + c * 32 + lg * 8);
-                const float4 v = *(const float4*)(qbase + (size_t)row * kDH + c * 32 + lg * 8 + 4);
-                x[0] = u.x; x[1] = u.y; x[2] = u.z; x[3] = u.w;
-                x[4] = v.x; x[5] = v.y; x[6] = v.z; x[7] = v.w;
-            } else {
-                for (int e = 0; e < 8; ++e) x[e] = 0.f;
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const bf16 hi = (bf16)x[e];
-                qf[rg][c][e] = hi;
-                ql[rg][c][e] = (bf16)(x[e] - (float)hi);
-            }
-        }
-    }
-    bool rg_live[RG];
-#pragma unroll
-    for (int rg = 0; rg < RG; ++rg) rg_live[rg] = (wr * RG + rg) * 16 < a.R;
+    const size_t cache_off = (size_t)bg * a.N * kDH;
+    const unsigned char* Kg = (const unsigned char*)((const bf16*)a.Kc + cache_off);
+    const unsigned char* Vg = (const unsigned char*)((const bf16*)a.Vc + cache_off);
+    const unsigned char* SKg = (const unsigned char*)((const bf16*)a.sideK + (size_t)bg * a.q_max * kDH);
+    const unsigned char* SVg = (const unsigned char*)((const bf16*)a.sideV + (size_t)bg * a.q_max * kDH);
 
     float m_run[RG], l_run[RG];
     f32x4 o[RG][8];
@@ -181,177 +214,216 @@ attn_mfma_kernel(AttnArgs a)
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[rg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    const int wk = wave % NWK, wr = wave / NWK;    // consumer coordinates
 
-    const size_t cache_off = (size_t)si.bg * a.N * kDH;
-    const bf16* Kg = (const bf16*)a.Kc + cache_off;
-    const bf16* Vg = (const bf16*)a.Vc + cache_off;
-    const bf16* SKg = (const bf16*)a.sideK + (size_t)si.bg * a.q_max * kDH;
-    const bf16* SVg = (const bf16*)a.sideV + (size_t)si.bg * a.q_max * kDH;
-    const uint8_t* vis_b = a.vis ? a.vis + (size_t)si.b * nq * nq : nullptr;
-
-    uint4 pre[C::CPT];
-    // tile loader: cache rows [t0, t0+TK) (mode 0) or side rows sDup[t0 ...] (mode 1)
-    auto load_tile = [&](int t0, int mode) {
-#pragma unroll
-        for (int i = 0; i < C::CPT; ++i) {
-            const int c = tid + i * C::NT;
-            pre[i] = make_uint4(0, 0, 0, 0);
-            if (c < C::CHUNKS) {
-                const int isv = c >= C::TK * 16;
-                const int rem = c - isv * C::TK * 16;
-                const int row = rem >> 4, part = rem & 15;
-                const int key = t0 + row;
-                if (mode == 0) {
-                    if (key < si.k1)
-                        pre[i] = *(const uint4*)((isv ? Vg : Kg) + (size_t)key * kDH + part * 8);
-                } else if (key < ndup) {
-                    const int j = sDup[key];
-                    pre[i] = *(const uint4*)((isv ? SVg : SKg) + (size_t)j * kDH + part * 8);
-                }
+    if (wave == C::NC) {
+        // ================= producer wave: K/V tiles -> LDS ring =================
+        int issued = 0;
+        for (; issued < min(C::NS - 1, ntot); ++issued) {
+            const bool dup = issued >= n_main;
+            issue_stage<C::TK, C::DMA>(smem + (issued % C::NS) * C::STAGE, dup,
+                                       dup ? (issued - n_main) * C::TK : k0 + issued * C::TK, k1, ndup,
+                                       sDup, Kg, Vg, SKg, SVg, lane);
+        }
+        for (int t = 0; t < ntot; ++t) {
+            producer_sync<C::DMA>(issued - t - 1);
+            if (issued < ntot) {
+                const bool dup = issued >= n_main;
+                issue_stage<C::TK, C::DMA>(smem + (issued % C::NS) * C::STAGE, dup,
+                                           dup ? (issued - n_main) * C::TK : k0 + issued * C::TK, k1, ndup,
+                                           sDup, Kg, Vg, SKg, SVg, lane);
+                ++issued;
             }
         }
-    };
-    auto store_tile = [&]() {
-#pragma unroll
-        for (int i = 0; i < C::CPT; ++i) {
-            const int c = tid + i * C::NT;
-            if (c < C::CHUNKS) {
-                const int isv = c >= C::TK * 16;
-                const int rem = c - isv * C::TK * 16;
-                const int row = rem >> 4, part = rem & 15;
-                *(uint4*)((isv ? sV : sK) + row * kRowPad + part * 8) = pre[i];
-            }
-        }
-    };
-
-    // one tile of math for this wave: keys [wk*KW, wk*KW+KW) of the LDS tile
-    auto compute_tile = [&](int t0, int mode) {
-        f32x4 sc[RG][C::KB];
-#pragma unroll
-        for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb) sc[rg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const bf16x8 kf = *(const bf16x8*)(sK + (wk * KW + kb * 16 + lr) * kRowPad + c * 32 + lg * 8);
-#pragma unroll
-                for (int rg = 0; rg < RG; ++rg)
-                    if (rg_live[rg]) {
-                        sc[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[rg][c], sc[rg][kb], 0, 0, 0);
-                        sc[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, ql[rg][c], sc[rg][kb], 0, 0, 0);
-                    }
-            }
-        }
-        // scale, mask, online softmax; lane: row lr of each group, keys kb*16 + 4lg + i
-        const bool gate = (mode == 1) || (a.vis && sTileFlag[(t0 - si.k0) / C::TK]);
+    } else {
+        // ================= consumer waves =================
+        // query fragments: lane holds row (wr*RG + rg)*16 + lr, dims 32c + 8lg .. +7,
+        // split into bf16 hi + lo so the scores keep q's fp32 precision
+        const float* qbase = a.qbuf + (size_t)bg * a.q_max * G * kDH;
+        bf16x8 qh[RG][4], ql[RG][4];
+        int qrow[RG];
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
-            if (!rg_live[rg]) continue;
-            float mx = -INFINITY;
+            const int row = (wr * RG + rg) * 16 + lr;
+            qrow[rg] = row < a.R ? row / G : -1;
 #pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb)
+            for (int c = 0; c < 4; ++c) {
+                float x[8];
+                if (row < a.R) {
+                    // scores come out of the MFMA already in log2 units
+                    const f32x4 u = *(const f32x4*)(qbase + (size_t)row * kDH + c * 32 + lg * 8) * a.scale_log2;
+                    const f32x4 v = *(const f32x4*)(qbase + (size_t)row * kDH + c * 32 + lg * 8 + 4) * a.scale_log2;
+                    x[0] = u[0]; x[1] = u[1]; x[2] = u[2]; x[3] = u[3];
+                    x[4] = v[0]; x[5] = v[1]; x[6] = v[2]; x[7] = v[3];
+                } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int kl = wk * KW + kb * 16 + lg * 4 + i;   // key within the tile
-                    float s = sc[rg][kb][i] * a.scale_log2;
-                    if (mode == 0) {
-                        const int key = t0 + kl;
-                        if (key >= si.k1) s = -INFINITY;
-                        else if (gate) {
-                            const int slot = sSlot[key - si.k0];
-                            if (slot >= 0 && (qrow_query[rg] < 0 || !vis_b[(size_t)qrow_query[rg] * nq + slot]))
-                                s = -INFINITY;
-                        }
-                    } else {
-                        const int key = t0 + kl;
-                        if (key >= ndup) s = -INFINITY;
-                        else if (vis_b) {
-                            const int j = sDup[key];
-                            if (qrow_query[rg] < 0 || !vis_b[(size_t)qrow_query[rg] * nq + j]) s = -INFINITY;
-                        }
-                    }
-                    sc[rg][kb][i] = s;
-                    mx = fmaxf(mx, s);
+                    for (int e = 0; e < 8; ++e) x[e] = 0.f;
                 }
-            mx = fmaxf(mx, __shfl_xor(mx, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run[rg], mx);
-            const float alpha = (m_run[rg] == -INFINITY) ? 0.f : exp2f(m_run[rg] - m_new);
-            const float msub = (m_new == -INFINITY) ? 0.f : m_new;
-            float lsum = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float p = exp2f(sc[rg][kb][i] - msub);   // exp2(-inf) = 0
-                    sc[rg][kb][i] = p;
-                    lsum += p;
+                for (int e = 0; e < 8; ++e) {
+                    const bf16 hi = (bf16)x[e];
+                    qh[rg][c][e] = hi;
+                    ql[rg][c][e] = (bf16)(x[e] - (float)hi);
                 }
-            l_run[rg] = l_run[rg] * alpha + lsum;
-            m_run[rg] = m_new;
-#pragma unroll
-            for (int db = 0; db < 8; ++db) o[rg][db] *= alpha;
+            }
         }
-        // O^T += V^T P^T, 32 keys per MFMA
+
+        for (int it = 0; it < ntot; ++it) {
+            consumer_sync();
+            const unsigned char* st = smem + (it % C::NS) * C::STAGE;
+            const unsigned char* sK = st;
+            const unsigned char* sV = st + C::TK * kRowB;
+            const bool dup = it >= n_main;
+
+            // ---- S^T = K Q^T for this wave's 32 keys
+            f32x4 sc[RG][2];
 #pragma unroll
-        for (int ch = 0; ch < KW / 32; ++ch) {
+            for (int rg = 0; rg < RG; ++rg) {
+                sc[rg][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                sc[rg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+            // all K fragments of the wave's 32 keys first (their LDS reads overlap),
+            // then the MFMAs; row groups past R run on zero q and are discarded
+            bf16x8 kf[2][4];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int row = wk * C::KW + kb * 16 + lr;
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    kf[kb][c] = *(const bf16x8*)(sK + row * kRowB + (((c * 4 + lg) ^ lr) << 4));
+            }
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int rg = 0; rg < RG; ++rg) {
+                        sc[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][c], qh[rg][c], sc[rg][kb], 0, 0, 0);
+                        sc[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][c], ql[rg][c], sc[rg][kb], 0, 0, 0);
+                    }
+
+            // ---- scale, mask, online softmax (lane: row lr, keys kb*16 + 4lg + i)
+            const int kl0 = wk * C::KW + lg * 4;                     // key within the tile
+            const bool gate = dup || (a.vis && sTileFlag[it]);
+            const int tbase = dup ? (it - n_main) * C::TK : k0 + it * C::TK;
+            // keys past the split (or past the duplicate list) are masked; a
+            // gated key (written this step, or a duplicate row) needs the
+            // query's visibility bit for its owning row
+            const int kend = dup ? ndup : k1;
+            bool keep_k[2][4];
+            int owner_k[2][4];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int key = tbase + kl0 + kb * 16 + i;
+                    keep_k[kb][i] = key < kend;
+                    owner_k[kb][i] = -1;
+                }
+            if (gate) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int key = tbase + kl0 + kb * 16 + i;
+                        if (keep_k[kb][i]) owner_k[kb][i] = dup ? sDup[key] : sSlot[key - k0];
+                        if (dup && !a.vis) owner_k[kb][i] = -1;
+                    }
+            }
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) {
+                float mx = -INFINITY;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        float s = sc[rg][kb][i];
+                        bool keep = keep_k[kb][i];
+                        if (gate) {
+                            const int j = owner_k[kb][i];
+                            const bool seen = qrow[rg] >= 0 &&
+                                              ((sVis[qrow[rg] * VW + (max(j, 0) >> 5)] >> (max(j, 0) & 31)) & 1u);
+                            keep = keep && (j < 0 || seen);
+                        }
+                        s = keep ? s : -INFINITY;
+                        sc[rg][kb][i] = s;
+                        mx = fmaxf(mx, s);
+                    }
+                mx = fmaxf(mx, __shfl_xor(mx, 16));
+                mx = fmaxf(mx, __shfl_xor(mx, 32));
+                // lazy rescale: a row's exponentials stay relative to a
+                // reference max that only moves when the row's max exceeds it
+                // by more than 2^8, so p <= 256 and the output accumulators are
+                // rescaled only a few times per split.  The decision is per
+                // row (each row's result depends on its own scores only); the
+                // whole block is skipped when no row of the wave grows.
+                const bool grow = mx > m_run[rg] + 8.f;
+                if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                    if (grow) {
+                        const float alpha = (m_run[rg] == -INFINITY) ? 0.f : exp2f(m_run[rg] - mx);
+                        l_run[rg] *= alpha;
+#pragma unroll
+                        for (int db = 0; db < 8; ++db) o[rg][db] *= alpha;
+                        m_run[rg] = mx;
+                    }
+                }
+                const float msub = (m_run[rg] == -INFINITY) ? 0.f : m_run[rg];
+                float lsum = 0.f;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float p = exp2f(sc[rg][kb][i] - msub);   // exp2(-inf) = 0
+                        sc[rg][kb][i] = p;
+                        lsum += p;
+                    }
+                l_run[rg] += lsum;
+            }
+
+            // ---- O^T += V^T P^T over the wave's 32 keys
             bf16x8 pf[RG];
 #pragma unroll
             for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    pf[rg][i] = (bf16)sc[rg][2 * ch][i];
-                    pf[rg][4 + i] = (bf16)sc[rg][2 * ch + 1][i];
+                    pf[rg][i] = (bf16)sc[rg][0][i];
+                    pf[rg][4 + i] = (bf16)sc[rg][1][i];
                 }
-            const int kbase = wk * KW + ch * 32 + lg * 4 + (lr >> 2);
+            const int rowA = wk * C::KW + 4 * lg + (lr >> 2);
+            const int rowB = rowA + 16;
+            bf16x8 vf[8];
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
-                const int col = db * 16 + (lr & 3) * 4;
-                const bf16x8 vf = read_vt_frag(sV + kbase * kRowPad + col, sV + (kbase + 16) * kRowPad + col);
+                const int chunk = 2 * db + ((lr & 3) >> 1);
+                const int half = (lr & 1) << 3;
+                const unsigned char* pA = sV + rowA * kRowB + ((chunk ^ (rowA & 15)) << 4) + half;
+                const unsigned char* pB = sV + rowB * kRowB + ((chunk ^ (rowB & 15)) << 4) + half;
+                vf[db] = read_vt_frag(pA, pB);
+            }
+#pragma unroll
+            for (int db = 0; db < 8; ++db)
 #pragma unroll
                 for (int rg = 0; rg < RG; ++rg)
-                    if (rg_live[rg])
-                        o[rg][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[rg], o[rg][db], 0, 0, 0);
-            }
+                    o[rg][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pf[rg], o[rg][db], 0, 0, 0);
         }
-    };
-
-    // --- main loop over the split's cache rows
-    if (ntiles > 0) load_tile(si.k0, 0);
-    for (int it = 0; it < ntiles; ++it) {
-        __syncthreads();                 // previous tile fully consumed
-        store_tile();
-        __syncthreads();
-        if (it + 1 < ntiles) load_tile(si.k0 + (it + 1) * C::TK, 0);
-        compute_tile(si.k0 + it * C::TK, 0);
-    }
-    // --- rows that share a position with an earlier row (first split only)
-    for (int t0 = 0; t0 < ndup; t0 += C::TK) {
-        load_tile(t0, 1);
-        __syncthreads();
-        store_tile();
-        __syncthreads();
-        compute_tile(t0, 1);
-    }
-
-    // --- finish per-lane sums (row lr is spread over the 4 lane groups)
+        // per-lane sums -> row sums (row lr is spread over the 4 lane groups)
 #pragma unroll
-    for (int rg = 0; rg < RG; ++rg) {
-        l_run[rg] += __shfl_xor(l_run[rg], 16);
-        l_run[rg] += __shfl_xor(l_run[rg], 32);
+        for (int rg = 0; rg < RG; ++rg) {
+            l_run[rg] += __shfl_xor(l_run[rg], 16);
+            l_run[rg] += __shfl_xor(l_run[rg], 32);
+        }
     }
+    __syncthreads();   // the LDS ring is free from here on
 
-    // --- merge the key-split waves through LDS (tree over wk)
+    // ---- merge the key-split consumer waves through LDS (tree over wk)
+    const bool consumer = wave < C::NC;
     if (NWK > 1) {
         float* scr = (float*)smem;
-        constexpr int SLOT = RG * 64 * (32 + 2);   // floats per wave state
+        constexpr int SLOT = RG * 64 * (32 + 2);
 #pragma unroll
         for (int stride = NWK / 2; stride >= 1; stride /= 2) {
-            __syncthreads();
-            if (wk >= stride && wk < 2 * stride) {
-                float* dst = scr + ((size_t)(wr * (NWK / 2) + (wk - stride))) * SLOT;
+            if (consumer && wk >= stride && wk < 2 * stride) {
+                float* dst = scr + (size_t)(wr * (NWK / 2) + (wk - stride)) * SLOT;
 #pragma unroll
                 for (int rg = 0; rg < RG; ++rg) {
 #pragma unroll
@@ -362,8 +434,8 @@ attn_mfma_kernel(AttnArgs a)
                 }
             }
             __syncthreads();
-            if (wk < stride) {
-                const float* src = scr + ((size_t)(wr * (NWK / 2) + wk)) * SLOT;
+            if (consumer && wk < stride) {
+                const float* src = scr + (size_t)(wr * (NWK / 2) + wk) * SLOT;
 #pragma unroll
                 for (int rg = 0; rg < RG; ++rg) {
                     const float mb = src[RG * 64 * 32 + (rg * 64 + lane) * 2 + 0];
@@ -380,25 +452,27 @@ attn_mfma_kernel(AttnArgs a)
                     m_run[rg] = mn;
                 }
             }
+            __syncthreads();
         }
     }
 
-    // --- outputs: lane holds row (wr*RG + rg)*16 + lr, dims db*16 + 4lg + i
+    // ---- outputs: lane holds row (wr*RG + rg)*16 + lr, dims db*16 + 4lg + i
     const float kLn2 = 0.69314718055994531f;
+    const bool writer = consumer && wk == 0;
     if (a.splits == 1) {
-        if (wk == 0) {
+        if (writer) {
 #pragma unroll
             for (int rg = 0; rg < RG; ++rg) {
                 const int row = (wr * RG + rg) * 16 + lr;
                 if (row >= a.R) continue;
                 const int j = row / G, hl = row - j * G;
-                const int h = si.g * G + hl;
-                const size_t orow = ((size_t)si.b * nq + j) * a.H + h;
+                const size_t orow = ((size_t)b * nq + j) * a.H + g * G + hl;
                 const float inv = l_run[rg] > 0.f ? 1.f / l_run[rg] : 0.f;
                 bf16* op = (bf16*)a.O + orow * kDH;
 #pragma unroll
                 for (int db = 0; db < 8; ++db) {
                     bf16x4v v;
+#pragma unroll
                     for (int i = 0; i < 4; ++i) v[i] = (bf16)(o[rg][db][i] * inv);
                     *(bf16x4v*)(op + db * 16 + lg * 4) = v;
                 }
@@ -409,13 +483,14 @@ attn_mfma_kernel(AttnArgs a)
         return;
     }
 
-    // publish this split's partial state, then the last split of the (b, g) merges
-    if (wk == 0) {
+    // publish this split's partial state (max in log2 units, sum, unnormalised
+    // output); the combine kernel merges the splits after this launch ends
+    if (writer) {
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
             const int row = (wr * RG + rg) * 16 + lr;
             if (row >= a.R) continue;
-            const size_t prow = ((size_t)si.bg * a.splits + si.s) * a.Rpad + row;
+            const size_t prow = ((size_t)bg * a.splits + split) * a.Rpad + row;
             float* pp = a.apart + prow * kDH;
 #pragma unroll
             for (int db = 0; db < 8; ++db) *(f32x4*)(pp + db * 16 + lg * 4) = o[rg][db];
@@ -425,56 +500,67 @@ attn_mfma_kernel(AttnArgs a)
             }
         }
     }
-    __threadfence();
-    __syncthreads();
-    if (tid == 0) sMisc[1] = (atomicAdd(&a.aticket[si.bg], 1u) == (unsigned)(a.splits - 1));
-    __syncthreads();
-    if (!sMisc[1]) return;
-    __threadfence();
-    // combine: one thread per (row, 4 dims)
-    const size_t pbase = (size_t)si.bg * a.splits * a.Rpad;
-    for (int w = tid; w < a.R * (kDH / 4); w += C::NT) {
-        const int row = w / (kDH / 4), d4 = w - row * (kDH / 4);
-        float mx = -INFINITY;
-        for (int s = 0; s < a.splits; ++s) mx = fmaxf(mx, a.aml[(pbase + (size_t)s * a.Rpad + row) * 2]);
-        float L = 0.f;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (mx != -INFINITY) {
-            for (int s = 0; s < a.splits; ++s) {
-                const size_t pr = pbase + (size_t)s * a.Rpad + row;
-                const float ms = a.aml[pr * 2];
-                if (ms == -INFINITY) continue;
-                const float f = exp2f(ms - mx);
-                L += a.aml[pr * 2 + 1] * f;
-                acc += *(const f32x4*)(a.apart + pr * kDH + d4 * 4) * f;
-            }
-        }
-        const int j = row / G, hl = row - j * G;
-        const size_t orow = ((size_t)si.b * nq + j) * a.H + si.g * G + hl;
-        const float inv = L > 0.f ? 1.f / L : 0.f;
-        bf16x4v v;
-        for (int i = 0; i < 4; ++i) v[i] = (bf16)(acc[i] * inv);
-        *(bf16x4v*)((bf16*)a.O + orow * kDH + d4 * 4) = v;
-        if (d4 == 0) a.LSE[orow] = L > 0.f ? (mx + log2f(L)) * kLn2 : -INFINITY;
-    }
-    if (tid == 0) a.aticket[si.bg] = 0u;
 }
 
-template <int RG, int NWR, int NWK, int KW>
+// Merge of the cache splits: O = sum_s 2^(m_s - M) acc_s / L and
+// LSE = (M + log2 L) ln 2 with M = max_s m_s, L = sum_s 2^(m_s - M) l_s.
+// One thread per (query row, 4 output dims); 8 rows per workgroup.
+__global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a)
+{
+    const int rows_per_wg = 8;
+    const int wgs_per_bg = (a.R + rows_per_wg - 1) / rows_per_wg;
+    const int bg = blockIdx.x / wgs_per_bg;
+    const int row = (blockIdx.x - bg * wgs_per_bg) * rows_per_wg + (threadIdx.x >> 5);
+    const int d4 = threadIdx.x & 31;
+    if (row >= a.R) return;
+    const int S = a.splits;
+    const size_t pbase = (size_t)bg * S * a.Rpad + row;
+    float mx = -INFINITY;
+    for (int s = 0; s < S; ++s) mx = fmaxf(mx, a.aml[(pbase + (size_t)s * a.Rpad) * 2]);
+    float L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (mx != -INFINITY) {
+#pragma unroll 4
+        for (int s = 0; s < S; ++s) {
+            const size_t pr = pbase + (size_t)s * a.Rpad;
+            const float ms = a.aml[pr * 2];
+            const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - mx);
+            L += a.aml[pr * 2 + 1] * w;
+            acc += *(const f32x4*)(a.apart + pr * kDH + d4 * 4) * w;
+        }
+    }
+    const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+    const int j = row / a.G, hl = row - j * a.G;
+    const size_t orow = ((size_t)b * a.nq + j) * a.H + g * a.G + hl;
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    bf16x4v v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (bf16)(acc[i] * inv);
+    *(bf16x4v*)((bf16*)a.O + orow * kDH + d4 * 4) = v;
+    if (d4 == 0) a.LSE[orow] = L > 0.f ? (mx + log2f(L)) * 0.69314718055994531f : -INFINITY;
+}
+
+template <int RG, int NWR, int NWK>
 hipError_t launch_cfg(const AttnArgs& a, hipStream_t s)
 {
-    using C = AttnCfg<RG, NWR, NWK, KW>;
-    const size_t shm = C::SCRATCH + 2 * (size_t)((a.keys_per_split + 1) & ~1) +
-                       sizeof(int) * (3 * (size_t)a.q_max + 2 + (a.keys_per_split + C::TK - 1) / C::TK + 2);
+    using C = AttnCfg<RG, NWR, NWK>;
+    const int VW = (a.nq + 31) / 32;
+    const int tiles = (a.keys_per_split + C::TK - 1) / C::TK;
+    const size_t book = 2 * (size_t)((a.keys_per_split + 1) & ~1) + 4 * (size_t)a.nq * VW +
+                        4 * (3 * (size_t)a.nq + 2 + tiles + 2);
+    if (C::SCRATCH + book > 160 * 1024) return hipErrorInvalidValue;
+    const size_t shm = C::SCRATCH + book;
     const int total = a.B * a.Hkv * a.splits;
     const int grid = ((total + 7) / 8) * 8;
-    auto kern = attn_mfma_kernel<RG, NWR, NWK, KW>;
-    if (shm > 64 * 1024) {
-        // raise the dynamic LDS limit; a refusal shows up as a launch error below
-        (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-        (void)hipGetLastError();
-    }
+    auto kern = attn_mfma_kernel<RG, NWR, NWK>;
+    // raise the dynamic LDS limit; a refusal shows up as a launch error below
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    (void)hipGetLastError();
     hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), shm, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.splits == 1) return e;
+    const int cgrid = a.B * a.Hkv * ((a.R + 7) / 8);
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(cgrid), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 
@@ -484,26 +570,22 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s)
 int attn_mfma_tile_keys(int R)
 {
     const int r16 = (R + 15) / 16;
-    return r16 <= 3 ? 128 : 64;
+    return r16 <= 9 ? 64 : 32;
 }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s)
 {
     if (a.B * a.Hkv * a.splits == 0 || a.R == 0) return hipSuccess;
     const int r16 = (a.R + 15) / 16;
-    switch (r16) {
-        case 1: return launch_cfg<1, 1, 4, 32>(a, s);
-        case 2: return launch_cfg<2, 1, 4, 32>(a, s);
-        case 3: return launch_cfg<3, 1, 4, 32>(a, s);
-        case 4: return launch_cfg<2, 2, 2, 32>(a, s);
-        case 5: case 6: return launch_cfg<2, 3, 1, 64>(a, s);
-        case 7: case 8: return launch_cfg<2, 4, 1, 64>(a, s);
-        case 9: case 10: return launch_cfg<2, 5, 1, 64>(a, s);
-        case 11: case 12: return launch_cfg<2, 6, 1, 64>(a, s);
-        case 13: case 14: return launch_cfg<2, 7, 1, 64>(a, s);
-        case 15: case 16: return launch_cfg<2, 8, 1, 64>(a, s);
-        default: return hipErrorInvalidValue;
-    }
+    if (r16 <= 1) return launch_cfg<1, 1, 2>(a, s);
+    if (r16 <= 2) return launch_cfg<1, 2, 2>(a, s);
+    if (r16 <= 4) return launch_cfg<1, 4, 2>(a, s);
+    if (r16 <= 6) return launch_cfg<2, 3, 2>(a, s);
+    if (r16 <= 9) return launch_cfg<3, 3, 2>(a, s);
+    if (r16 <= 12) return launch_cfg<2, 6, 1>(a, s);
+    if (r16 <= 14) return launch_cfg<2, 7, 1>(a, s);
+    if (r16 <= 18) return launch_cfg<3, 6, 1>(a, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace fdllm

@@ -57,31 +57,26 @@ Plan make_plan(const fdllm_ctx* h, int nq)
     const fdllm_config_t& c = h->cfg;
     Plan p{};
     int fam = h->tune.kernel_family;
-    const bool mfma_ok = c.dtype == FDLLM_BF16 && c.dh == 128 && c.d_model % 64 == 0;
+    const bool mfma_ok = c.dtype == FDLLM_BF16 && c.dh == 128 && c.d_model % 128 == 0;
     if (fam == 0) fam = mfma_ok ? FAMILY_MFMA : FAMILY_GENERIC;
     if (fam == FAMILY_MFMA && !mfma_ok) fam = FAMILY_GENERIC;
     p.proj_family = fam;
     p.R = nq * h->G;
     p.Rpad = ((p.R + 15) / 16) * 16;
-    p.attn_family = (fam == FAMILY_MFMA && (p.R + 15) / 16 <= 16) ? FAMILY_MFMA : FAMILY_GENERIC;
+    p.attn_family = (fam == FAMILY_MFMA && (p.R + 15) / 16 <= 18) ? FAMILY_MFMA : FAMILY_GENERIC;
 
-    // projection: tiles of BM rows x one head; split d_model until ~512 workgroups
+    // projection: rotary-closed column tiles give enough workgroups on their
+    // own; the d_model loop is never split across workgroups
     const int M = c.B * nq;
     p.splitk = 1;
     if (p.proj_family == FAMILY_MFMA && M > 0) {
         p.bm = proj_mfma_block_m(M);
-        const int m_tiles = (M + p.bm - 1) / p.bm;
-        p.proj_tiles = m_tiles * (c.H + 2 * c.Hkv);
-        const int nk = c.d_model / 64;
-        int sk = h->tune.gemm_splitk > 0 ? h->tune.gemm_splitk : env_int("FDLLM_SPLITK", 0);
-        if (sk <= 0) {
-            sk = (512 + p.proj_tiles - 1) / p.proj_tiles;
-            sk = std::min(sk, std::max(1, nk / 4));
-        }
-        p.splitk = std::max(1, std::min(sk, nk));
+        p.proj_tiles = ((M + p.bm - 1) / p.bm) * (c.H + 2 * c.Hkv) *
+                       (128 / proj_mfma_columns_per_tile(M, env_int("FDLLM_PROJ_TILE", 0)));
     }
 
-    // attention: (sequence, kv head) pairs x cache splits, ~512 workgroups
+    // attention: (sequence, kv head) pairs x cache splits; one workgroup fills
+    // a CU (its LDS ring is 128 KB), so aim at one round of 256 workgroups
     p.splits = 1;
     p.keys_per_split = c.N;
     if (p.attn_family == FAMILY_MFMA && nq > 0) {
@@ -89,7 +84,7 @@ Plan make_plan(const fdllm_ctx* h, int nq)
         const int bgs = c.B * c.Hkv;
         const int max_splits = (c.N + tk - 1) / tk;
         int sp = h->tune.attn_splits > 0 ? h->tune.attn_splits : env_int("FDLLM_SPLITS", 0);
-        if (sp <= 0) sp = (512 + bgs - 1) / bgs;
+        if (sp <= 0) sp = (256 + bgs - 1) / bgs;
         sp = std::max(1, std::min(sp, max_splits));
         int kps = (c.N + sp - 1) / sp;
         kps = ((kps + tk - 1) / tk) * tk;
@@ -124,10 +119,6 @@ int ensure_split_ws(fdllm_ctx* h)
     size_t gbytes = 0, gtickets = 0, arows = 0;
     for (int nq = 1; nq <= c.q_max; ++nq) {
         const Plan p = make_plan(h, nq);
-        if (p.proj_family == FAMILY_MFMA && p.splitk > 1) {
-            gbytes = std::max(gbytes, (size_t)p.proj_tiles * p.splitk * p.bm * 128 * sizeof(float));
-            gtickets = std::max(gtickets, (size_t)p.proj_tiles);
-        }
         if (p.attn_family == FAMILY_MFMA && p.splits > 1)
             arows = std::max(arows, (size_t)c.B * c.Hkv * p.splits * p.Rpad);
     }
@@ -177,6 +168,7 @@ ProjArgs proj_args(const fdllm_ctx* h, const void* X, int x_rows, const int32_t*
     a.B = c.B; a.N = c.N; a.d = c.d_model; a.H = c.H; a.Hkv = c.Hkv; a.dh = c.dh; a.G = h->G;
     a.x_rows = x_rows; a.rows_per_seq = rows_per_seq; a.q_max = c.q_max;
     a.prefill = prefill; a.splitk = splitk;
+    a.tile_choice = prefill ? 0 : env_int("FDLLM_PROJ_TILE", 0);
     return a;
 }
 
@@ -327,9 +319,6 @@ int fdllm_step_project(fdllm_handle_t h, const void* X, int32_t x_rows, const in
             if (qi[t] < 0 || qi[t] >= x_rows || pi[t] < 0 || pi[t] >= c.N) return FDLLM_ERR_INDEX;
     }
     const Plan p = make_plan(h, nq);
-    if (p.proj_family == FAMILY_MFMA && p.splitk > 1 &&
-        (size_t)p.proj_tiles * p.splitk * p.bm * 128 * sizeof(float) > h->gpart_bytes)
-        return FDLLM_ERR_ALLOC;   // not reached: the workspace is sized for every nq
     ProjArgs pa = proj_args(h, X, x_rows, Q_idx, pos_ids, nq, W, Kc, Vc, 0, p.splitk);
     hipError_t e = p.proj_family == FAMILY_MFMA ? launch_proj_mfma(pa, s) : launch_proj_generic(pa, c.dtype, s);
     return hip_status(e);

@@ -11,6 +11,7 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Everything a launch of the projection kernels needs.  Rows of the
 // projection are m = b * rows_per_seq + j.
@@ -33,6 +34,7 @@ struct ProjArgs {
     int q_max;
     int prefill;            // 1: k/v heads only, no q, no side buffer
     int splitk;
+    int tile_choice;        // 0: default tile configuration for the row count
 };
 
 struct AttnArgs {
@@ -64,6 +66,7 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
 
 // Tile geometry of the MFMA kernels, needed by the host planner.
 int proj_mfma_block_m(int M);
+int proj_mfma_columns_per_tile(int M, int choice);
 int attn_mfma_tile_keys(int R);
 
 // Conversions between storage types and fp32.

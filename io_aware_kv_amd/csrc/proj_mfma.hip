@@ -1,32 +1,69 @@
 // proj_mfma.hip -- gather X[Q] + QKV projection + rotary + in-place k/v write,
-// as one tiled bf16 MFMA kernel for gfx950 (head width 128).
+// as one bf16 MFMA kernel for gfx950 (head width 128).
 //
 // Flash-dLLM's fused kernel reads only the query rows' hidden states, builds
 // q, k, v on chip and writes k, v straight into the cache (jaehun.me review,
 // "How It Works: A Concrete Example", Step 1: Draft, citing the paper's
-// Alg. 1; alanhou.org summary, "Core Mechanism" item 1).  Here one workgroup
-// owns an output tile of BM query rows x one head (128 columns): the query
-// rows are gathered from X by index straight into LDS, W is streamed through
-// LDS once per tile, the fp32 accumulators are rotated in registers (the
-// rotate-half pairs (c, c+64) sit in the same lane), and each row is stored to
-// its final place: q in fp32 to the attention's staging buffer, k/v rounded
+// Alg. 1; alanhou.org summary, "Core Mechanism" item 1).
+//
+// One workgroup owns an output tile of BM query rows x BN columns of one
+// head.  The columns are a rotary-closed set: 16-column blocks {p .. p+n-1}
+// and {p+4 .. p+4+n-1}, so every lane holds both halves of its rotate-half
+// pairs (c, c+64).  Narrow tiles (BN = 32) give small row counts enough
+// workgroups to stream the weight at full bandwidth without splitting the
+// d_model loop across workgroups (which would need a device-wide reduction).
+//
+// A producer wave streams 128-deep d_model stages of the gathered X rows
+// (addressed through Q_idx) and of the tile's W rows into an LDS ring with
+// global_load_lds; the consumer waves run v_mfma_f32_16x16x32_bf16 from LDS
+// (256 B rows, 16 B chunks XOR-swizzled by row: conflict-free fragment reads).
+// The fp32 accumulators are rotated in registers, staged in LDS and stored as
+// whole rows: q in fp32 to the attention's staging buffer, k and v rounded
 // once to bf16 into Kc/Vc at the row's position (or into the side buffer when
 // an earlier query row owns that position).
-//
-// Small row counts leave W-bandwidth-bound work with few tiles, so the d_model
-// loop can be split across workgroups; the last workgroup of a tile (atomic
-// ticket) sums the fp32 partials in fixed order, so results do not depend on
-// the arrival order.
-#include "fdllm_common.h"
+#include "pipeline.h"
 
 namespace fdllm {
 
 namespace {
 
-constexpr int kBN = 128;       // one head of 128 columns
-constexpr int kBK = 64;        // d_model slice per pipeline stage
-constexpr int kLdsRow = kBK + 8;   // padded LDS row (bf16): 144 B, conflict-light 16 B reads
-constexpr int kThreads = 256;
+constexpr int kDH = 128;          // head width
+
+// BK: d_model depth per stage (64 or 128, so a staged row is 128 or 256 B);
+// NPROD producer waves split each stage's 1 KB DMA blocks, so up to NPROD x 63
+// blocks can be in flight per workgroup.
+template <int BM, int NCB, int NRW, int NPW, int NSMAX, int BK, int NPROD>
+struct ProjCfg {
+    static constexpr int NCW = NRW * NPW;                 // consumer waves
+    static constexpr int NT = (NCW + NPROD) * 64;
+    static constexpr int BN = 16 * NCB;
+    static constexpr int ROWB = BK * 2;                   // bytes per staged row
+    static constexpr int RPD = 1024 / ROWB;               // rows per 1 KB DMA block
+    static constexpr int CPR = BK / 8;                    // 16 B chunks per staged row
+    static constexpr int ROWS = BM + BN;                  // staged rows per stage
+    static constexpr int STAGE = ROWS * ROWB;
+    static constexpr int NS0 = (128 * 1024) / STAGE;
+    static constexpr int NS = NS0 > NSMAX ? NSMAX : NS0;
+    static constexpr int DMA = ROWS / RPD;                // 1 KB DMA blocks per stage
+    static constexpr int DMAP = DMA / NPROD;              // per producer wave
+    static constexpr int RBW = BM / 16 / NRW;             // row blocks per consumer wave
+    static constexpr int PAIRS = NCB / 2;                 // rotary block pairs per tile
+    static constexpr int PPW = PAIRS / NPW;               // pairs per consumer wave
+    static_assert(BK == 64 || BK == 128, "stage depth");
+    static_assert(BM % (16 * NRW) == 0 && PAIRS % NPW == 0 && NS >= 2, "tile shape");
+    static_assert(DMA % NPROD == 0 && BM % RPD == 0, "DMA split");
+    static_assert(BM * (BN + 4) * 4 <= NS * STAGE, "epilogue staging");
+};
+
+// Chunk swizzle of a staged row: 16 B chunk c of row r sits in slot c ^ f(r).
+// With 256 B rows, f(r) = r & 15; with 128 B rows (two rows per 64-bank
+// sweep), f(r) = (r >> 1) & 7.  Either way the 16 rows read by one fragment
+// load hit 16 distinct 16 B bank groups.
+template <int BK>
+__device__ __forceinline__ int chunk_swz(int row)
+{
+    return BK == 128 ? (row & 15) : ((row >> 1) & 7);
+}
 
 __device__ __forceinline__ bool owns_position(const int32_t* pos_b, int j)
 {
@@ -36,286 +73,290 @@ __device__ __forceinline__ bool owns_position(const int32_t* pos_b, int j)
     return true;
 }
 
-// BM rows per tile; WR waves split the rows, 4/WR waves split the 8 column
-// blocks (a wave's blocks are {wc, wc + WC, ...}, closed under +4 so each lane
-// holds both halves of its rotary pairs).
-template <int BM, int WR>
-__global__ void __launch_bounds__(kThreads) proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
+template <int BM, int NCB, int NRW, int NPW, int NSMAX, int BK, int NPROD>
+__global__ void __launch_bounds__((NRW * NPW + NPROD) * 64)
+proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
 {
-    constexpr int WC = 4 / WR;
-    constexpr int RB = BM / WR / 16;       // 16-row blocks per wave
-    constexpr int CB = 8 / WC;             // 16-column blocks per wave
-    constexpr int XCH = BM * (kBK / 8);    // 16 B chunks of an X stage
-    constexpr int XPT = (XCH + kThreads - 1) / kThreads;
-    constexpr int WPT = kBN * (kBK / 8) / kThreads;  // 4
-    static_assert(RB >= 1 && BM % (16 * WR) == 0, "bad tile");
+    using C = ProjCfg<BM, NCB, NRW, NPW, NSMAX, BK, NPROD>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __shared__ size_t sXoff[BM];   // element offset of the row's X row
+    __shared__ int sPos[BM];
+    __shared__ int sDst[BM];       // 1: owns its position, 0: duplicate, -1: padding row
 
-    const int total = m_tiles * n_tiles * a.splitk;
+    const int total = m_tiles * n_tiles;
     const int logical = xcd_remap(blockIdx.x, total);
     if (logical < 0) return;
-    const int mt = logical % m_tiles;
-    const int nz = logical / m_tiles;
-    const int z = nz % a.splitk;
-    const int nt = nz / a.splitk;
-    const int head = a.prefill ? a.H + nt : nt;
+    const int mt = logical % m_tiles;              // row tiles of one column tile share an XCD
+    const int nt = logical / m_tiles;
+    constexpr int TPH = 8 / NCB;                   // column tiles per head
+    const int head = (a.prefill ? a.H : 0) + nt / TPH;
+    const int p0 = (nt % TPH) * C::PAIRS;          // first 16-column block of the tile
     const int M = a.B * a.rows_per_seq;
     const int m0 = mt * BM;
 
-    // one LDS block: the two pipeline stages of X and W, reused afterwards to
-    // stage the finished tile (fp32 for q rows, bf16 for k/v rows)
-    constexpr int kStageBytes = 2 * (BM + kBN) * kLdsRow * 2;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[kStageBytes];
-    bf16 (*sX)[BM][kLdsRow] = reinterpret_cast<bf16 (*)[BM][kLdsRow]>(smem);
-    bf16 (*sW)[kBN][kLdsRow] = reinterpret_cast<bf16 (*)[kBN][kLdsRow]>(smem + 2 * BM * kLdsRow * 2);
-    __shared__ int sPos[BM];
-    __shared__ int sDst[BM];        // 1: owns its position, 0: duplicate, -1: padding row
-    __shared__ int sLast;
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int wr = wave / WC, wc = wave % WC;
-
-    if (tid < BM) {
-        const int m = m0 + tid;
-        if (m < M) {
-            const int b = m / a.rows_per_seq, j = m - b * a.rows_per_seq;
-            sPos[tid] = a.prefill ? j : a.pos_ids[m];
-            sDst[tid] = a.prefill ? 1 : (owns_position(a.pos_ids + (size_t)b * a.rows_per_seq, j) ? 1 : 0);
-        } else {
-            sPos[tid] = 0;
-            sDst[tid] = -1;
-        }
-    }
-
-    // d_model range of this split
-    const int nk_total = a.d / kBK;
-    const int nk_per = (nk_total + a.splitk - 1) / a.splitk;
-    const int kb0 = z * nk_per;
-    const int niter = min(nk_total, kb0 + nk_per) - kb0;
-
-    // per-thread source pointers (constant over the d_model loop)
-    const bf16* xsrc[XPT];
-    int xrow[XPT], xpart[XPT];
-#pragma unroll
-    for (int i = 0; i < XPT; ++i) {
-        const int c = tid + i * kThreads;
-        xrow[i] = c / (kBK / 8);
-        xpart[i] = c % (kBK / 8);
-        xsrc[i] = nullptr;
-        const int m = m0 + xrow[i];
-        if (c < XCH && m < M) {
-            const int b = m / a.rows_per_seq, j = m - b * a.rows_per_seq;
-            const int r = a.prefill ? j : a.Q_idx[m];
-            xsrc[i] = (const bf16*)a.X + ((size_t)b * a.x_rows + r) * a.d + xpart[i] * 8;
-        }
-    }
-    const bf16* wsrc[WPT];
-    int wrow[WPT], wpart[WPT];
-#pragma unroll
-    for (int i = 0; i < WPT; ++i) {
-        const int c = tid + i * kThreads;
-        wrow[i] = c / (kBK / 8);
-        wpart[i] = c % (kBK / 8);
-        wsrc[i] = (const bf16*)a.W + ((size_t)head * kBN + wrow[i]) * a.d + wpart[i] * 8;
-    }
-
-    uint4 xr[XPT], wreg[WPT];
-    auto load_stage = [&](int kb) {
-        const int koff = kb * kBK;
-#pragma unroll
-        for (int i = 0; i < XPT; ++i)
-            xr[i] = xsrc[i] ? *(const uint4*)(xsrc[i] + koff) : make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < WPT; ++i) wreg[i] = *(const uint4*)(wsrc[i] + koff);
-    };
-    auto store_stage = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < XPT; ++i)
-            if (tid + i * kThreads < XCH) *(uint4*)&sX[buf][xrow[i]][xpart[i] * 8] = xr[i];
-#pragma unroll
-        for (int i = 0; i < WPT; ++i) *(uint4*)&sW[buf][wrow[i]][wpart[i] * 8] = wreg[i];
-    };
-
-    f32x4 acc[RB][CB];
-#pragma unroll
-    for (int r = 0; r < RB; ++r)
-#pragma unroll
-        for (int q = 0; q < CB; ++q) acc[r][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
-    if (niter > 0) load_stage(kb0);
-    for (int it = 0; it < niter; ++it) {
-        const int buf = it & 1;
-        store_stage(buf);
-        __syncthreads();
-        if (it + 1 < niter) load_stage(kb0 + it + 1);
-#pragma unroll
-        for (int ks = 0; ks < kBK / 32; ++ks) {
-            bf16x8 af[RB], bfr[CB];
-#pragma unroll
-            for (int r = 0; r < RB; ++r)
-                af[r] = *(const bf16x8*)&sX[buf][(wr * RB + r) * 16 + lr][ks * 32 + lg * 8];
-#pragma unroll
-            for (int q = 0; q < CB; ++q)
-                bfr[q] = *(const bf16x8*)&sW[buf][(wc + WC * q) * 16 + lr][ks * 32 + lg * 8];
-#pragma unroll
-            for (int r = 0; r < RB; ++r)
-#pragma unroll
-                for (int q = 0; q < CB; ++q)
-                    acc[r][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[r], bfr[q], acc[r][q], 0, 0, 0);
-        }
-    }
 
-    const int tile = nt * m_tiles + mt;
-    if (a.splitk > 1) {
-        // publish this split's partial tile in fragment order, then take a ticket
-        constexpr int NACC = RB * CB;
-        float4* part = (float4*)a.gpart + ((size_t)tile * a.splitk + z) * NACC * kThreads;
+    for (int r = tid; r < BM; r += C::NT) {
+        int m = m0 + r;
+        const bool valid = m < M;
+        if (!valid) m = m0;                          // padding rows read a valid row, then are dropped
+        const int b = m / a.rows_per_seq, j = m - b * a.rows_per_seq;
+        const int xr = a.prefill ? j : a.Q_idx[m];
+        sXoff[r] = ((size_t)b * a.x_rows + xr) * a.d;
+        sPos[r] = valid ? (a.prefill ? j : a.pos_ids[m]) : 0;
+        sDst[r] = !valid ? -1 : (a.prefill ? 1 : (owns_position(a.pos_ids + (size_t)b * a.rows_per_seq, j) ? 1 : 0));
+    }
+    __syncthreads();
+
+    const int nk = a.d / BK;
+    const bf16* X = (const bf16*)a.X;
+    const bf16* W = (const bf16*)a.W;
+
+    f32x4 acc[C::RBW][2 * C::PPW];
 #pragma unroll
-        for (int r = 0; r < RB; ++r)
+    for (int r = 0; r < C::RBW; ++r)
 #pragma unroll
-            for (int q = 0; q < CB; ++q) {
-                const f32x4 v = acc[r][q];
-                part[(size_t)(r * CB + q) * kThreads + tid] = make_float4(v[0], v[1], v[2], v[3]);
-            }
-        __threadfence();
-        __syncthreads();
-        if (tid == 0) sLast = (atomicAdd(&a.gticket[tile], 1u) == (unsigned)(a.splitk - 1));
-        __syncthreads();
-        if (!sLast) return;
-        __threadfence();
-        const float4* all = (const float4*)a.gpart + (size_t)tile * a.splitk * NACC * kThreads;
+        for (int q = 0; q < 2 * C::PPW; ++q) acc[r][q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int wr = wave / NPW, wp = wave % NPW;   // consumer coordinates
+
+    if (wave >= C::NCW) {
+        // ================= producer waves =================
+        const int pw = wave - C::NCW;
+        const int srow = lane / C::CPR, slot = lane % C::CPR;
+        auto issue = [&](int t) {
+            unsigned char* st = smem + (t % C::NS) * C::STAGE;
+            const int k0 = t * BK;
 #pragma unroll
-        for (int r = 0; r < RB; ++r)
-#pragma unroll
-            for (int q = 0; q < CB; ++q) acc[r][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int zz = 0; zz < a.splitk; ++zz) {
-#pragma unroll
-            for (int r = 0; r < RB; ++r)
-#pragma unroll
-                for (int q = 0; q < CB; ++q) {
-                    const float4 v = all[((size_t)zz * NACC + r * CB + q) * kThreads + tid];
-                    acc[r][q][0] += v.x;
-                    acc[r][q][1] += v.y;
-                    acc[r][q][2] += v.z;
-                    acc[r][q][3] += v.w;
+            for (int ii = 0; ii < C::DMAP; ++ii) {
+                const int i = ii * NPROD + pw;                  // this wave's DMA blocks
+                const int row = C::RPD * i + srow;
+                const int chunk = slot ^ chunk_swz<BK>(row);
+                const bf16* src;
+                if (C::RPD * i < BM) {
+                    src = X + sXoff[row] + k0 + chunk * 8;
+                } else {
+                    const int wi = row - BM, blk = wi >> 4;
+                    const int cb = blk < C::PAIRS ? p0 + blk : p0 + 4 + (blk - C::PAIRS);
+                    src = W + ((size_t)(head * kDH + cb * 16 + (wi & 15))) * a.d + k0 + chunk * 8;
                 }
+                dma16(src, st + i * 1024);
+            }
+        };
+        int issued = 0;
+        for (; issued < min(C::NS - 1, nk); ++issued) issue(issued);
+        for (int t = 0; t < nk; ++t) {
+            ring_producer_sync((issued - t - 1) * C::DMAP);
+            if (issued < nk) issue(issued++);
         }
-        if (tid == 0) a.gticket[tile] = 0u;
+    } else {
+        // ================= consumer waves =================
+        for (int t = 0; t < nk; ++t) {
+            ring_consumer_sync();
+            const unsigned char* st = smem + (t % C::NS) * C::STAGE;
+#pragma unroll
+            for (int ks = 0; ks < BK / 32; ++ks) {
+                bf16x8 af[C::RBW], bfr[2 * C::PPW];
+#pragma unroll
+                for (int r = 0; r < C::RBW; ++r) {
+                    const int row = (wr * C::RBW + r) * 16 + lr;
+                    af[r] = *(const bf16x8*)(st + row * C::ROWB + (((ks * 4 + lg) ^ chunk_swz<BK>(row)) << 4));
+                }
+#pragma unroll
+                for (int q = 0; q < 2 * C::PPW; ++q) {
+                    const int blk = q < C::PPW ? wp * C::PPW + q : C::PAIRS + wp * C::PPW + (q - C::PPW);
+                    const int row = BM + blk * 16 + lr;
+                    bfr[q] = *(const bf16x8*)(st + row * C::ROWB + (((ks * 4 + lg) ^ chunk_swz<BK>(row)) << 4));
+                }
+#pragma unroll
+                for (int r = 0; r < C::RBW; ++r)
+#pragma unroll
+                    for (int q = 0; q < 2 * C::PPW; ++q)
+                        acc[r][q] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[r], bfr[q], acc[r][q], 0, 0, 0);
+            }
+        }
     }
+    __syncthreads();   // the ring is free: it stages the finished tile below
 
-    // rotary on q and k heads: lane holds column c = cb*16 + lr (< 64 for the
-    // first half of the wave's blocks) and rows 4*lg + i of each row block
+    // rotary on q and k heads: lane holds tile column blk*16 + lr of each block
+    // (head column cb*16 + lr) and rows 4*lg + i of each row block
+    const bool consumer = wave < C::NCW;
     const bool rotate = head < a.H + a.Hkv;
-    if (rotate) {
+    if (consumer && rotate) {
 #pragma unroll
-        for (int q = 0; q < CB / 2; ++q) {
-            const int c = (wc + WC * q) * 16 + lr;
+        for (int q = 0; q < C::PPW; ++q) {
+            const int c = (p0 + wp * C::PPW + q) * 16 + lr;    // < 64: first half of the pair
 #pragma unroll
-            for (int r = 0; r < RB; ++r)
+            for (int r = 0; r < C::RBW; ++r)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int row = (wr * RB + r) * 16 + lg * 4 + i;
-                    const float2 cs = a.rope[(size_t)sPos[row] * (kBN / 2) + c];
-                    const float y0 = acc[r][q][i], y1 = acc[r][q + CB / 2][i];
+                    const int row = (wr * C::RBW + r) * 16 + lg * 4 + i;
+                    const float2 cs = a.rope[(size_t)sPos[row] * (kDH / 2) + c];
+                    const float y0 = acc[r][q][i], y1 = acc[r][q + C::PPW][i];
                     acc[r][q][i] = y0 * cs.x - y1 * cs.y;
-                    acc[r][q + CB / 2][i] = y1 * cs.x + y0 * cs.y;
+                    acc[r][q + C::PPW][i] = y1 * cs.x + y0 * cs.y;
                 }
         }
     }
 
-    // stage the finished tile in LDS and store whole rows: q rows stay fp32
-    // (consumed on chip by the attention, never stored as bf16), k/v rows are
-    // rounded once to bf16 (they are the cache contents)
-    __syncthreads();   // everyone is done reading the pipeline stages
+    // stage the tile: q rows stay fp32 (consumed on chip by the attention),
+    // k/v rows are rounded once to bf16 (they are the cache contents)
     const int G = a.G;
-    if (head < a.H) {
-        constexpr int kRowF = kBN + 4;
-        static_assert(kStageBytes >= BM * kRowF * 4, "fp32 staging does not fit");
-        float* sOutF = reinterpret_cast<float*>(smem);
+    constexpr int BN = C::BN;
+    const bool isq = head < a.H;
+    if (isq) {
+        constexpr int RS = BN + 4;
+        float* sOut = (float*)smem;
+        if (consumer) {
 #pragma unroll
-        for (int r = 0; r < RB; ++r)
+            for (int r = 0; r < C::RBW; ++r)
 #pragma unroll
-            for (int q = 0; q < CB; ++q)
+                for (int q = 0; q < 2 * C::PPW; ++q) {
+                    const int blk = q < C::PPW ? wp * C::PPW + q : C::PAIRS + wp * C::PPW + (q - C::PPW);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    sOutF[((wr * RB + r) * 16 + lg * 4 + i) * kRowF + (wc + WC * q) * 16 + lr] = acc[r][q][i];
+                    for (int i = 0; i < 4; ++i)
+                        sOut[((wr * C::RBW + r) * 16 + lg * 4 + i) * RS + blk * 16 + lr] = acc[r][q][i];
+                }
+        }
         __syncthreads();
         const int g = head / G, hl = head - g * G;
-        constexpr int OCH = BM * (kBN / 4);
-        for (int c = tid; c < OCH; c += kThreads) {
-            const int row = c / (kBN / 4), part = c % (kBN / 4);
+        constexpr int CPR = BN / 4;                  // 16 B chunks per row
+        for (int c = tid; c < BM * CPR; c += C::NT) {
+            const int row = c / CPR, part = c - row * CPR;
             if (sDst[row] < 0) continue;
             const int m = m0 + row;
             const int b = m / a.rows_per_seq, j = m - b * a.rows_per_seq;
-            float* dst = a.qbuf + (((size_t)b * a.Hkv + g) * a.q_max * G + (size_t)j * G + hl) * kBN;
-            *(float4*)(dst + part * 4) = *(const float4*)&sOutF[row * kRowF + part * 4];
+            const int tcol = part * 4;                                   // tile column
+            const int hcol = tcol < BN / 2 ? p0 * 16 + tcol : 64 + p0 * 16 + (tcol - BN / 2);
+            float* dst = a.qbuf + (((size_t)b * a.Hkv + g) * a.q_max * G + (size_t)j * G + hl) * kDH + hcol;
+            *(f32x4*)dst = *(const f32x4*)&sOut[row * RS + tcol];
         }
         return;
     }
-    static_assert(kStageBytes >= BM * (kBN + 8) * 2, "bf16 staging does not fit");
-    bf16 (*sOut)[kBN + 8] = reinterpret_cast<bf16 (*)[kBN + 8]>(smem);
+    constexpr int RS = BN + 8;
+    bf16* sOut = (bf16*)smem;
+    if (consumer) {
 #pragma unroll
-    for (int r = 0; r < RB; ++r)
+        for (int r = 0; r < C::RBW; ++r)
 #pragma unroll
-        for (int q = 0; q < CB; ++q)
+            for (int q = 0; q < 2 * C::PPW; ++q) {
+                const int blk = q < C::PPW ? wp * C::PPW + q : C::PAIRS + wp * C::PPW + (q - C::PPW);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sOut[(wr * RB + r) * 16 + lg * 4 + i][(wc + WC * q) * 16 + lr] = (bf16)acc[r][q][i];
+                for (int i = 0; i < 4; ++i)
+                    sOut[((wr * C::RBW + r) * 16 + lg * 4 + i) * RS + blk * 16 + lr] = (bf16)acc[r][q][i];
+            }
+    }
     __syncthreads();
-
     const bool isk = head < a.H + a.Hkv;
     const int g = head - a.H - (isk ? 0 : a.Hkv);
-    constexpr int OCH = BM * (kBN / 8);
-    for (int c = tid; c < OCH; c += kThreads) {
-        const int row = c / (kBN / 8), part = c % (kBN / 8);
+    constexpr int CPR = BN / 8;
+    for (int c = tid; c < BM * CPR; c += C::NT) {
+        const int row = c / CPR, part = c - row * CPR;
         const int kind = sDst[row];
         if (kind < 0) continue;
         const int m = m0 + row;
         const int b = m / a.rows_per_seq, j = m - b * a.rows_per_seq;
+        const int tcol = part * 8;
+        const int hcol = tcol < BN / 2 ? p0 * 16 + tcol : 64 + p0 * 16 + (tcol - BN / 2);
         bf16* dst;
         if (kind == 1)
-            dst = (bf16*)(isk ? a.Kc : a.Vc) + (((size_t)b * a.Hkv + g) * a.N + sPos[row]) * kBN;
+            dst = (bf16*)(isk ? a.Kc : a.Vc) + (((size_t)b * a.Hkv + g) * a.N + sPos[row]) * kDH;
         else
-            dst = (bf16*)(isk ? a.sideK : a.sideV) + (((size_t)b * a.Hkv + g) * a.q_max + j) * kBN;
-        *(uint4*)(dst + part * 8) = *(const uint4*)&sOut[row][part * 8];
+            dst = (bf16*)(isk ? a.sideK : a.sideV) + (((size_t)b * a.Hkv + g) * a.q_max + j) * kDH;
+        *(u32x4*)(dst + hcol) = *(const u32x4*)&sOut[row * RS + tcol];
     }
 }
 
-template <int BM, int WR>
-hipError_t launch_bm(const ProjArgs& a, hipStream_t s)
+template <int BM, int NCB, int NRW, int NPW, int NSMAX, int BK = 128, int NPROD = 1>
+hipError_t launch_tile(const ProjArgs& a, hipStream_t s)
 {
+    using C = ProjCfg<BM, NCB, NRW, NPW, NSMAX, BK, NPROD>;
     const int M = a.B * a.rows_per_seq;
     const int m_tiles = (M + BM - 1) / BM;
-    const int n_tiles = a.prefill ? 2 * a.Hkv : a.H + 2 * a.Hkv;
-    const int total = m_tiles * n_tiles * a.splitk;
+    const int heads = a.prefill ? 2 * a.Hkv : a.H + 2 * a.Hkv;
+    const int n_tiles = heads * (8 / NCB);
+    const int total = m_tiles * n_tiles;
     const int grid = ((total + 7) / 8) * 8;
-    hipLaunchKernelGGL((proj_mfma_kernel<BM, WR>), dim3(grid), dim3(kThreads), 0, s, a, m_tiles, n_tiles);
+    const size_t shm = (size_t)C::NS * C::STAGE;
+    auto kern = proj_mfma_kernel<BM, NCB, NRW, NPW, NSMAX, BK, NPROD>;
+    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), shm, s, a, m_tiles, n_tiles);
     return hipGetLastError();
 }
 
 }  // namespace
+
+// Tile configurations: rows BM, 16-column blocks NCB, consumer waves split
+// as NRW (rows) x NPW (rotary block pairs), at most NSMAX ring stages.
+struct ProjChoice { int bm, ncb; };
+static const ProjChoice kProjChoices[] = {
+    {0, 0},
+    {16, 2}, {32, 2}, {48, 2}, {64, 2},      // 1-4: narrow tiles, one consumer wave, deep ring
+    {128, 8},                               // 5: 128 x 128, four consumer waves, two stages
+    {64, 4}, {64, 8}, {128, 4},             // 6-8
+    {48, 2}, {64, 2}, {16, 2},              // 9-11: narrow tiles with a 3-stage ring (2 workgroups per CU)
+    {32, 4}, {64, 4},                       // 12-13: 64-column tiles, 3-stage ring
+    {128, 8}, {128, 8}, {64, 4}, {128, 4}, {64, 8}, {48, 2}, {64, 4},   // 14-20: two producer waves
+};
 
 int proj_mfma_block_m(int M)
 {
     if (M <= 16) return 16;
     if (M <= 32) return 32;
     if (M <= 48) return 48;
-    if (M <= 64) return 64;
+    if (M <= 128) return 64;
     return 128;
+}
+
+static int default_choice(int M)
+{
+    switch (proj_mfma_block_m(M)) {
+        case 16: return 1;
+        case 32: return 2;
+        case 48: return 3;
+        case 64: return 4;
+        default: return 5;
+    }
+}
+
+int proj_mfma_columns_per_tile(int M, int choice)
+{
+    if (choice <= 0 || choice >= (int)(sizeof(kProjChoices) / sizeof(kProjChoices[0]))) choice = default_choice(M);
+    return 16 * kProjChoices[choice].ncb;
 }
 
 hipError_t launch_proj_mfma(const ProjArgs& a, hipStream_t s)
 {
     const int M = a.B * a.rows_per_seq;
     if (M == 0) return hipSuccess;
-    switch (proj_mfma_block_m(M)) {
-        case 16: return launch_bm<16, 1>(a, s);
-        case 32: return launch_bm<32, 2>(a, s);
-        case 48: return launch_bm<48, 1>(a, s);
-        case 64: return launch_bm<64, 2>(a, s);
-        default: return launch_bm<128, 2>(a, s);
+    if (a.d % 128 != 0) return hipErrorInvalidValue;
+    int choice = a.tile_choice;
+    if (choice <= 0 || choice >= (int)(sizeof(kProjChoices) / sizeof(kProjChoices[0]))) choice = default_choice(M);
+    switch (choice) {
+        case 1: return launch_tile<16, 2, 1, 1, 8>(a, s);
+        case 2: return launch_tile<32, 2, 1, 1, 8>(a, s);
+        case 3: return launch_tile<48, 2, 1, 1, 8>(a, s);
+        case 4: return launch_tile<64, 2, 1, 1, 8>(a, s);
+        case 5: return launch_tile<128, 8, 2, 2, 8>(a, s);
+        case 6: return launch_tile<64, 4, 2, 2, 8>(a, s);
+        case 7: return launch_tile<64, 8, 2, 2, 8>(a, s);
+        case 8: return launch_tile<128, 4, 2, 2, 8>(a, s);
+        case 9: return launch_tile<48, 2, 1, 1, 3>(a, s);
+        case 10: return launch_tile<64, 2, 1, 1, 3>(a, s);
+        case 11: return launch_tile<16, 2, 1, 1, 3>(a, s);
+        case 12: return launch_tile<32, 4, 1, 2, 3>(a, s);
+        case 13: return launch_tile<64, 4, 2, 2, 3>(a, s);
+        case 14: return launch_tile<128, 8, 2, 2, 8, 64, 2>(a, s);
+        case 15: return launch_tile<128, 8, 2, 2, 8, 128, 2>(a, s);
+        case 16: return launch_tile<64, 4, 2, 2, 8, 128, 2>(a, s);
+        case 17: return launch_tile<128, 4, 2, 2, 8, 64, 2>(a, s);
+        case 18: return launch_tile<64, 8, 2, 2, 8, 64, 2>(a, s);
+        case 19: return launch_tile<48, 2, 1, 1, 3, 128, 2>(a, s);
+        case 20: return launch_tile<64, 4, 2, 2, 3, 64, 2>(a, s);
+        default: return hipErrorInvalidValue;
     }
 }
 

@@ -56,6 +56,8 @@ def bind(path: str):
     lib.fdllm_oracle_step.restype = ctypes.c_int
     lib.fdllm_oracle_prefill.argtypes = [P, P, i32, P, P, P]
     lib.fdllm_oracle_prefill.restype = ctypes.c_int
+    lib.fdllm_oracle_threads.argtypes = []
+    lib.fdllm_oracle_threads.restype = ctypes.c_int
     return lib
 
 
@@ -107,6 +109,11 @@ def _ptr(a):
 def _cfg(shape: Shape, round_mode: int) -> _Cfg:
     return _Cfg(shape.B, shape.N, shape.d_model, shape.H, shape.Hkv, shape.dh,
                 float(shape.rope_base), int(round_mode))
+
+
+def threads() -> int:
+    """OpenMP threads the oracle's loops run on."""
+    return int(_load().fdllm_oracle_threads())
 
 
 def round_store(x, mode: int) -> np.ndarray:

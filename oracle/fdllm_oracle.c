@@ -45,6 +45,7 @@
  *     LSE = -inf.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -79,6 +80,9 @@ static double round_store(double x, int mode)
     if (mode == 2) return round_to_bf16(x);
     return x;
 }
+
+/* Threads the OpenMP loops of this library use. */
+int fdllm_oracle_threads(void) { return omp_get_max_threads(); }
 
 void fdllm_oracle_round(const double* in, double* out, int64_t n, int32_t mode)
 {
