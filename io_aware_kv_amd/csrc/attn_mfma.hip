@@ -44,40 +44,52 @@ namespace fdllm {
 namespace {
 
 constexpr int kDH = 128;
-constexpr int kRowB = kDH * 2;   // bytes of one K or V row
+constexpr int kRowB = kDH * 2;        // bytes of one K or V row
+constexpr int kRing = 128 * 1024;     // LDS ring of K/V stages per workgroup
+constexpr int kMaxChunks = 5;         // query rows per sequence, in chunks of 64 (R <= 288)
+constexpr float kNegBig = -1.0e30f;   // running max of a row that has seen no key
 
 typedef __bf16 bf16x4g __attribute__((__vector_size__(4 * sizeof(__bf16))));
 typedef __attribute__((address_space(3))) bf16x4g lds_bf16x4;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
-template <int RG, int NWR, int NWK>
+// RG row groups of 16 query rows per consumer wave, NWR x NWK consumer waves
+// (rows x keys of a tile), NPROD producer waves.
+template <int RG, int NWR, int NWK, int NPROD>
 struct AttnCfg {
     static constexpr int NC = NWR * NWK;            // consumer waves
-    static constexpr int NT = (NC + 1) * 64;        // + one producer wave
+    static constexpr int NT = (NC + NPROD) * 64;
     static constexpr int KW = 32;                   // keys per consumer wave per tile
     static constexpr int TK = KW * NWK;             // keys per tile
     static constexpr int STAGE = TK * 2 * kRowB;    // K rows then V rows
-    static constexpr int NS = (128 * 1024) / STAGE; // ring of 128 KB
-    static constexpr int DMA = STAGE / 1024;        // producer instructions per stage
+    static constexpr int NS = kRing / STAGE;
+    static constexpr int DMA = STAGE / 1024;        // 1 KB DMA instructions per stage
+    static constexpr int DMAP = DMA / NPROD;        // ... issued by each producer wave
     static constexpr int MERGE = (NWK / 2) * NWR * RG * 64 * (32 + 2) * 4;
     static constexpr int SCRATCH = NS * STAGE > MERGE ? NS * STAGE : MERGE;
-    static_assert(NS >= 2 && NS * STAGE == 128 * 1024, "stage ring");
+    static_assert(NS >= 2 && NS * STAGE == kRing, "stage ring");
+    static_assert(DMA % (2 * NPROD) == 0, "K and V halves split evenly over the producers");
 };
 
-// Producer wait: stage `it` has landed once at most `younger` * DMA of this
-// wave's loads are outstanding; then release the stage to the consumers.
-template <int DMA>
+// Producer wait: this wave's loads of stage t have landed once at most
+// `younger` * DMAP of its loads are in flight (loads complete in order and
+// the counter saturates at 63); then release the stage with the barrier.
+template <int N>
+__device__ __forceinline__ void producer_release()
+{
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int DMAP, int Y>
 __device__ __forceinline__ void producer_sync(int younger)
 {
-#define FDLLM_PSYNC(N) asm volatile("s_waitcnt vmcnt(" #N ")\n\ts_barrier" ::: "memory")
-    const int n = younger * DMA;
-    if (n >= 63) FDLLM_PSYNC(63);
-    else if (n >= 48) FDLLM_PSYNC(48);
-    else if (n >= 32) FDLLM_PSYNC(32);
-    else if (n >= 16) FDLLM_PSYNC(16);
-    else FDLLM_PSYNC(0);
-#undef FDLLM_PSYNC
+    if constexpr (Y <= 0) {
+        producer_release<0>();
+    } else {
+        if (younger >= Y) producer_release<(Y * DMAP > 63 ? 63 : Y * DMAP)>();
+        else producer_sync<DMAP, Y - 1>(younger);
+    }
 }
 
 // Consumer side of the same barrier: its LDS reads of the previous stage have
@@ -85,6 +97,29 @@ __device__ __forceinline__ void producer_sync(int younger)
 __device__ __forceinline__ void consumer_sync()
 {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ void dma16(const unsigned char* src, unsigned char* dst)
+{
+    __builtin_amdgcn_global_load_lds((glb_void*)src, (lds_void*)dst, 16, 0, 0);
+}
+
+// max and sum over the four lanes l, l^16, l^32, l^48 (the 16-lane groups of
+// a wave), with the gfx950 row-swap permutes
+__device__ __forceinline__ float max4(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+
+__device__ __forceinline__ float sum4(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
 __device__ __forceinline__ bf16x8 read_vt_frag(const unsigned char* p0, const unsigned char* p1)
@@ -97,49 +132,59 @@ __device__ __forceinline__ bf16x8 read_vt_frag(const unsigned char* p0, const un
     return r;
 }
 
-// One stage of the ring: TK cache rows from `base` (or side-buffer rows
-// sDup[base ...] for the duplicate tiles), K then V, as 1 KB DMA blocks of 4
-// rows; chunk c of row r lands in slot c ^ (r & 15).
-template <int TK, int DMA>
-__device__ __forceinline__ void issue_stage(unsigned char* st, bool dup, int base, int k1, int ndup,
-                                            const int* sDup, const unsigned char* Kg, const unsigned char* Vg,
-                                            const unsigned char* SKg, const unsigned char* SVg, int lane)
+// One stage of cache rows: TK rows from key `base` (rows past the split end
+// repeat its last key and are masked later), K then V, as 1 KB DMA blocks of
+// 4 rows; chunk c of row r lands in slot c ^ (r & 15).  Producer p issues
+// blocks p, p + NPROD, ...
+template <int TK, int DMA, int NPROD>
+__device__ __forceinline__ void issue_main(unsigned char* st, int base, int k1, const unsigned char* Kg,
+                                           const unsigned char* Vg, int p, int lane)
 {
     const int srow = lane >> 4, slot = lane & 15;
 #pragma unroll
-    for (int i = 0; i < DMA / 2; ++i) {
+    for (int ii = 0; ii < DMA / 2 / NPROD; ++ii) {
+        const int i = ii * NPROD + p;
         const int row = 4 * i + srow;
-        const int chunk = slot ^ (row & 15);
-        size_t src;
-        if (!dup) {
-            const int key = min(base + row, k1 - 1);   // rows past the split are masked later
-            src = (size_t)key * kRowB + chunk * 16;
-        } else {
-            const int kk = base + row;
-            const int j = kk < ndup ? sDup[kk] : sDup[0];
-            src = (size_t)j * kRowB + chunk * 16;
-        }
-        __builtin_amdgcn_global_load_lds((glb_void*)((dup ? SKg : Kg) + src), (lds_void*)(st + i * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((glb_void*)((dup ? SVg : Vg) + src),
-                                         (lds_void*)(st + TK * kRowB + i * 1024), 16, 0, 0);
+        const int key = min(base + row, k1 - 1);
+        const size_t src = (size_t)key * kRowB + ((slot ^ (row & 15)) << 4);
+        dma16(Kg + src, st + i * 1024);
+        dma16(Vg + src, st + TK * kRowB + i * 1024);
     }
 }
 
-template <int RG, int NWR, int NWK>
-__global__ void __launch_bounds__((NWR * NWK + 1) * 64)
+// A stage of side-buffer rows: duplicate number base + r is query row sDup[.]
+template <int TK, int DMA, int NPROD>
+__device__ __forceinline__ void issue_dup(unsigned char* st, int base, int ndup, const int* sDup,
+                                          const unsigned char* SKg, const unsigned char* SVg, int p, int lane)
+{
+    const int srow = lane >> 4, slot = lane & 15;
+#pragma unroll
+    for (int ii = 0; ii < DMA / 2 / NPROD; ++ii) {
+        const int i = ii * NPROD + p;
+        const int row = 4 * i + srow;
+        const int j = sDup[min(base + row, ndup - 1)];
+        const size_t src = (size_t)j * kRowB + ((slot ^ (row & 15)) << 4);
+        dma16(SKg + src, st + i * 1024);
+        dma16(SVg + src, st + TK * kRowB + i * 1024);
+    }
+}
+
+template <int RG, int NWR, int NWK, int NPROD>
+__global__ void __launch_bounds__((NWR * NWK + NPROD) * 64)
 attn_mfma_kernel(AttnArgs a)
 {
-    using C = AttnCfg<RG, NWR, NWK>;
+    using C = AttnCfg<RG, NWR, NWK, NPROD>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int kps = a.keys_per_split;
     const int nq = a.nq;
+    const int G = a.G;
     const int VW = (nq + 31) >> 5;                  // 32-bit words per visibility row
-    int16_t* sSlot = (int16_t*)(smem + C::SCRATCH); // [kps] owner row of written positions, -1
-    uint32_t* sVis = (uint32_t*)(smem + C::SCRATCH + 2 * ((kps + 1) & ~1));   // [nq][VW]
-    int* sPos = (int*)(sVis + (size_t)nq * VW);     // [nq]
-    int* sOwn = sPos + nq;                          // [nq] 1 if the row owns its position
-    int* sDup = sOwn + nq;                          // [nq] rows that do not own their position
-    int* sMisc = sDup + nq;                         // [0] dup count, [2..] tile flags
+    const int tiles_max = (kps + C::TK - 1) / C::TK;
+    int16_t* sSlot = (int16_t*)(smem + C::SCRATCH); // [kps] row owning a written position, or -1
+    int* sFlag = (int*)(smem + C::SCRATCH + 2 * ((kps + 1) & ~1));   // [tiles] tile holds one
+    uint32_t* sVis = (uint32_t*)(sFlag + tiles_max);   // [nq][VW] visibility bits
+    int* sDup = (int*)(sVis + (size_t)nq * VW);     // [nq] rows that do not own their position
+    int* sMisc = sDup + nq;                         // [0] number of such rows
 
     const int total = a.B * a.Hkv * a.splits;
     const int logical = xcd_remap(blockIdx.x, total);
@@ -150,96 +195,159 @@ attn_mfma_kernel(AttnArgs a)
     const int g = bg - b * a.Hkv;
     const int k0 = split * kps;
     const int k1 = min(a.N, k0 + kps);
-    const int nkeys = k1 - k0;
-    const int n_main = (nkeys + C::TK - 1) / C::TK;
+    const int n_main = (k1 - k0 + C::TK - 1) / C::TK;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // wave-uniform in an SGPR, so branches on it stay scalar
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
-    const int G = a.G;
-    int* sTileFlag = sMisc + 2;
-
-    // ---- per-sequence bookkeeping: positions, ownership, duplicates, gating
-    const int32_t* pos_b = a.pos_ids + (size_t)b * nq;
-    for (int j = tid; j < nq; j += C::NT) sPos[j] = pos_b[j];
-    if (a.vis) {
-        for (int k = tid; k < nkeys; k += C::NT) sSlot[k] = -1;
-        for (int t = tid; t < n_main; t += C::NT) sTileFlag[t] = 0;
-        const uint8_t* vb = a.vis + (size_t)b * nq * nq;
-        for (int w = tid; w < nq * VW; w += C::NT) {
-            const int i = w / VW, j0 = (w - i * VW) * 32;
-            uint32_t bits = 0;
-            for (int j = j0; j < min(nq, j0 + 32); ++j)
-                bits |= (vb[(size_t)i * nq + j] ? 1u : 0u) << (j - j0);
-            sVis[w] = bits;
-        }
-    }
-    __syncthreads();
-    for (int j = tid; j < nq; j += C::NT) {
-        int own = 1;
-        for (int q = 0; q < j; ++q)
-            if (sPos[q] == sPos[j]) { own = 0; break; }
-        sOwn[j] = own;
-        const int p = sPos[j];
-        if (own && a.vis && p >= k0 && p < k1) {
-            sSlot[p - k0] = (int16_t)j;
-            sTileFlag[(p - k0) / C::TK] = 1;
-        }
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int n = 0;
-        for (int j = 0; j < nq; ++j)
-            if (!sOwn[j]) sDup[n++] = j;
-        sMisc[0] = n;
-    }
-    __syncthreads();
-    const int ndup = (split == 0) ? sMisc[0] : 0;
-    const int ntot = n_main + (ndup + C::TK - 1) / C::TK;
+    const bool producer = wave >= C::NC;
+    const int wk = wave % NWK, wr = wave / NWK;    // consumer coordinates
+    const int nch = (nq + 63) >> 6;                 // 64-row chunks of the query set
 
     const size_t cache_off = (size_t)bg * a.N * kDH;
     const unsigned char* Kg = (const unsigned char*)((const bf16*)a.Kc + cache_off);
     const unsigned char* Vg = (const unsigned char*)((const bf16*)a.Vc + cache_off);
     const unsigned char* SKg = (const unsigned char*)((const bf16*)a.sideK + (size_t)bg * a.q_max * kDH);
     const unsigned char* SVg = (const unsigned char*)((const bf16*)a.sideV + (size_t)bg * a.q_max * kDH);
+    const int32_t* pos_b = a.pos_ids + (size_t)b * nq;
+    const uint8_t* vis_b = a.vis ? a.vis + (size_t)b * nq * nq : nullptr;
+    const int nunits = vis_b ? nq * nch : 0;        // (visibility row, 64-column chunk) pairs
+
+    // ---- every global load of the consumers is issued before the producers
+    //      start streaming, so none of them waits behind the K/V tiles
+    f32x4 qraw[RG][8];
+    int posr[kMaxChunks];
+    int vbyte[8];
+    if (!producer) {
+        const float* qbase = a.qbuf + (size_t)bg * a.q_max * G * kDH;
+#pragma unroll
+        for (int rg = 0; rg < RG; ++rg) {
+            const int row = (wr * RG + rg) * 16 + lr;
+#pragma unroll
+            for (int h = 0; h < 8; ++h)
+                qraw[rg][h] = row < a.R ? *(const f32x4*)(qbase + (size_t)row * kDH + (h >> 1) * 32 + lg * 8 + (h & 1) * 4)
+                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        if (wave == 0) {
+#pragma unroll
+            for (int c = 0; c < kMaxChunks; ++c) {
+                const int j = 64 * c + lane;
+                posr[c] = j < nq ? pos_b[j] : -1;
+            }
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int u = wave + C::NC * t;
+            vbyte[t] = 0;
+            if (u < nunits) {
+                const int i = u / nch, col = (u - i * nch) * 64 + lane;
+                if (col < nq) vbyte[t] = vis_b[(size_t)i * nq + col];
+            }
+        }
+        if (vis_b) {
+            for (int k = tid; k < kps; k += C::NC * 64) sSlot[k] = -1;
+            for (int t = tid; t < n_main; t += C::NC * 64) sFlag[t] = 0;
+        }
+    }
+    __syncthreads();
 
     float m_run[RG], l_run[RG];
     f32x4 o[RG][8];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
-        m_run[rg] = -INFINITY;
+        m_run[rg] = kNegBig;
         l_run[rg] = 0.f;
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[rg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    const int wk = wave % NWK, wr = wave / NWK;    // consumer coordinates
 
-    if (wave == C::NC) {
-        // ================= producer wave: K/V tiles -> LDS ring =================
+    if (producer) {
+        // ================= producer waves: K/V tiles -> LDS ring =================
+        const int p = wave - C::NC;
         int issued = 0;
-        for (; issued < min(C::NS - 1, ntot); ++issued) {
-            const bool dup = issued >= n_main;
-            issue_stage<C::TK, C::DMA>(smem + (issued % C::NS) * C::STAGE, dup,
-                                       dup ? (issued - n_main) * C::TK : k0 + issued * C::TK, k1, ndup,
-                                       sDup, Kg, Vg, SKg, SVg, lane);
-        }
-        for (int t = 0; t < ntot; ++t) {
-            producer_sync<C::DMA>(issued - t - 1);
-            if (issued < ntot) {
-                const bool dup = issued >= n_main;
-                issue_stage<C::TK, C::DMA>(smem + (issued % C::NS) * C::STAGE, dup,
-                                           dup ? (issued - n_main) * C::TK : k0 + issued * C::TK, k1, ndup,
-                                           sDup, Kg, Vg, SKg, SVg, lane);
-                ++issued;
+        for (; issued < min(C::NS - 1, n_main); ++issued)
+            issue_main<C::TK, C::DMA, NPROD>(smem + (issued % C::NS) * C::STAGE, k0 + issued * C::TK, k1, Kg, Vg, p, lane);
+        int ntot = n_main;
+        int ndup = 0;
+        for (int t = 0;; ++t) {
+            producer_sync<C::DMAP, C::NS - 2>(issued - t - 1);
+            if (t == 0 && split == 0) {
+                // the consumers published the duplicate rows before this barrier
+                ndup = __builtin_amdgcn_readfirstlane(sMisc[0]);
+                ntot = n_main + (ndup + C::TK - 1) / C::TK;
+            }
+            if (t + 1 >= ntot) break;
+            for (; issued < ntot && issued < t + C::NS; ++issued) {
+                unsigned char* st = smem + (issued % C::NS) * C::STAGE;
+                if (issued < n_main)
+                    issue_main<C::TK, C::DMA, NPROD>(st, k0 + issued * C::TK, k1, Kg, Vg, p, lane);
+                else
+                    issue_dup<C::TK, C::DMA, NPROD>(st, (issued - n_main) * C::TK, ndup, sDup, SKg, SVg, p, lane);
             }
         }
     } else {
         // ================= consumer waves =================
+        // per-sequence bookkeeping while the first tiles stream in
+        if (wave == 0) {
+            // row j owns the cache write of its position unless an earlier
+            // row has the same position; the others are listed in sDup
+            int ndup = 0;
+#pragma unroll
+            for (int c = 0; c < kMaxChunks; ++c) {
+                if (64 * c >= nq) break;
+                const int j = 64 * c + lane;
+                bool own = true;
+#pragma unroll
+                for (int cq = 0; cq <= c; ++cq) {
+                    const int lim = min(64, nq - 64 * cq);
+                    for (int t = 0; t < lim; ++t) {
+                        const int pq = __builtin_amdgcn_readlane(posr[cq], t);
+                        own = own && !(pq == posr[c] && 64 * cq + t < j);
+                    }
+                }
+                const bool valid = j < nq;
+                const uint64_t dm = __builtin_amdgcn_ballot_w64(valid && !own);
+                const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(dm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)dm, 0u));
+                if (valid && !own) sDup[ndup + below] = j;
+                ndup += __builtin_popcountll(dm);
+                if (vis_b && valid && own) {
+                    const int pp = posr[c];
+                    if (pp >= k0 && pp < k1) {
+                        sSlot[pp - k0] = (int16_t)j;
+                        sFlag[(pp - k0) / C::TK] = 1;
+                    }
+                }
+            }
+            if (lane == 0) sMisc[0] = ndup;
+        }
+        // visibility rows as bit words: chunk c of row i fills words 2c, 2c+1
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int u = wave + C::NC * t;
+            if (u < nunits) {
+                const int i = u / nch, c = u - i * nch;
+                const uint64_t m = __builtin_amdgcn_ballot_w64(vbyte[t] != 0);
+                if (lane == 0) {
+                    sVis[i * VW + 2 * c] = (uint32_t)m;
+                    if (2 * c + 1 < VW) sVis[i * VW + 2 * c + 1] = (uint32_t)(m >> 32);
+                }
+            }
+        }
+        for (int u = wave + C::NC * 8; u < nunits; u += C::NC) {
+            const int i = u / nch, c = u - i * nch, col = c * 64 + lane;
+            const int v = col < nq ? vis_b[(size_t)i * nq + col] : 0;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(v != 0);
+            if (lane == 0) {
+                sVis[i * VW + 2 * c] = (uint32_t)m;
+                if (2 * c + 1 < VW) sVis[i * VW + 2 * c + 1] = (uint32_t)(m >> 32);
+            }
+        }
+
         // query fragments: lane holds row (wr*RG + rg)*16 + lr, dims 32c + 8lg .. +7,
-        // split into bf16 hi + lo so the scores keep q's fp32 precision
-        const float* qbase = a.qbuf + (size_t)bg * a.q_max * G * kDH;
+        // as bf16 hi + lo parts so the scores keep q's fp32 precision; the
+        // scale (log2 e / sqrt(dh)) puts the scores in log2 units
         bf16x8 qh[RG][4], ql[RG][4];
         int qrow[RG];
 #pragma unroll
@@ -247,176 +355,141 @@ attn_mfma_kernel(AttnArgs a)
             const int row = (wr * RG + rg) * 16 + lr;
             qrow[rg] = row < a.R ? row / G : -1;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                float x[8];
-                if (row < a.R) {
-                    // scores come out of the MFMA already in log2 units
-                    const f32x4 u = *(const f32x4*)(qbase + (size_t)row * kDH + c * 32 + lg * 8) * a.scale_log2;
-                    const f32x4 v = *(const f32x4*)(qbase + (size_t)row * kDH + c * 32 + lg * 8 + 4) * a.scale_log2;
-                    x[0] = u[0]; x[1] = u[1]; x[2] = u[2]; x[3] = u[3];
-                    x[4] = v[0]; x[5] = v[1]; x[6] = v[2]; x[7] = v[3];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) x[e] = 0.f;
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const bf16 hi = (bf16)x[e];
-                    qh[rg][c][e] = hi;
-                    ql[rg][c][e] = (bf16)(x[e] - (float)hi);
-                }
-            }
-        }
-
-        for (int it = 0; it < ntot; ++it) {
-            consumer_sync();
-            const unsigned char* st = smem + (it % C::NS) * C::STAGE;
-            const unsigned char* sK = st;
-            const unsigned char* sV = st + C::TK * kRowB;
-            const bool dup = it >= n_main;
-
-            // ---- S^T = K Q^T for this wave's 32 keys
-            f32x4 sc[RG][2];
-#pragma unroll
-            for (int rg = 0; rg < RG; ++rg) {
-                sc[rg][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-                sc[rg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-            // all K fragments of the wave's 32 keys first (their LDS reads overlap),
-            // then the MFMAs; row groups past R run on zero q and are discarded
-            bf16x8 kf[2][4];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const int row = wk * C::KW + kb * 16 + lr;
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    kf[kb][c] = *(const bf16x8*)(sK + row * kRowB + (((c * 4 + lg) ^ lr) << 4));
-            }
-#pragma unroll
             for (int c = 0; c < 4; ++c)
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int rg = 0; rg < RG; ++rg) {
-                        sc[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][c], qh[rg][c], sc[rg][kb], 0, 0, 0);
-                        sc[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][c], ql[rg][c], sc[rg][kb], 0, 0, 0);
-                    }
-
-            // ---- scale, mask, online softmax (lane: row lr, keys kb*16 + 4lg + i)
-            const int kl0 = wk * C::KW + lg * 4;                     // key within the tile
-            const bool gate = dup || (a.vis && sTileFlag[it]);
-            const int tbase = dup ? (it - n_main) * C::TK : k0 + it * C::TK;
-            // keys past the split (or past the duplicate list) are masked; a
-            // gated key (written this step, or a duplicate row) needs the
-            // query's visibility bit for its owning row
-            const int kend = dup ? ndup : k1;
-            bool keep_k[2][4];
-            int owner_k[2][4];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int key = tbase + kl0 + kb * 16 + i;
-                    keep_k[kb][i] = key < kend;
-                    owner_k[kb][i] = -1;
+                for (int e = 0; e < 8; ++e) {
+                    const float x = qraw[rg][2 * c + (e >> 2)][e & 3] * a.scale_log2;
+                    const bf16 hi = (bf16)x;
+                    qh[rg][c][e] = hi;
+                    ql[rg][c][e] = (bf16)(x - (float)hi);
                 }
-            if (gate) {
+        }
+
+        // per-lane LDS offsets of the fragments within a stage
+        int kofs[4], vofs[8];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kofs[c] = (wk * C::KW + lr) * kRowB + (((c * 4 + lg) ^ lr) << 4);
+        const int rowA = wk * C::KW + 4 * lg + (lr >> 2);   // rowA + 16 has the same swizzle
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            const int chunk = 2 * db + ((lr & 3) >> 1);
+            vofs[db] = C::TK * kRowB + rowA * kRowB + ((chunk ^ (rowA & 15)) << 4) + ((lr & 1) << 3);
+        }
+
+        int ntot = n_main;
+        int ndup = 0;
+        for (int it0 = 0; it0 < ntot; it0 += C::NS) {
+#pragma unroll
+            for (int s = 0; s < C::NS; ++s) {
+                const int it = it0 + s;
+                if (it >= ntot) break;
+                consumer_sync();
+                if (it == 0 && split == 0) {
+                    ndup = __builtin_amdgcn_readfirstlane(sMisc[0]);
+                    ntot = n_main + (ndup + C::TK - 1) / C::TK;
+                }
+                const unsigned char* st = smem + s * C::STAGE;
+
+                // ---- S^T = K Q^T for this wave's 32 keys (rows past R run on zero q)
+                bf16x8 kf[2][4];
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int key = tbase + kl0 + kb * 16 + i;
-                        if (keep_k[kb][i]) owner_k[kb][i] = dup ? sDup[key] : sSlot[key - k0];
-                        if (dup && !a.vis) owner_k[kb][i] = -1;
-                    }
-            }
+                    for (int c = 0; c < 4; ++c) kf[kb][c] = *(const bf16x8*)(st + kofs[c] + kb * 16 * kRowB);
+                f32x4 sc[RG][2];
 #pragma unroll
-            for (int rg = 0; rg < RG; ++rg) {
-                float mx = -INFINITY;
+                for (int rg = 0; rg < RG; ++rg) {
+                    sc[rg][0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    sc[rg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int c = 0; c < 4; ++c)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        float s = sc[rg][kb][i];
-                        bool keep = keep_k[kb][i];
-                        if (gate) {
-                            const int j = owner_k[kb][i];
-                            const bool seen = qrow[rg] >= 0 &&
-                                              ((sVis[qrow[rg] * VW + (max(j, 0) >> 5)] >> (max(j, 0) & 31)) & 1u);
-                            keep = keep && (j < 0 || seen);
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int rg = 0; rg < RG; ++rg) {
+                            sc[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][c], qh[rg][c], sc[rg][kb], 0, 0, 0);
+                            sc[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][c], ql[rg][c], sc[rg][kb], 0, 0, 0);
                         }
-                        s = keep ? s : -INFINITY;
-                        sc[rg][kb][i] = s;
-                        mx = fmaxf(mx, s);
-                    }
-                mx = fmaxf(mx, __shfl_xor(mx, 16));
-                mx = fmaxf(mx, __shfl_xor(mx, 32));
-                // lazy rescale: a row's exponentials stay relative to a
-                // reference max that only moves when the row's max exceeds it
-                // by more than 2^8, so p <= 256 and the output accumulators are
-                // rescaled only a few times per split.  The decision is per
-                // row (each row's result depends on its own scores only); the
-                // whole block is skipped when no row of the wave grows.
-                const bool grow = mx > m_run[rg] + 8.f;
-                if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-                    if (grow) {
-                        const float alpha = (m_run[rg] == -INFINITY) ? 0.f : exp2f(m_run[rg] - mx);
-                        l_run[rg] *= alpha;
-#pragma unroll
-                        for (int db = 0; db < 8; ++db) o[rg][db] *= alpha;
-                        m_run[rg] = mx;
-                    }
-                }
-                const float msub = (m_run[rg] == -INFINITY) ? 0.f : m_run[rg];
-                float lsum = 0.f;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float p = exp2f(sc[rg][kb][i] - msub);   // exp2(-inf) = 0
-                        sc[rg][kb][i] = p;
-                        lsum += p;
-                    }
-                l_run[rg] += lsum;
-            }
 
-            // ---- O^T += V^T P^T over the wave's 32 keys
-            bf16x8 pf[RG];
+                // ---- masks (lane: row lr, keys kb*16 + 4lg + i of the wave's 32).
+                // Only the split's last tile, tiles holding positions written
+                // this step (under a visibility mask) and duplicate tiles need them.
+                const bool dup = it >= n_main;
+                const int tbase = dup ? (it - n_main) * C::TK : k0 + it * C::TK;
+                const int kend = dup ? ndup : k1;
+                const bool gate = vis_b && (dup || __builtin_amdgcn_readfirstlane(sFlag[it]) != 0);
+                if (gate || tbase + C::TK > kend) {
 #pragma unroll
-            for (int rg = 0; rg < RG; ++rg)
+                    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pf[rg][i] = (bf16)sc[rg][0][i];
-                    pf[rg][4 + i] = (bf16)sc[rg][1][i];
+                        for (int i = 0; i < 4; ++i) {
+                            const int key = tbase + wk * C::KW + kb * 16 + lg * 4 + i;
+                            const bool in = key < kend;
+                            int j = -1;
+                            if (gate && in) j = dup ? sDup[key] : sSlot[key - k0];
+#pragma unroll
+                            for (int rg = 0; rg < RG; ++rg) {
+                                bool keep = in;
+                                if (j >= 0)
+                                    keep = keep && qrow[rg] >= 0 && ((sVis[qrow[rg] * VW + (j >> 5)] >> (j & 31)) & 1u);
+                                if (!keep) sc[rg][kb][i] = -INFINITY;
+                            }
+                        }
                 }
-            const int rowA = wk * C::KW + 4 * lg + (lr >> 2);
-            const int rowB = rowA + 16;
-            bf16x8 vf[8];
+
+                // ---- online softmax.  Lazy rescale: a row's exponentials stay
+                // relative to a reference max that only moves when the row's
+                // max exceeds it by more than 2^8, so p <= 256 and the
+                // accumulators are rescaled a few times per split.  The
+                // decision is per row; the block is skipped when no row grows.
+                bf16x8 pf[RG];
 #pragma unroll
-            for (int db = 0; db < 8; ++db) {
-                const int chunk = 2 * db + ((lr & 3) >> 1);
-                const int half = (lr & 1) << 3;
-                const unsigned char* pA = sV + rowA * kRowB + ((chunk ^ (rowA & 15)) << 4) + half;
-                const unsigned char* pB = sV + rowB * kRowB + ((chunk ^ (rowB & 15)) << 4) + half;
-                vf[db] = read_vt_frag(pA, pB);
+                for (int rg = 0; rg < RG; ++rg) {
+                    float mx = fmaxf(fmaxf(fmaxf(sc[rg][0][0], sc[rg][0][1]), fmaxf(sc[rg][0][2], sc[rg][0][3])),
+                                     fmaxf(fmaxf(sc[rg][1][0], sc[rg][1][1]), fmaxf(sc[rg][1][2], sc[rg][1][3])));
+                    mx = max4(mx);
+                    const bool grow = mx > m_run[rg] + 8.f;
+                    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                        if (grow) {
+                            const float alpha = __builtin_amdgcn_exp2f(m_run[rg] - mx);
+                            l_run[rg] *= alpha;
+#pragma unroll
+                            for (int db = 0; db < 8; ++db) o[rg][db] *= alpha;
+                            m_run[rg] = mx;
+                        }
+                    }
+                    float lsum = 0.f;
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float pv = __builtin_amdgcn_exp2f(sc[rg][kb][i] - m_run[rg]);   // exp2(-inf) = 0
+                            lsum += pv;
+                            pf[rg][kb * 4 + i] = (bf16)pv;
+                        }
+                    l_run[rg] += lsum;
+                }
+
+                // ---- O^T += V^T P^T over the wave's 32 keys
+                bf16x8 vf[8];
+#pragma unroll
+                for (int db = 0; db < 8; ++db) vf[db] = read_vt_frag(st + vofs[db], st + vofs[db] + 16 * kRowB);
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+#pragma unroll
+                    for (int rg = 0; rg < RG; ++rg)
+                        o[rg][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pf[rg], o[rg][db], 0, 0, 0);
             }
-#pragma unroll
-            for (int db = 0; db < 8; ++db)
-#pragma unroll
-                for (int rg = 0; rg < RG; ++rg)
-                    o[rg][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pf[rg], o[rg][db], 0, 0, 0);
         }
         // per-lane sums -> row sums (row lr is spread over the 4 lane groups)
 #pragma unroll
-        for (int rg = 0; rg < RG; ++rg) {
-            l_run[rg] += __shfl_xor(l_run[rg], 16);
-            l_run[rg] += __shfl_xor(l_run[rg], 32);
-        }
+        for (int rg = 0; rg < RG; ++rg) l_run[rg] = sum4(l_run[rg]);
     }
     __syncthreads();   // the LDS ring is free from here on
 
     // ---- merge the key-split consumer waves through LDS (tree over wk)
-    const bool consumer = wave < C::NC;
+    const bool consumer = !producer;
     if (NWK > 1) {
         float* scr = (float*)smem;
         constexpr int SLOT = RG * 64 * (32 + 2);
@@ -441,8 +514,8 @@ attn_mfma_kernel(AttnArgs a)
                     const float mb = src[RG * 64 * 32 + (rg * 64 + lane) * 2 + 0];
                     const float lb = src[RG * 64 * 32 + (rg * 64 + lane) * 2 + 1];
                     const float mn = fmaxf(m_run[rg], mb);
-                    const float fa = (m_run[rg] == -INFINITY) ? 0.f : exp2f(m_run[rg] - mn);
-                    const float fb = (mb == -INFINITY) ? 0.f : exp2f(mb - mn);
+                    const float fa = __builtin_amdgcn_exp2f(m_run[rg] - mn);
+                    const float fb = __builtin_amdgcn_exp2f(mb - mn);
 #pragma unroll
                     for (int db = 0; db < 8; ++db) {
                         const f32x4 ob = *(const f32x4*)(src + ((rg * 8 + db) * 64 + lane) * 4);
@@ -540,19 +613,20 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a)
     if (d4 == 0) a.LSE[orow] = L > 0.f ? (mx + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
-template <int RG, int NWR, int NWK>
+template <int RG, int NWR, int NWK, int NPROD>
 hipError_t launch_cfg(const AttnArgs& a, hipStream_t s)
 {
-    using C = AttnCfg<RG, NWR, NWK>;
+    using C = AttnCfg<RG, NWR, NWK, NPROD>;
+    if (a.nq > 64 * kMaxChunks || a.keys_per_split % C::TK != 0) return hipErrorInvalidValue;
     const int VW = (a.nq + 31) / 32;
     const int tiles = (a.keys_per_split + C::TK - 1) / C::TK;
-    const size_t book = 2 * (size_t)((a.keys_per_split + 1) & ~1) + 4 * (size_t)a.nq * VW +
-                        4 * (3 * (size_t)a.nq + 2 + tiles + 2);
+    const size_t book = 2 * (size_t)((a.keys_per_split + 1) & ~1) + 4 * (size_t)tiles + 4 * (size_t)a.nq * VW +
+                        4 * ((size_t)a.nq + 1);
     if (C::SCRATCH + book > 160 * 1024) return hipErrorInvalidValue;
     const size_t shm = C::SCRATCH + book;
     const int total = a.B * a.Hkv * a.splits;
     const int grid = ((total + 7) / 8) * 8;
-    auto kern = attn_mfma_kernel<RG, NWR, NWK>;
+    auto kern = attn_mfma_kernel<RG, NWR, NWK, NPROD>;
     // raise the dynamic LDS limit; a refusal shows up as a launch error below
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     (void)hipGetLastError();
@@ -570,21 +644,23 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s)
 int attn_mfma_tile_keys(int R)
 {
     const int r16 = (R + 15) / 16;
-    return r16 <= 9 ? 64 : 32;
+    return r16 <= 6 ? 64 : 32;
 }
 
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s)
 {
     if (a.B * a.Hkv * a.splits == 0 || a.R == 0) return hipSuccess;
+    // row groups of 16 per wave x row waves x key waves x producer waves; at
+    // most two waves per SIMD once a wave holds two or more row groups
     const int r16 = (a.R + 15) / 16;
-    if (r16 <= 1) return launch_cfg<1, 1, 2>(a, s);
-    if (r16 <= 2) return launch_cfg<1, 2, 2>(a, s);
-    if (r16 <= 4) return launch_cfg<1, 4, 2>(a, s);
-    if (r16 <= 6) return launch_cfg<2, 3, 2>(a, s);
-    if (r16 <= 9) return launch_cfg<3, 3, 2>(a, s);
-    if (r16 <= 12) return launch_cfg<2, 6, 1>(a, s);
-    if (r16 <= 14) return launch_cfg<2, 7, 1>(a, s);
-    if (r16 <= 18) return launch_cfg<3, 6, 1>(a, s);
+    if (r16 <= 1) return launch_cfg<1, 1, 2, 1>(a, s);
+    if (r16 <= 2) return launch_cfg<1, 2, 2, 2>(a, s);
+    if (r16 <= 3) return launch_cfg<1, 3, 2, 2>(a, s);
+    if (r16 <= 4) return launch_cfg<1, 4, 2, 2>(a, s);
+    if (r16 <= 6) return launch_cfg<2, 3, 2, 2>(a, s);
+    if (r16 <= 10) return launch_cfg<2, 5, 1, 2>(a, s);
+    if (r16 <= 14) return launch_cfg<2, 7, 1, 1>(a, s);
+    if (r16 <= 18) return launch_cfg<3, 6, 1, 1>(a, s);
     return hipErrorInvalidValue;
 }
 

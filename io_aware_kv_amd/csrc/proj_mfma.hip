@@ -300,6 +300,7 @@ static const ProjChoice kProjChoices[] = {
     {48, 2}, {64, 2}, {16, 2},              // 9-11: narrow tiles with a 3-stage ring (2 workgroups per CU)
     {32, 4}, {64, 4},                       // 12-13: 64-column tiles, 3-stage ring
     {128, 8}, {128, 8}, {64, 4}, {128, 4}, {64, 8}, {48, 2}, {64, 4},   // 14-20: two producer waves
+    {16, 2}, {32, 2},                                                     // 21-22: two producers, 3 stages
 };
 
 int proj_mfma_block_m(int M)
@@ -311,15 +312,17 @@ int proj_mfma_block_m(int M)
     return 128;
 }
 
+// Defaults measured on MI355X (bench sweeps of the layer workloads): narrow
+// tiles with a 3-stage ring (two workgroups per CU) and two producer waves for
+// up to 48 rows; 64x64 tiles up to 128 rows; 128x128 tiles with 64-deep
+// stages (four in the ring) beyond.
 static int default_choice(int M)
 {
-    switch (proj_mfma_block_m(M)) {
-        case 16: return 1;
-        case 32: return 2;
-        case 48: return 3;
-        case 64: return 4;
-        default: return 5;
-    }
+    if (M <= 16) return 21;
+    if (M <= 32) return 22;
+    if (M <= 48) return 19;
+    if (M <= 128) return 16;
+    return 14;
 }
 
 int proj_mfma_columns_per_tile(int M, int choice)
@@ -356,6 +359,8 @@ hipError_t launch_proj_mfma(const ProjArgs& a, hipStream_t s)
         case 18: return launch_tile<64, 8, 2, 2, 8, 64, 2>(a, s);
         case 19: return launch_tile<48, 2, 1, 1, 3, 128, 2>(a, s);
         case 20: return launch_tile<64, 4, 2, 2, 3, 64, 2>(a, s);
+        case 21: return launch_tile<16, 2, 1, 1, 3, 128, 2>(a, s);
+        case 22: return launch_tile<32, 2, 1, 1, 3, 128, 2>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
