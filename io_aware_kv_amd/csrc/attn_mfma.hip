@@ -181,8 +181,9 @@ attn_mfma_kernel(AttnArgs a)
     const int VW = (nq + 31) >> 5;                  // 32-bit words per visibility row
     const int tiles_max = (kps + C::TK - 1) / C::TK;
     int16_t* sSlot = (int16_t*)(smem + C::SCRATCH); // [kps] row owning a written position, or -1
-    int* sFlag = (int*)(smem + C::SCRATCH + 2 * ((kps + 1) & ~1));   // [tiles] tile holds one
-    uint32_t* sVis = (uint32_t*)(sFlag + tiles_max);   // [nq][VW] visibility bits
+    // [tiles][2] bit k of a tile: its key k is a position written this step
+    uint32_t* sMask = (uint32_t*)(smem + C::SCRATCH + 2 * ((kps + 1) & ~1));
+    uint32_t* sVis = sMask + 2 * tiles_max;         // [nq][VW] visibility bits
     int* sDup = (int*)(sVis + (size_t)nq * VW);     // [nq] rows that do not own their position
     int* sMisc = sDup + nq;                         // [0] number of such rows
 
@@ -222,33 +223,29 @@ attn_mfma_kernel(AttnArgs a)
     int vbyte[8];
     if (!producer) {
         const float* qbase = a.qbuf + (size_t)bg * a.q_max * G * kDH;
+        // indices are clamped into range and the values of padding lanes
+        // discarded afterwards, so the loads carry no branches
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
-            const int row = (wr * RG + rg) * 16 + lr;
+            const int row = min((wr * RG + rg) * 16 + lr, a.R - 1);
 #pragma unroll
             for (int h = 0; h < 8; ++h)
-                qraw[rg][h] = row < a.R ? *(const f32x4*)(qbase + (size_t)row * kDH + (h >> 1) * 32 + lg * 8 + (h & 1) * 4)
-                                        : f32x4{0.f, 0.f, 0.f, 0.f};
+                qraw[rg][h] = *(const f32x4*)(qbase + (size_t)row * kDH + (h >> 1) * 32 + lg * 8 + (h & 1) * 4);
         }
         if (wave == 0) {
 #pragma unroll
-            for (int c = 0; c < kMaxChunks; ++c) {
-                const int j = 64 * c + lane;
-                posr[c] = j < nq ? pos_b[j] : -1;
-            }
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int u = wave + C::NC * t;
-            vbyte[t] = 0;
-            if (u < nunits) {
-                const int i = u / nch, col = (u - i * nch) * 64 + lane;
-                if (col < nq) vbyte[t] = vis_b[(size_t)i * nq + col];
-            }
+            for (int c = 0; c < kMaxChunks; ++c)
+                if (64 * c < nq) posr[c] = pos_b[min(64 * c + lane, nq - 1)];
         }
         if (vis_b) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int u = min(wave + C::NC * t, nunits - 1);
+                const int i = u / nch, col = min((u - i * nch) * 64 + lane, nq - 1);
+                vbyte[t] = vis_b[(size_t)i * nq + col];
+            }
             for (int k = tid; k < kps; k += C::NC * 64) sSlot[k] = -1;
-            for (int t = tid; t < n_main; t += C::NC * 64) sFlag[t] = 0;
+            for (int t = tid; t < 2 * n_main; t += C::NC * 64) sMask[t] = 0u;
         }
     }
     __syncthreads();
@@ -298,6 +295,7 @@ attn_mfma_kernel(AttnArgs a)
             for (int c = 0; c < kMaxChunks; ++c) {
                 if (64 * c >= nq) break;
                 const int j = 64 * c + lane;
+                if (j >= nq) posr[c] = -1;   // padding lanes (their load repeated the last row)
                 bool own = true;
 #pragma unroll
                 for (int cq = 0; cq <= c; ++cq) {
@@ -315,8 +313,9 @@ attn_mfma_kernel(AttnArgs a)
                 if (vis_b && valid && own) {
                     const int pp = posr[c];
                     if (pp >= k0 && pp < k1) {
-                        sSlot[pp - k0] = (int16_t)j;
-                        sFlag[(pp - k0) / C::TK] = 1;
+                        const int kt = pp - k0;
+                        sSlot[kt] = (int16_t)j;
+                        atomicOr(&sMask[2 * (kt / C::TK) + ((kt % C::TK) >> 5)], 1u << (kt & 31));
                     }
                 }
             }
@@ -328,7 +327,7 @@ attn_mfma_kernel(AttnArgs a)
             const int u = wave + C::NC * t;
             if (u < nunits) {
                 const int i = u / nch, c = u - i * nch;
-                const uint64_t m = __builtin_amdgcn_ballot_w64(vbyte[t] != 0);
+                const uint64_t m = __builtin_amdgcn_ballot_w64(vbyte[t] != 0 && c * 64 + lane < nq);
                 if (lane == 0) {
                     sVis[i * VW + 2 * c] = (uint32_t)m;
                     if (2 * c + 1 < VW) sVis[i * VW + 2 * c + 1] = (uint32_t)(m >> 32);
@@ -402,24 +401,34 @@ attn_mfma_kernel(AttnArgs a)
                     sc[rg][0] = f32x4{0.f, 0.f, 0.f, 0.f};
                     sc[rg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
+                // (hi and lo passes alternate between the accumulators so that
+                // back-to-back MFMAs do not depend on each other)
 #pragma unroll
-                for (int c = 0; c < 4; ++c)
+                for (int c = 0; c < 4; ++c) {
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                        for (int rg = 0; rg < RG; ++rg) {
+                        for (int rg = 0; rg < RG; ++rg)
                             sc[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][c], qh[rg][c], sc[rg][kb], 0, 0, 0);
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                        for (int rg = 0; rg < RG; ++rg)
                             sc[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][c], ql[rg][c], sc[rg][kb], 0, 0, 0);
-                        }
+                }
+                // all eight K fragment reads are issued before the first MFMA waits on one
+                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 16 * RG, 0);
 
                 // ---- masks (lane: row lr, keys kb*16 + 4lg + i of the wave's 32).
-                // Only the split's last tile, tiles holding positions written
-                // this step (under a visibility mask) and duplicate tiles need them.
+                // Under a visibility mask a tile holding positions written this
+                // step gates just those keys; the split's last tile and the
+                // duplicate tiles take the general path.
                 const bool dup = it >= n_main;
                 const int tbase = dup ? (it - n_main) * C::TK : k0 + it * C::TK;
                 const int kend = dup ? ndup : k1;
-                const bool gate = vis_b && (dup || __builtin_amdgcn_readfirstlane(sFlag[it]) != 0);
-                if (gate || tbase + C::TK > kend) {
+                if (dup || tbase + C::TK > kend) {
+                    const bool gate = vis_b != nullptr;
 #pragma unroll
                     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -436,6 +445,24 @@ attn_mfma_kernel(AttnArgs a)
                                 if (!keep) sc[rg][kb][i] = -INFINITY;
                             }
                         }
+                } else if (vis_b) {
+                    uint32_t wm = __builtin_amdgcn_readfirstlane(sMask[2 * it + wk]);
+                    while (wm != 0u) {
+                        const int k = __builtin_ctz(wm);          // key wk*32 + k of the tile
+                        wm &= wm - 1u;
+                        const int j = __builtin_amdgcn_readfirstlane(sSlot[it * C::TK + wk * C::KW + k]);
+                        const bool mine = lg == ((k >> 2) & 3);
+#pragma unroll
+                        for (int rg = 0; rg < RG; ++rg) {
+                            const bool hide = mine && (qrow[rg] < 0 ||
+                                                       !((sVis[max(qrow[rg], 0) * VW + (j >> 5)] >> (j & 31)) & 1u));
+#pragma unroll
+                            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    if (kb == (k >> 4) && i == (k & 3) && hide) sc[rg][kb][i] = -INFINITY;
+                        }
+                    }
                 }
 
                 // ---- online softmax.  Lazy rescale: a row's exponentials stay
@@ -577,31 +604,62 @@ attn_mfma_kernel(AttnArgs a)
 
 // Merge of the cache splits: O = sum_s 2^(m_s - M) acc_s / L and
 // LSE = (M + log2 L) ln 2 with M = max_s m_s, L = sum_s 2^(m_s - M) l_s.
-// One thread per (query row, 4 output dims); 8 rows per workgroup.
+// A workgroup takes 8 query rows of one (sequence, kv head): the (m, l) of
+// every split go through LDS first, then each thread sums 4 output dims of
+// its row over the splits with the loads of 8 splits in flight at a time.
+constexpr int kCombineRows = 8;
+
 __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a)
 {
-    const int rows_per_wg = 8;
-    const int wgs_per_bg = (a.R + rows_per_wg - 1) / rows_per_wg;
-    const int bg = blockIdx.x / wgs_per_bg;
-    const int row = (blockIdx.x - bg * wgs_per_bg) * rows_per_wg + (threadIdx.x >> 5);
-    const int d4 = threadIdx.x & 31;
-    if (row >= a.R) return;
+    extern __shared__ float sW[];   // [kCombineRows][S]: split maxima, then their weights
     const int S = a.splits;
-    const size_t pbase = (size_t)bg * S * a.Rpad + row;
-    float mx = -INFINITY;
-    for (int s = 0; s < S; ++s) mx = fmaxf(mx, a.aml[(pbase + (size_t)s * a.Rpad) * 2]);
-    float L = 0.f;
+    const int wgs_per_bg = (a.R + kCombineRows - 1) / kCombineRows;
+    const int bg = blockIdx.x / wgs_per_bg;
+    const int r0 = (blockIdx.x - bg * wgs_per_bg) * kCombineRows;
+    const int tid = threadIdx.x;
+    const size_t pbase = (size_t)bg * S * a.Rpad;
+    for (int t = tid; t < kCombineRows * S; t += 256) {
+        const int r = t / S, sp = t - r * S;
+        sW[t] = a.aml[(pbase + (size_t)sp * a.Rpad + min(r0 + r, a.R - 1)) * 2];
+    }
+    __syncthreads();
+    // the 32 threads of a row reduce its maxima, then turn them into weights
+    const int r = tid >> 5, d4 = tid & 31;
+    float mx = kNegBig;
+    for (int sp = d4; sp < S; sp += 32) mx = fmaxf(mx, sW[r * S + sp]);
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
+    __syncthreads();
+    for (int sp = d4; sp < S; sp += 32) sW[r * S + sp] = __builtin_amdgcn_exp2f(sW[r * S + sp] - mx);
+    __syncthreads();
+    const int row = r0 + r;
+    const int rowc = min(row, a.R - 1);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (mx != -INFINITY) {
-#pragma unroll 4
-        for (int s = 0; s < S; ++s) {
-            const size_t pr = pbase + (size_t)s * a.Rpad;
-            const float ms = a.aml[pr * 2];
-            const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - mx);
-            L += a.aml[pr * 2 + 1] * w;
-            acc += *(const f32x4*)(a.apart + pr * kDH + d4 * 4) * w;
+    float L = 0.f;
+    int sp = 0;
+    for (; sp + 8 <= S; sp += 8) {
+        f32x4 v[8];
+        float l[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const size_t pr = pbase + (size_t)(sp + u) * a.Rpad + rowc;
+            v[u] = *(const f32x4*)(a.apart + pr * kDH + d4 * 4);
+            l[u] = a.aml[pr * 2 + 1];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const float w = sW[r * S + sp + u];
+            acc += v[u] * w;
+            L += l[u] * w;
         }
     }
+    for (; sp < S; ++sp) {
+        const size_t pr = pbase + (size_t)sp * a.Rpad + rowc;
+        const float w = sW[r * S + sp];
+        acc += *(const f32x4*)(a.apart + pr * kDH + d4 * 4) * w;
+        L += a.aml[pr * 2 + 1] * w;
+    }
+    if (row >= a.R) return;
     const int b = bg / a.Hkv, g = bg - b * a.Hkv;
     const int j = row / a.G, hl = row - j * a.G;
     const size_t orow = ((size_t)b * a.nq + j) * a.H + g * a.G + hl;
@@ -620,7 +678,7 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s)
     if (a.nq > 64 * kMaxChunks || a.keys_per_split % C::TK != 0) return hipErrorInvalidValue;
     const int VW = (a.nq + 31) / 32;
     const int tiles = (a.keys_per_split + C::TK - 1) / C::TK;
-    const size_t book = 2 * (size_t)((a.keys_per_split + 1) & ~1) + 4 * (size_t)tiles + 4 * (size_t)a.nq * VW +
+    const size_t book = 2 * (size_t)((a.keys_per_split + 1) & ~1) + 8 * (size_t)tiles + 4 * (size_t)a.nq * VW +
                         4 * ((size_t)a.nq + 1);
     if (C::SCRATCH + book > 160 * 1024) return hipErrorInvalidValue;
     const size_t shm = C::SCRATCH + book;
@@ -633,8 +691,10 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s)
     hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), shm, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
-    const int cgrid = a.B * a.Hkv * ((a.R + 7) / 8);
-    hipLaunchKernelGGL(attn_combine_kernel, dim3(cgrid), dim3(256), 0, s, a);
+    const int cgrid = a.B * a.Hkv * ((a.R + kCombineRows - 1) / kCombineRows);
+    const size_t cshm = sizeof(float) * kCombineRows * (size_t)a.splits;
+    if (cshm > 64 * 1024) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(attn_combine_kernel, dim3(cgrid), dim3(256), cshm, s, a);
     return hipGetLastError();
 }
 

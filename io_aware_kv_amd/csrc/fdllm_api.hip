@@ -70,9 +70,9 @@ Plan make_plan(const fdllm_ctx* h, int nq)
     const int M = c.B * nq;
     p.splitk = 1;
     if (p.proj_family == FAMILY_MFMA && M > 0) {
-        p.bm = proj_mfma_block_m(M);   // rows per tile (the tile table may use the same or fewer)
-        p.proj_tiles = ((M + p.bm - 1) / p.bm) * (c.H + 2 * c.Hkv) *
-                       (128 / proj_mfma_columns_per_tile(M, env_int("FDLLM_PROJ_TILE", 0)));
+        const ProjTile pt = proj_mfma_tile(M, c.H + 2 * c.Hkv, env_int("FDLLM_PROJ_TILE", 0));
+        p.bm = pt.bm;
+        p.proj_tiles = ((M + pt.bm - 1) / pt.bm) * (c.H + 2 * c.Hkv) * (128 / pt.bn);
     }
 
     // attention: (sequence, kv head) pairs x cache splits; one workgroup fills

@@ -65,8 +65,8 @@ hipError_t launch_proj_mfma(const ProjArgs& a, hipStream_t s);
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
 
 // Tile geometry of the MFMA kernels, needed by the host planner.
-int proj_mfma_block_m(int M);
-int proj_mfma_columns_per_tile(int M, int choice);
+struct ProjTile { int bm, bn, choice; };
+ProjTile proj_mfma_tile(int M, int heads, int choice);   // choice 0: the default for M rows
 int attn_mfma_tile_keys(int R);
 
 // Conversions between storage types and fp32.

@@ -65,14 +65,6 @@ __device__ __forceinline__ int chunk_swz(int row)
     return BK == 128 ? (row & 15) : ((row >> 1) & 7);
 }
 
-__device__ __forceinline__ bool owns_position(const int32_t* pos_b, int j)
-{
-    const int p = pos_b[j];
-    for (int jj = 0; jj < j; ++jj)
-        if (pos_b[jj] == p) return false;
-    return true;
-}
-
 template <int BM, int NCB, int NRW, int NPW, int NSMAX, int BK, int NPROD>
 __global__ void __launch_bounds__((NRW * NPW + NPROD) * 64)
 proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
@@ -99,6 +91,9 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lr = lane & 15, lg = lane >> 4;
 
+    // row bookkeeping: one load of Q_idx and pos_ids per row.  Ownership of
+    // the cache write (needed only by the epilogue) is settled by the
+    // consumer waves while the first stages stream in.
     for (int r = tid; r < BM; r += C::NT) {
         int m = m0 + r;
         const bool valid = m < M;
@@ -107,11 +102,17 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
         const int xr = a.prefill ? j : a.Q_idx[m];
         sXoff[r] = ((size_t)b * a.x_rows + xr) * a.d;
         sPos[r] = valid ? (a.prefill ? j : a.pos_ids[m]) : 0;
-        sDst[r] = !valid ? -1 : (a.prefill ? 1 : (owns_position(a.pos_ids + (size_t)b * a.rows_per_seq, j) ? 1 : 0));
+        sDst[r] = valid ? 1 : -1;
     }
     __syncthreads();
 
     const int nk = a.d / BK;
+    // Rows of X and W sit d_model elements apart, so one stage of every row
+    // falls in the same few L2 channels.  Each tile starts its d_model loop
+    // at its own stage (and wraps around), so the tiles that run together
+    // spread over the channels instead of all hitting the same ones.
+    const int krot = (2 * logical) % nk;
+    auto kstage = [&](int t) { const int u = t + krot; return u >= nk ? u - nk : u; };
     const bf16* X = (const bf16*)a.X;
     const bf16* W = (const bf16*)a.W;
 
@@ -126,24 +127,27 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
         // ================= producer waves =================
         const int pw = wave - C::NCW;
         const int srow = lane / C::CPR, slot = lane % C::CPR;
-        auto issue = [&](int t) {
-            unsigned char* st = smem + (t % C::NS) * C::STAGE;
-            const int k0 = t * BK;
+        // source row (with its swizzled chunk) of each of this wave's DMA
+        // blocks; a stage only adds its d_model offset
+        const bf16* rowp[C::DMAP];
 #pragma unroll
-            for (int ii = 0; ii < C::DMAP; ++ii) {
-                const int i = ii * NPROD + pw;                  // this wave's DMA blocks
-                const int row = C::RPD * i + srow;
-                const int chunk = slot ^ chunk_swz<BK>(row);
-                const bf16* src;
-                if (C::RPD * i < BM) {
-                    src = X + sXoff[row] + k0 + chunk * 8;
-                } else {
-                    const int wi = row - BM, blk = wi >> 4;
-                    const int cb = blk < C::PAIRS ? p0 + blk : p0 + 4 + (blk - C::PAIRS);
-                    src = W + ((size_t)(head * kDH + cb * 16 + (wi & 15))) * a.d + k0 + chunk * 8;
-                }
-                dma16(src, st + i * 1024);
+        for (int ii = 0; ii < C::DMAP; ++ii) {
+            const int i = ii * NPROD + pw;
+            const int row = C::RPD * i + srow;
+            const int chunk = slot ^ chunk_swz<BK>(row);
+            if (C::RPD * i < BM) {
+                rowp[ii] = X + sXoff[row] + chunk * 8;
+            } else {
+                const int wi = row - BM, blk = wi >> 4;
+                const int cb = blk < C::PAIRS ? p0 + blk : p0 + 4 + (blk - C::PAIRS);
+                rowp[ii] = W + ((size_t)(head * kDH + cb * 16 + (wi & 15))) * a.d + chunk * 8;
             }
+        }
+        auto issue = [&](int t) {
+            unsigned char* st = smem + (t % C::NS) * C::STAGE + pw * 1024;
+            const int k0 = kstage(t) * BK;
+#pragma unroll
+            for (int ii = 0; ii < C::DMAP; ++ii) dma16(rowp[ii] + k0, st + ii * NPROD * 1024);
         };
         int issued = 0;
         for (; issued < min(C::NS - 1, nk); ++issued) issue(issued);
@@ -153,6 +157,28 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
         }
     } else {
         // ================= consumer waves =================
+        if (!a.prefill && head >= a.H) {
+            // first-occurrence rule: a row owns the cache write of its
+            // position unless an earlier row of its sequence has the same one
+            for (int r = tid; r < BM; r += C::NCW * 64) {
+                const int m = m0 + r;
+                if (m >= M) continue;
+                const int b = m / a.rows_per_seq, j = m - b * a.rows_per_seq;
+                const int32_t* pb = a.pos_ids + (size_t)b * a.rows_per_seq;
+                const int p = sPos[r];
+                bool own = true;
+                int jj = 0;
+                for (; jj + 8 <= j; jj += 8) {
+                    int v[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) v[u] = pb[jj + u];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) own = own && v[u] != p;
+                }
+                for (; jj < j; ++jj) own = own && pb[jj] != p;
+                if (!own) sDst[r] = 0;
+            }
+        }
         for (int t = 0; t < nk; ++t) {
             ring_consumer_sync();
             const unsigned char* st = smem + (t % C::NS) * C::STAGE;
@@ -269,7 +295,7 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
     }
 }
 
-template <int BM, int NCB, int NRW, int NPW, int NSMAX, int BK = 128, int NPROD = 1>
+template <int BM, int NCB, int NRW, int NPW, int NSMAX, int BK, int NPROD>
 hipError_t launch_tile(const ProjArgs& a, hipStream_t s)
 {
     using C = ProjCfg<BM, NCB, NRW, NPW, NSMAX, BK, NPROD>;
@@ -289,46 +315,34 @@ hipError_t launch_tile(const ProjArgs& a, hipStream_t s)
 
 }  // namespace
 
-// Tile configurations: rows BM, 16-column blocks NCB, consumer waves split
-// as NRW (rows) x NPW (rotary block pairs), at most NSMAX ring stages.
+// Tile configurations (rows BM x 16-column blocks NCB): narrow tiles with a
+// 3-stage ring (two workgroups per CU) for a few rows, 64 x 64 tiles up to
+// 128 rows, and 128-column (one head) tiles beyond, as tall as needed to fit
+// every tile into a single round of the 256 CUs.  Measured on MI355X over the
+// layer workloads.
 struct ProjChoice { int bm, ncb; };
 static const ProjChoice kProjChoices[] = {
     {0, 0},
-    {16, 2}, {32, 2}, {48, 2}, {64, 2},      // 1-4: narrow tiles, one consumer wave, deep ring
-    {128, 8},                               // 5: 128 x 128, four consumer waves, two stages
-    {64, 4}, {64, 8}, {128, 4},             // 6-8
-    {48, 2}, {64, 2}, {16, 2},              // 9-11: narrow tiles with a 3-stage ring (2 workgroups per CU)
-    {32, 4}, {64, 4},                       // 12-13: 64-column tiles, 3-stage ring
-    {128, 8}, {128, 8}, {64, 4}, {128, 4}, {64, 8}, {48, 2}, {64, 4},   // 14-20: two producer waves
-    {16, 2}, {32, 2},                                                     // 21-22: two producers, 3 stages
+    {16, 2}, {32, 2}, {48, 2}, {64, 4},   // 1-4
+    {128, 8}, {176, 8}, {208, 8}, {96, 8},  // 5-8
 };
+constexpr int kNumChoices = (int)(sizeof(kProjChoices) / sizeof(kProjChoices[0]));
 
-int proj_mfma_block_m(int M)
+static int default_choice(int M, int heads)
 {
-    if (M <= 16) return 16;
-    if (M <= 32) return 32;
-    if (M <= 48) return 48;
-    if (M <= 128) return 64;
-    return 128;
+    if (M <= 16) return 1;
+    if (M <= 32) return 2;
+    if (M <= 48) return 3;
+    if (M <= 128) return 4;
+    for (int c : {5, 6, 7})
+        if ((long)((M + kProjChoices[c].bm - 1) / kProjChoices[c].bm) * heads <= 256) return c;
+    return 5;
 }
 
-// Defaults measured on MI355X (bench sweeps of the layer workloads): narrow
-// tiles with a 3-stage ring (two workgroups per CU) and two producer waves for
-// up to 48 rows; 64x64 tiles up to 128 rows; 128x128 tiles with 64-deep
-// stages (four in the ring) beyond.
-static int default_choice(int M)
+ProjTile proj_mfma_tile(int M, int heads, int choice)
 {
-    if (M <= 16) return 21;
-    if (M <= 32) return 22;
-    if (M <= 48) return 19;
-    if (M <= 128) return 16;
-    return 14;
-}
-
-int proj_mfma_columns_per_tile(int M, int choice)
-{
-    if (choice <= 0 || choice >= (int)(sizeof(kProjChoices) / sizeof(kProjChoices[0]))) choice = default_choice(M);
-    return 16 * kProjChoices[choice].ncb;
+    if (choice <= 0 || choice >= kNumChoices) choice = default_choice(M, heads);
+    return ProjTile{kProjChoices[choice].bm, 16 * kProjChoices[choice].ncb, choice};
 }
 
 hipError_t launch_proj_mfma(const ProjArgs& a, hipStream_t s)
@@ -336,31 +350,16 @@ hipError_t launch_proj_mfma(const ProjArgs& a, hipStream_t s)
     const int M = a.B * a.rows_per_seq;
     if (M == 0) return hipSuccess;
     if (a.d % 128 != 0) return hipErrorInvalidValue;
-    int choice = a.tile_choice;
-    if (choice <= 0 || choice >= (int)(sizeof(kProjChoices) / sizeof(kProjChoices[0]))) choice = default_choice(M);
-    switch (choice) {
-        case 1: return launch_tile<16, 2, 1, 1, 8>(a, s);
-        case 2: return launch_tile<32, 2, 1, 1, 8>(a, s);
-        case 3: return launch_tile<48, 2, 1, 1, 8>(a, s);
-        case 4: return launch_tile<64, 2, 1, 1, 8>(a, s);
-        case 5: return launch_tile<128, 8, 2, 2, 8>(a, s);
-        case 6: return launch_tile<64, 4, 2, 2, 8>(a, s);
-        case 7: return launch_tile<64, 8, 2, 2, 8>(a, s);
-        case 8: return launch_tile<128, 4, 2, 2, 8>(a, s);
-        case 9: return launch_tile<48, 2, 1, 1, 3>(a, s);
-        case 10: return launch_tile<64, 2, 1, 1, 3>(a, s);
-        case 11: return launch_tile<16, 2, 1, 1, 3>(a, s);
-        case 12: return launch_tile<32, 4, 1, 2, 3>(a, s);
-        case 13: return launch_tile<64, 4, 2, 2, 3>(a, s);
-        case 14: return launch_tile<128, 8, 2, 2, 8, 64, 2>(a, s);
-        case 15: return launch_tile<128, 8, 2, 2, 8, 128, 2>(a, s);
-        case 16: return launch_tile<64, 4, 2, 2, 8, 128, 2>(a, s);
-        case 17: return launch_tile<128, 4, 2, 2, 8, 64, 2>(a, s);
-        case 18: return launch_tile<64, 8, 2, 2, 8, 64, 2>(a, s);
-        case 19: return launch_tile<48, 2, 1, 1, 3, 128, 2>(a, s);
-        case 20: return launch_tile<64, 4, 2, 2, 3, 64, 2>(a, s);
-        case 21: return launch_tile<16, 2, 1, 1, 3, 128, 2>(a, s);
-        case 22: return launch_tile<32, 2, 1, 1, 3, 128, 2>(a, s);
+    const int heads = a.prefill ? 2 * a.Hkv : a.H + 2 * a.Hkv;
+    switch (proj_mfma_tile(M, heads, a.tile_choice).choice) {
+        case 1: return launch_tile<16, 2, 1, 1, 3, 128, 2>(a, s);
+        case 2: return launch_tile<32, 2, 1, 1, 3, 128, 2>(a, s);
+        case 3: return launch_tile<48, 2, 1, 1, 3, 128, 2>(a, s);
+        case 4: return launch_tile<64, 4, 2, 2, 8, 128, 2>(a, s);
+        case 5: return launch_tile<128, 8, 2, 2, 8, 64, 2>(a, s);
+        case 6: return launch_tile<176, 8, 1, 4, 8, 64, 2>(a, s);
+        case 7: return launch_tile<208, 8, 1, 4, 8, 64, 2>(a, s);
+        case 8: return launch_tile<96, 8, 1, 4, 8, 64, 2>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
