@@ -38,6 +38,27 @@ __device__ __forceinline__ void ring_producer_sync(int outstanding)
 #undef FDLLM_PSYNC
 }
 
+// Exact form for a ring whose stages each take DMAP of this wave's loads:
+// stage t has landed once at most `younger` * DMAP loads are in flight (loads
+// complete in order and the counter saturates at 63).  Y is the largest
+// number of younger stages the ring can hold.
+template <int N>
+__device__ __forceinline__ void ring_release()
+{
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+template <int DMAP, int Y>
+__device__ __forceinline__ void ring_producer_wait(int younger)
+{
+    if constexpr (Y <= 0) {
+        ring_release<0>();
+    } else {
+        if (younger >= Y) ring_release<(Y * DMAP > 63 ? 63 : Y * DMAP)>();
+        else ring_producer_wait<DMAP, Y - 1>(younger);
+    }
+}
+
 // Consumer side of the same barrier: its LDS reads of the previous stage have
 // returned, so the producer may overwrite that stage after the barrier.
 __device__ __forceinline__ void ring_consumer_sync()

@@ -29,7 +29,7 @@ namespace {
 
 constexpr int kDH = 128;          // head width
 
-// BK: d_model depth per stage (64 or 128, so a staged row is 128 or 256 B);
+// BK: d_model depth per stage (64 or 128: a staged row is 128 or 256 B);
 // NPROD producer waves split each stage's 1 KB DMA blocks, so up to NPROD x 63
 // blocks can be in flight per workgroup.
 template <int BM, int NCB, int NRW, int NPW, int NSMAX, int BK, int NPROD>
@@ -42,7 +42,7 @@ struct ProjCfg {
     static constexpr int CPR = BK / 8;                    // 16 B chunks per staged row
     static constexpr int ROWS = BM + BN;                  // staged rows per stage
     static constexpr int STAGE = ROWS * ROWB;
-    static constexpr int NS0 = (128 * 1024) / STAGE;
+    static constexpr int NS0 = (144 * 1024) / STAGE;      // the ring takes up to 144 KB of LDS
     static constexpr int NS = NS0 > NSMAX ? NSMAX : NS0;
     static constexpr int DMA = ROWS / RPD;                // 1 KB DMA blocks per stage
     static constexpr int DMAP = DMA / NPROD;              // per producer wave
@@ -50,9 +50,11 @@ struct ProjCfg {
     static constexpr int PAIRS = NCB / 2;                 // rotary block pairs per tile
     static constexpr int PPW = PAIRS / NPW;               // pairs per consumer wave
     static_assert(BK == 64 || BK == 128, "stage depth");
+    static_assert((NS - 2) * DMAP <= 63 || NS <= 2, "in-flight DMA blocks per producer");
     static_assert(BM % (16 * NRW) == 0 && PAIRS % NPW == 0 && NS >= 2, "tile shape");
     static_assert(DMA % NPROD == 0 && BM % RPD == 0, "DMA split");
     static_assert(BM * (BN + 4) * 4 <= NS * STAGE, "epilogue staging");
+    static_assert(BM * PAIRS * 16 * 8 <= NS * STAGE, "rotary table staging");
 };
 
 // Chunk swizzle of a staged row: 16 B chunk c of row r sits in slot c ^ f(r).
@@ -152,7 +154,7 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
         int issued = 0;
         for (; issued < min(C::NS - 1, nk); ++issued) issue(issued);
         for (int t = 0; t < nk; ++t) {
-            ring_producer_sync((issued - t - 1) * C::DMAP);
+            ring_producer_wait<C::DMAP, C::NS - 2>(issued - t - 1);
             if (issued < nk) issue(issued++);
         }
     } else {
@@ -207,24 +209,37 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
     __syncthreads();   // the ring is free: it stages the finished tile below
 
     // rotary on q and k heads: lane holds tile column blk*16 + lr of each block
-    // (head column cb*16 + lr) and rows 4*lg + i of each row block
+    // (head column cb*16 + lr) and rows 4*lg + i of each row block.  The
+    // table rows of the tile's positions (first-half columns of its pairs)
+    // are first staged in the free ring with all loads in flight at once.
     const bool consumer = wave < C::NCW;
     const bool rotate = head < a.H + a.Hkv;
-    if (consumer && rotate) {
-#pragma unroll
-        for (int q = 0; q < C::PPW; ++q) {
-            const int c = (p0 + wp * C::PPW + q) * 16 + lr;    // < 64: first half of the pair
-#pragma unroll
-            for (int r = 0; r < C::RBW; ++r)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = (wr * C::RBW + r) * 16 + lg * 4 + i;
-                    const float2 cs = a.rope[(size_t)sPos[row] * (kDH / 2) + c];
-                    const float y0 = acc[r][q][i], y1 = acc[r][q + C::PPW][i];
-                    acc[r][q][i] = y0 * cs.x - y1 * cs.y;
-                    acc[r][q + C::PPW][i] = y1 * cs.x + y0 * cs.y;
-                }
+    if (rotate) {
+        constexpr int PC = C::PAIRS * 16;                  // table columns of the tile
+        float2* sCS = (float2*)smem;                       // [BM][PC]
+        constexpr int V4 = PC / 2;                         // 16 B loads per row
+        for (int e = tid; e < BM * V4; e += C::NT) {
+            const int row = e / V4, v = e - row * V4;
+            *(f32x4*)&sCS[row * PC + 2 * v] =
+                *(const f32x4*)&a.rope[(size_t)sPos[row] * (kDH / 2) + p0 * 16 + 2 * v];
         }
+        __syncthreads();
+        if (consumer) {
+#pragma unroll
+            for (int q = 0; q < C::PPW; ++q) {
+                const int c = (wp * C::PPW + q) * 16 + lr;     // table column within the tile
+#pragma unroll
+                for (int r = 0; r < C::RBW; ++r)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float2 cs = sCS[((wr * C::RBW + r) * 16 + lg * 4 + i) * PC + c];
+                        const float y0 = acc[r][q][i], y1 = acc[r][q + C::PPW][i];
+                        acc[r][q][i] = y0 * cs.x - y1 * cs.y;
+                        acc[r][q + C::PPW][i] = y1 * cs.x + y0 * cs.y;
+                    }
+            }
+        }
+        __syncthreads();   // the staging below reuses the ring
     }
 
     // stage the tile: q rows stay fp32 (consumed on chip by the attention),
