@@ -42,8 +42,11 @@
  *     (old content), plus each new row j with vis_mask[b,i,j] != 0.  The old
  *     content at positions in pos_ids[b] is never attended.  An empty key set
  *     gives O = 0 and LSE = -inf.
- *   - Rounding: q, k, v are rounded once to the dtype after the rotation
- *     (nearest even); accumulation is fp32; O is rounded once at the end.
+ *   - Rounding: k and v are rounded once to the dtype after the rotation
+ *     (nearest even): they are what the cache stores.  q is built and
+ *     consumed on chip, so it keeps its fp32 accumulation and is never
+ *     rounded to the dtype.  Accumulation is fp32; O is rounded once at the
+ *     end; LSE stays fp32.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
  *     asynchronous on that stream and never synchronise, except that
  *     FDLLM_VALIDATE=1 in the environment makes fdllm_fused_step copy the
@@ -123,7 +126,7 @@ int fdllm_fused_step(fdllm_handle_t h, const void* X, int32_t x_rows, const int3
 /* The two launches of fdllm_fused_step, callable separately (same arguments
  * and statuses; used to time the phases or to run work between them).
  * fdllm_step_project runs gather + projection + rotary + k/v write and leaves
- * the step's rounded q rows and duplicate-position k/v rows in the handle's
+ * the step's fp32 q rows and duplicate-position k/v rows in the handle's
  * workspace; fdllm_step_attend consumes them (it must follow the project call
  * of the same step on the same stream, with the same nq and pos_ids). */
 int fdllm_step_project(fdllm_handle_t h, const void* X, int32_t x_rows, const int32_t* Q_idx,

@@ -24,7 +24,7 @@
  *   a7  under a visibility mask that stops the draft view and the [MASK] view
  *       of the verification pass from seeing each other.
  *
- * Readings where the pages are silent (each is listed in the design doc):
+ * Readings where the pages are silent:
  *   - X is addressed by row (Q_idx) and the rotary phase by position
  *     (pos_ids), so the two views can share a position but not a row.
  *   - rotary variant: rotate-half pairs (i, i + dh/2), theta_i =
