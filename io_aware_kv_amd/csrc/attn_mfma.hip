@@ -237,18 +237,24 @@ attn_mfma_kernel(AttnArgs a)
             for (int c = 0; c < kMaxChunks; ++c)
                 if (64 * c < nq) posr[c] = pos_b[min(64 * c + lane, nq - 1)];
         }
-        if (vis_b) {
+        // (without a mask the loads read a valid dummy byte; no branch or
+        // select around them, so nothing waits for them before the barrier)
+        const int8_t* vsrc = (const int8_t*)(vis_b ? vis_b : (const uint8_t*)pos_b);
+        const int vstep = vis_b ? 1 : 0;
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const int u = min(wave + C::NC * t, nunits - 1);
-                const int i = u / nch, col = min((u - i * nch) * 64 + lane, nq - 1);
-                vbyte[t] = vis_b[(size_t)i * nq + col];
-            }
+        for (int t = 0; t < 8; ++t) {
+            const int u = min(wave + C::NC * t, max(nunits - 1, 0));
+            const int i = u / nch, col = min((u - i * nch) * 64 + lane, nq - 1);
+            vbyte[t] = vsrc[(size_t)(i * nq + col) * vstep];
+        }
+        if (vis_b) {
             for (int k = tid; k < kps; k += C::NC * 64) sSlot[k] = -1;
             for (int t = tid; t < 2 * n_main; t += C::NC * 64) sMask[t] = 0u;
         }
     }
-    __syncthreads();
+    // a plain barrier: the LDS writes above must land, but the loads stay in
+    // flight (a full __syncthreads would wait for them before the stream starts)
+    consumer_sync();
 
     float m_run[RG], l_run[RG];
     f32x4 o[RG][8];
@@ -368,7 +374,7 @@ attn_mfma_kernel(AttnArgs a)
         int kofs[4], vofs[8];
 #pragma unroll
         for (int c = 0; c < 4; ++c) kofs[c] = (wk * C::KW + lr) * kRowB + (((c * 4 + lg) ^ lr) << 4);
-        const int rowA = wk * C::KW + 4 * lg + (lr >> 2);   // rowA + 16 has the same swizzle
+        const int rowA = wk * C::KW + 4 * lg + (lr >> 2);   // (rowA + 16 has the same swizzle)
 #pragma unroll
         for (int db = 0; db < 8; ++db) {
             const int chunk = 2 * db + ((lr & 3) >> 1);
@@ -390,35 +396,35 @@ attn_mfma_kernel(AttnArgs a)
                 const unsigned char* st = smem + s * C::STAGE;
 
                 // ---- S^T = K Q^T for this wave's 32 keys (rows past R run on zero q)
-                bf16x8 kf[2][4];
+                constexpr int KB = C::KW / 16;                 // 16-key blocks per wave
+                bf16x8 kf[KB][4];
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int c = 0; c < 4; ++c) kf[kb][c] = *(const bf16x8*)(st + kofs[c] + kb * 16 * kRowB);
-                f32x4 sc[RG][2];
+                // (the hi and lo passes alternate between the two key blocks'
+                // accumulators, so back-to-back MFMAs do not depend on each other)
+                f32x4 sc[RG][KB];
 #pragma unroll
-                for (int rg = 0; rg < RG; ++rg) {
-                    sc[rg][0] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    sc[rg][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-                // (hi and lo passes alternate between the accumulators so that
-                // back-to-back MFMAs do not depend on each other)
+                for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) sc[rg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
+                    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                         for (int rg = 0; rg < RG; ++rg)
                             sc[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][c], qh[rg][c], sc[rg][kb], 0, 0, 0);
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
+                    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                         for (int rg = 0; rg < RG; ++rg)
                             sc[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][c], ql[rg][c], sc[rg][kb], 0, 0, 0);
                 }
-                // all eight K fragment reads are issued before the first MFMA waits on one
-                __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-                __builtin_amdgcn_sched_group_barrier(0x008, 16 * RG, 0);
+                // all K fragment reads are issued before the first MFMA waits on one
+                __builtin_amdgcn_sched_group_barrier(0x100, 4 * KB, 0);
+                __builtin_amdgcn_sched_group_barrier(0x008, 8 * KB * RG, 0);
 
                 // ---- masks (lane: row lr, keys kb*16 + 4lg + i of the wave's 32).
                 // Under a visibility mask a tile holding positions written this
@@ -430,7 +436,7 @@ attn_mfma_kernel(AttnArgs a)
                 if (dup || tbase + C::TK > kend) {
                     const bool gate = vis_b != nullptr;
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
+                    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const int key = tbase + wk * C::KW + kb * 16 + lg * 4 + i;
@@ -446,6 +452,7 @@ attn_mfma_kernel(AttnArgs a)
                             }
                         }
                 } else if (vis_b) {
+                    // this wave's 32 bits of the tile's written-key mask
                     uint32_t wm = __builtin_amdgcn_readfirstlane(sMask[2 * it + wk]);
                     while (wm != 0u) {
                         const int k = __builtin_ctz(wm);          // key wk*32 + k of the tile
@@ -457,7 +464,7 @@ attn_mfma_kernel(AttnArgs a)
                             const bool hide = mine && (qrow[rg] < 0 ||
                                                        !((sVis[max(qrow[rg], 0) * VW + (j >> 5)] >> (j & 31)) & 1u));
 #pragma unroll
-                            for (int kb = 0; kb < 2; ++kb)
+                            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                                 for (int i = 0; i < 4; ++i)
                                     if (kb == (k >> 4) && i == (k & 3) && hide) sc[rg][kb][i] = -INFINITY;
@@ -470,11 +477,13 @@ attn_mfma_kernel(AttnArgs a)
                 // max exceeds it by more than 2^8, so p <= 256 and the
                 // accumulators are rescaled a few times per split.  The
                 // decision is per row; the block is skipped when no row grows.
-                bf16x8 pf[RG];
+                float pv[RG][KB][4];
 #pragma unroll
                 for (int rg = 0; rg < RG; ++rg) {
-                    float mx = fmaxf(fmaxf(fmaxf(sc[rg][0][0], sc[rg][0][1]), fmaxf(sc[rg][0][2], sc[rg][0][3])),
-                                     fmaxf(fmaxf(sc[rg][1][0], sc[rg][1][1]), fmaxf(sc[rg][1][2], sc[rg][1][3])));
+                    float mx = fmaxf(fmaxf(sc[rg][0][0], sc[rg][0][1]), fmaxf(sc[rg][0][2], sc[rg][0][3]));
+#pragma unroll
+                    for (int kb = 1; kb < KB; ++kb)
+                        mx = fmaxf(mx, fmaxf(fmaxf(sc[rg][kb][0], sc[rg][kb][1]), fmaxf(sc[rg][kb][2], sc[rg][kb][3])));
                     mx = max4(mx);
                     const bool grow = mx > m_run[rg] + 8.f;
                     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
@@ -488,17 +497,24 @@ attn_mfma_kernel(AttnArgs a)
                     }
                     float lsum = 0.f;
 #pragma unroll
-                    for (int kb = 0; kb < 2; ++kb)
+                    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            const float pv = __builtin_amdgcn_exp2f(sc[rg][kb][i] - m_run[rg]);   // exp2(-inf) = 0
-                            lsum += pv;
-                            pf[rg][kb * 4 + i] = (bf16)pv;
+                            pv[rg][kb][i] = __builtin_amdgcn_exp2f(sc[rg][kb][i] - m_run[rg]);   // exp2(-inf) = 0
+                            lsum += pv[rg][kb][i];
                         }
                     l_run[rg] += lsum;
                 }
 
                 // ---- O^T += V^T P^T over the wave's 32 keys
+                bf16x8 pf[RG];
+#pragma unroll
+                for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        pf[rg][i] = (bf16)pv[rg][0][i];
+                        pf[rg][4 + i] = (bf16)pv[rg][1][i];
+                    }
                 bf16x8 vf[8];
 #pragma unroll
                 for (int db = 0; db < 8; ++db) vf[db] = read_vt_frag(st + vofs[db], st + vofs[db] + 16 * kRowB);
