@@ -61,6 +61,8 @@ SHAPES = {
     3: LayerShape(B=8, N=2048, d_model=4096, H=32, Hkv=32, dh=128),
     4: LayerShape(B=4, N=8192, d_model=3584, H=28, Hkv=4, dh=128),
     5: LayerShape(B=64, N=2048, d_model=4096, H=32, Hkv=8, dh=128),
+    6: LayerShape(B=8, N=1024, d_model=4096, H=32, Hkv=32, dh=128),
+    7: LayerShape(B=8, N=1024, d_model=4096, H=32, Hkv=32, dh=128),
 }
 
 NAMES = {
@@ -69,13 +71,28 @@ NAMES = {
     3: "8B-class layer Flash-Verify pass B=8 N=2048 d=4096 H=Hkv=32 dh=128 |Q|=44",
     4: "long-context GQA layer B=4 N=8192 d=3584 H=28 Hkv=4 dh=128 |Q|=32",
     5: "large-batch GQA layer B=64 N=2048 d=4096 H=32 Hkv=8 dh=128 |Q|=16",
+    6: "default-window draft pass B=8 N=1024 d=4096 H=Hkv=32 dh=128 |Q|=144 (beta_t=80, beta_m=64)",
+    7: "default-window verification pass, chain mask, B=8 N=1024 d=4096 H=Hkv=32 dh=128 |Q|=176",
 }
 
 BASE_SEED = 20260
 
 
-def _randn(g, shape, std, dtype):
-    return (torch.randn(shape, generator=g, dtype=torch.float32) * std).to(dtype)
+# Hidden states and weights are normal draws rounded to a dyadic grid: X to
+# multiples of 1/8 (std 1), W to multiples of 1/512 (std w_std).  Every
+# product x*w is then a multiple of 2^-12 and every partial sum of a row's
+# projection (d_model <= 4096 terms, magnitude far below 2^11) fits in fp32's
+# 24-bit significand, so the projection is exact in fp32 in any summation
+# order.  The stored k/v rounding then depends on the rotary step alone.
+X_GRID = 2.0 ** -3
+W_GRID = 2.0 ** -9
+
+
+def _randn(g, shape, std, dtype, grid=None):
+    t = torch.randn(shape, generator=g, dtype=torch.float32) * std
+    if grid is not None:
+        t = torch.round(t / grid) * grid
+    return t.to(dtype)
 
 
 def _randint(g, lo, hi_incl):
@@ -87,8 +104,8 @@ def _perm(g, n):
 
 
 def hidden_and_weights(shape: LayerShape, x_rows: int, g: torch.Generator, w_std: float = 0.02):
-    X_pre = _randn(g, (shape.B, shape.N, shape.d_model), 1.0, shape.dtype)
-    W = _randn(g, (shape.cols, shape.d_model), w_std, shape.dtype)
+    X_pre = _randn(g, (shape.B, shape.N, shape.d_model), 1.0, shape.dtype, X_GRID)
+    W = _randn(g, (shape.cols, shape.d_model), w_std, shape.dtype, W_GRID)
     return X_pre, W
 
 
@@ -99,11 +116,11 @@ def step_hidden(shape: LayerShape, X_pre, Q_idx, x_rows, g):
     X = torch.empty((B, x_rows, d), dtype=shape.dtype)
     X[:, :N] = X_pre
     if x_rows > N:
-        X[:, N:] = _randn(g, (B, x_rows - N, d), 1.0, shape.dtype)
+        X[:, N:] = _randn(g, (B, x_rows - N, d), 1.0, shape.dtype, X_GRID)
     for b in range(B):
         rows = sorted(set(int(r) for r in Q_idx[b].tolist() if r < N))
         if rows:
-            X[b, rows] = _randn(g, (len(rows), d), 1.0, shape.dtype)
+            X[b, rows] = _randn(g, (len(rows), d), 1.0, shape.dtype, X_GRID)
     return X
 
 
@@ -122,8 +139,32 @@ def view_block_mask(groups: List[List[str]]) -> torch.Tensor:
     return vis
 
 
-def make_workload(cid: int, layer: int = 0, w_std: float = 0.02) -> Workload:
-    """The five layer configurations, seeded with 20260 + id (+1000 per layer)."""
+def view_chain_mask(groups: List[List[str]]) -> torch.Tensor:
+    """[B, nq, nq] uint8 chain-rule verification mask.  The k-th mask-view row
+    (views in ascending position order) sees the draft view of the earlier
+    exploratory positions and the mask view of its own and the later ones;
+    draft-view rows and the context rows (tracked, confident) see the context
+    and the whole draft view, never the mask view."""
+    B, nq = len(groups), len(groups[0])
+    vis = torch.zeros((B, nq, nq), dtype=torch.uint8)
+    for b in range(B):
+        gr = groups[b]
+        ctx = [i for i, t in enumerate(gr) if t in ("track", "confident")]
+        d_rows = [i for i, t in enumerate(gr) if t == "draft"]
+        m_rows = [i for i, t in enumerate(gr) if t == "mask"]
+        for i in ctx + d_rows:
+            for j in ctx + d_rows:
+                vis[b, i, j] = 1
+        for k, i in enumerate(m_rows):
+            for j in ctx + d_rows[:k] + m_rows[k:]:
+                vis[b, i, j] = 1
+    return vis
+
+
+def make_workload(cid: int, layer: int = 0, w_std: float = 0.02, n_confident: int = 32) -> Workload:
+    """The layer configurations, seeded with 20260 + id (+1000 per layer).
+    n_confident sets how many of the 64 window positions the verification
+    pass (7) takes as confident; the rest are exploratory."""
     shape = SHAPES[cid]
     seed = BASE_SEED + cid + 1000 * layer
     g = torch.Generator().manual_seed(seed)
@@ -180,11 +221,45 @@ def make_workload(cid: int, layer: int = 0, w_std: float = 0.02) -> Workload:
         Q = torch.tensor([list(range(L, L + nq)) for L in Ls], dtype=torch.int32)
         P = Q.clone()
         meta["decoded_prefix"] = Ls
+    elif cid in (6, 7):
+        # the pages' default window: beta_t = 80 tracked decoded positions and
+        # the first beta_m = 64 masked positions after a decoded prefix
+        n_t, n_m = 80, 64
+        Qs, Ps, groups = [], [], []
+        if not 0 <= n_confident <= n_m:
+            raise ValueError("n_confident must be in [0, %d]" % n_m)
+        n_d = n_confident if cid == 7 else 0
+        n_s = n_m - n_d
+        for b in range(B):
+            L = _randint(g, N // 2 + n_t, N - n_m)
+            tv = sorted(_perm(g, L)[:n_t])
+            front = list(range(L, L + n_m))
+            if cid == 6:
+                Qs.append(tv + front)
+                Ps.append(tv + front)
+                groups.append(["track"] * n_t + ["mask"] * n_m)
+            else:
+                order = _perm(g, n_m)
+                Dset = sorted(front[i] for i in order[:n_d])
+                Sset = sorted(front[i] for i in order[n_d:])
+                Qs.append(tv + Dset + Sset + [N + k for k in range(n_s)])
+                Ps.append(tv + Dset + Sset + Sset)
+                groups.append(["track"] * n_t + ["confident"] * n_d + ["draft"] * n_s + ["mask"] * n_s)
+            meta.setdefault("decoded_prefix", []).append(L)
+        nq = len(Qs[0])
+        x_rows = N + (n_s if cid == 7 else 0)
+        Q = torch.tensor(Qs, dtype=torch.int32)
+        P = torch.tensor(Ps, dtype=torch.int32)
+        if cid == 7:
+            vis = view_chain_mask(groups)
+        meta["groups"] = groups
     else:
         raise ValueError("unknown configuration %r" % cid)
     X_pre, W = hidden_and_weights(shape, x_rows, g, w_std)
     X = step_hidden(shape, X_pre, Q, x_rows, g)
-    return Workload(NAMES[cid], shape, nq, x_rows, seed, X_pre, X, W, Q.contiguous(),
+    meta["w_std"] = w_std
+    name = NAMES[cid] if cid != 7 else NAMES[cid].replace("|Q|=176", "|Q|=%d" % nq)
+    return Workload(name, shape, nq, x_rows, seed, X_pre, X, W, Q.contiguous(),
                     P.contiguous(), vis, meta)
 
 
@@ -229,4 +304,23 @@ def make_random_case(shape: LayerShape, nq: int, seed: int, *, n_extra_rows: int
     X_pre, W = hidden_and_weights(shape, x_rows, g, w_std)
     X = step_hidden(shape, X_pre, Q, x_rows, g)
     return Workload("random", shape, nq, x_rows, seed, X_pre, X, W, Q.contiguous(),
-                    P.contiguous(), vis, {})
+                    P.contiguous(), vis, {"w_std": w_std})
+
+
+CACHE_SEED_OFFSET = 7_000_003
+
+
+def initial_cache(wl: Workload):
+    """Seeded cache content before the step: Kc, Vc [B, Hkv, N, dh] in the
+    storage dtype, drawn i.i.d. normal with the spread of a projected k/v
+    element (w_std * sqrt(d_model) for unit-variance hidden states).  The step
+    only reads the rows it does not overwrite, so any seeded content serves;
+    both the GPU run and the oracle start from these tensors."""
+    key = "_initial_cache"
+    if key not in wl.meta:
+        ls = wl.shape
+        g = torch.Generator().manual_seed(wl.seed + CACHE_SEED_OFFSET)
+        std = wl.meta.get("w_std", 0.02) * float(ls.d_model) ** 0.5
+        shape = (ls.B, ls.Hkv, ls.N, ls.dh)
+        wl.meta[key] = (_randn(g, shape, std, ls.dtype), _randn(g, shape, std, ls.dtype))
+    return wl.meta[key]

@@ -90,6 +90,31 @@ def view_visibility(rows) -> List[List[int]]:
     return vis
 
 
+def chain_visibility(rows) -> List[List[int]]:
+    """Chain-rule visibility over the rows of ``verify_rows`` (jaehun.me review,
+    "Flash-Verify": the verification mask is causal so that the mask view
+    scores the block's true joint, Appx. C).  Reading: the mask-view row of
+    the k-th exploratory position in decoding (ascending position) order sees
+    the draft view of the positions before it and the mask view of itself and
+    the positions after it; draft-view and context rows see the context and
+    the draft view only.  1 = row i may see row j."""
+    n = len(rows)
+    s_pos = sorted({p for g, p in rows if g == "draft"})
+    rank = {p: k for k, p in enumerate(s_pos)}
+    vis = [[0] * n for _ in range(n)]
+    for i, (gi, pi) in enumerate(rows):
+        for j, (gj, pj) in enumerate(rows):
+            if gi != "mask":
+                vis[i][j] = 0 if gj == "mask" else 1
+            elif gj == "draft":
+                vis[i][j] = 1 if rank[pj] < rank[pi] else 0
+            elif gj == "mask":
+                vis[i][j] = 1 if rank[pj] >= rank[pi] else 0
+            else:
+                vis[i][j] = 1
+    return vis
+
+
 def accept(S_order: Sequence[int], x_hat: Dict[int, int], x_tilde: Dict[int, int],
            c_tilde: Dict[int, float], gamma: float) -> List[int]:
     """Sequential acceptance: walk S_t in decoding order and accept position i

@@ -1,8 +1,9 @@
 """GPU parity of the fused KV-cache step (HIP path through the C ABI) against
-the fp64 oracle, on seeded inputs: the five layer workloads at full size in
+the fp64 oracle, on seeded inputs: the layer workloads at full size in
 the launch configuration the bench times, small cases that span several
 tiles with ragged tails, duplicates and masks, forced split counts, the
-scalar kernel family, determinism, the views' mutual invisibility, edge
+scalar kernel family, determinism, the views' mutual invisibility and the
+chain-rule mask's dependencies, the largest verification window, edge
 positions and empty key sets."""
 import zlib
 
@@ -16,13 +17,52 @@ from parity_util import compare, log, run_gpu, run_oracle
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4])
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 6, 7])
 def test_layer_workload_full_size(cid):
     log("case: workload %d full size" % cid)
     wl = make_workload(cid)
     g = run_gpu(wl)
-    r = run_oracle(wl, g["K0"], g["V0"])
+    r = run_oracle(wl)
     compare(wl, g, r, "workload%d" % cid)
+
+
+def test_verification_window_all_exploratory():
+    """The largest verification query set of the default window: no confident
+    position, 64 exploratory positions in both views (nq = 208)."""
+    log("case: workload 7, all exploratory")
+    wl = make_workload(7, n_confident=0)
+    assert wl.nq == 208
+    g = run_gpu(wl)
+    compare(wl, g, run_oracle(wl), "workload7-all-exploratory")
+
+
+def test_chain_mask_dependencies_on_gpu():
+    """Under the chain-rule mask the draft row of the last exploratory position
+    is seen by no mask-view row, and the mask row of the first is seen by no
+    other row: perturbing either leaves every other row's O and LSE
+    bit-identical."""
+    log("case: chain mask dependencies")
+    wl = make_workload(7)
+    groups = wl.meta["groups"]
+    base = run_gpu(wl)
+    for view, pick in (("draft", -1), ("mask", 0)):
+        X2 = wl.X.clone()
+        moved = []
+        for b in range(wl.shape.B):
+            rows = [i for i, t in enumerate(groups[b]) if t == view]
+            i = rows[pick]
+            moved.append(i)
+            r = int(wl.Q_idx[b, i])
+            X2[b, r] = (X2[b, r].float() + 2.0).to(X2.dtype)
+        pert = run_gpu(wl, X=X2)
+        for b in range(wl.shape.B):
+            if view == "draft":
+                same = [i for i, t in enumerate(groups[b]) if t == "mask"]
+            else:
+                same = [i for i in range(wl.nq) if i != moved[b]]
+            assert torch.equal(pert["O"][b, same].view(torch.int16), base["O"][b, same].view(torch.int16))
+            assert torch.equal(pert["LSE"][b, same].view(torch.int32), base["LSE"][b, same].view(torch.int32))
+            assert not torch.equal(pert["O"][b, moved[b]], base["O"][b, moved[b]])
 
 
 @pytest.mark.parametrize("layer", [0, 31])
@@ -30,7 +70,7 @@ def test_large_batch_stack_layers(layer):
     log("case: workload 5 layer %d" % layer)
     wl = make_workload(5, layer=layer)
     g = run_gpu(wl)
-    r = run_oracle(wl, g["K0"], g["V0"])
+    r = run_oracle(wl)
     compare(wl, g, r, "workload5-layer%d" % layer)
 
 
@@ -55,7 +95,7 @@ def test_small_cases(label, shape, nq, kw):
     ls = LayerShape(**shape)
     wl = make_random_case(ls, nq, seed=zlib.crc32(label.encode()) % 10000, w_std=0.05, **kw)
     g = run_gpu(wl)
-    r = run_oracle(wl, g["K0"], g["V0"])
+    r = run_oracle(wl)
     compare(wl, g, r, label)
 
 
@@ -67,7 +107,7 @@ def test_forced_splits(splits, nq):
     wl = make_random_case(ls, nq, seed=77, n_extra_rows=3, dup_frac=0.2, masked_vis=True, w_std=0.05)
     g = run_gpu(wl, tuning={"attn_splits": splits})
     assert g["plan"]["attn_splits"] == splits and g["plan"]["gemm_splitk"] == 1
-    r = run_oracle(wl, g["K0"], g["V0"])
+    r = run_oracle(wl)
     compare(wl, g, r, "splits%d-nq%d" % (splits, nq))
 
 
@@ -77,7 +117,7 @@ def test_generic_family_on_bf16():
     wl = make_random_case(ls, 10, seed=5, n_extra_rows=3, dup_frac=0.3, masked_vis=True, w_std=0.05)
     g = run_gpu(wl, tuning={"kernel_family": 2})
     assert g["plan"]["kernel_family"] == 2
-    r = run_oracle(wl, g["K0"], g["V0"])
+    r = run_oracle(wl)
     compare(wl, g, r, "generic-bf16")
 
 
@@ -86,7 +126,7 @@ def test_q_max_larger_than_nq_and_edge_positions():
     ls = LayerShape(B=2, N=160, d_model=128, H=2, Hkv=2, dh=128)
     wl = make_random_case(ls, 4, seed=6, positions=[[0, 159, 1, 158], [159, 0, 80, 81]], w_std=0.05)
     g = run_gpu(wl, q_max=40)
-    r = run_oracle(wl, g["K0"], g["V0"])
+    r = run_oracle(wl)
     compare(wl, g, r, "edges")
 
 
@@ -129,7 +169,7 @@ def test_empty_key_set_gives_zero_and_minus_inf():
     wl.vis = torch.zeros((1, 3, 3), dtype=torch.uint8)
     wl.vis[0, 1, 1] = 1
     g = run_gpu(wl)
-    r = run_oracle(wl, g["K0"], g["V0"])
+    r = run_oracle(wl)
     assert torch.all(g["O"][0, [0, 2]].float() == 0)
     assert torch.all(torch.isneginf(g["LSE"][0, [0, 2]]))
     compare(wl, g, r, "empty-keys")
@@ -137,16 +177,16 @@ def test_empty_key_set_gives_zero_and_minus_inf():
 
 def test_prefill_matches_oracle():
     import oracle
-    from parity_util import rel_err, shape_of, round_mode
+    from parity_util import rel_err, run_prefill, shape_of, round_mode
     log("case: prefill")
     for ls in (LayerShape(B=1, N=64, d_model=128, H=4, Hkv=4, dh=32, dtype=torch.float32),
                LayerShape(B=2, N=200, d_model=256, H=4, Hkv=2, dh=128)):
         wl = make_random_case(ls, 1, seed=9, w_std=0.05)
-        g = run_gpu(wl)
+        Kg, Vg = run_prefill(wl)
         Kr, Vr = oracle.prefill(shape_of(ls), wl.X_pre, wl.W, round_mode(ls.dtype))
         tol = 1e-4 if ls.dtype == torch.float32 else 2e-2
-        assert rel_err(g["K0"].double().numpy(), Kr) <= tol
-        assert rel_err(g["V0"].double().numpy(), Vr) <= tol
+        assert rel_err(Kg.double().numpy(), Kr) <= tol
+        assert rel_err(Vg.double().numpy(), Vr) <= tol
 
 
 def test_status_codes_on_gpu():

@@ -1,0 +1,68 @@
+"""The seeded input recipe: hidden states and weights sit on their dyadic
+grids after the cast to the storage dtype, and the projection's partial sums
+stay inside fp32's exact range, so that the stored rows' rounding is decided
+by the rotary step alone; the tie test of the parity helpers behaves as its
+derivation says."""
+import sys
+import os
+
+import numpy as np
+import pytest
+import torch
+
+sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+from io_aware_kv_amd.workloads import (LayerShape, W_GRID, X_GRID, initial_cache, make_random_case,
+                                       make_workload)
+
+
+def _on_grid(t, grid):
+    a = t.double() / grid
+    return bool(torch.equal(a, torch.round(a)))
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7])
+def test_workload_inputs_on_grid_and_exact_in_fp32(cid):
+    wl = make_workload(cid)
+    assert _on_grid(wl.X, X_GRID) and _on_grid(wl.W, W_GRID)
+    # every partial sum of a query row's projection is a multiple of
+    # X_GRID * W_GRID = 2^-12 bounded by sum |x||w|; exact in fp32 while that
+    # bound stays below 2^(24 - 12)
+    Wa = wl.W.double().abs()
+    for b in range(wl.shape.B):
+        rows = wl.X[b, wl.Q_idx[b].long()].double().abs()
+        bound = (rows @ Wa.T).max().item()
+        assert bound < 2.0 ** 12, bound
+    assert X_GRID * W_GRID == 2.0 ** -12
+
+
+def test_initial_cache_is_seeded_and_shaped():
+    ls = LayerShape(B=2, N=40, d_model=64, H=4, Hkv=2, dh=32)
+    a = make_random_case(ls, 3, seed=4)
+    b = make_random_case(ls, 3, seed=4)
+    Ka, Va = initial_cache(a)
+    Kb, Vb = initial_cache(b)
+    assert Ka.shape == (2, 2, 40, 32) and Ka.dtype == ls.dtype
+    assert torch.equal(Ka, Kb) and torch.equal(Va, Vb) and not torch.equal(Ka, Va)
+    assert initial_cache(a)[0] is Ka
+
+
+def test_rounding_range_brackets_ties_only():
+    from parity_util import k_rounding_range, rounding_ties, storage_unit
+    u = 2.0 ** -7                      # bf16 spacing in [1, 2)
+    mid = 1.0 + 3 * u + u / 2          # a rounding boundary
+    # pairs (x_i, x_{i+half}) with half = 2
+    k = np.array([[mid, 1.0 + 3 * u, 0.0, 0.0],
+                  [mid + 1e-4, mid - 1e-12, 0.5, 0.25],
+                  [1e-9, 1.0, 1.0, 1.0],
+                  [0.0, 0.0, 0.0, 0.0]])
+    t = rounding_ties(k, torch.bfloat16)
+    assert t[0, 0] and not t[0, 1]     # exactly on the boundary / on a value
+    assert not t[1, 0] and t[1, 1]     # 1e-4 away is decided; 1e-12 away is not
+    assert t[0, 2] and t[0, 3]         # a zero paired with a large element is not decided
+    assert not t[3].any()              # zeros in zero pairs are
+    lo, hi = k_rounding_range(k, torch.bfloat16)
+    assert lo[0, 0] == 1.0 + 3 * u and hi[0, 0] == 1.0 + 4 * u
+    # a tiny element paired with a large one: its range spans zero
+    assert lo[2, 0] < 0 < hi[2, 0] and not t[2, 2]
+    assert storage_unit(np.array([1.5, 0.75, 3.0]), torch.bfloat16).tolist() == [u, u / 2, 2 * u]
+    assert storage_unit(np.array([1.5]), torch.float32)[0] == 2.0 ** -23
