@@ -328,25 +328,71 @@ attn_mfma_kernel(AttnArgs a)
             if (lane == 0) sMisc[0] = ndup;
         }
         // visibility rows as bit words: chunk c of row i fills words 2c, 2c+1
+        if (nunits <= 8 * C::NC) {
+            // (the bytes were loaded before the stream started)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int u = wave + C::NC * t;
-            if (u < nunits) {
-                const int i = u / nch, c = u - i * nch;
-                const uint64_t m = __builtin_amdgcn_ballot_w64(vbyte[t] != 0 && c * 64 + lane < nq);
-                if (lane == 0) {
-                    sVis[i * VW + 2 * c] = (uint32_t)m;
-                    if (2 * c + 1 < VW) sVis[i * VW + 2 * c + 1] = (uint32_t)(m >> 32);
+            for (int t = 0; t < 8; ++t) {
+                const int u = wave + C::NC * t;
+                if (u < nunits) {
+                    const int i = u / nch, c = u - i * nch;
+                    const uint64_t m = __builtin_amdgcn_ballot_w64(vbyte[t] != 0 && c * 64 + lane < nq);
+                    if (lane == 0) {
+                        sVis[i * VW + 2 * c] = (uint32_t)m;
+                        if (2 * c + 1 < VW) sVis[i * VW + 2 * c + 1] = (uint32_t)(m >> 32);
+                    }
                 }
             }
-        }
-        for (int u = wave + C::NC * 8; u < nunits; u += C::NC) {
-            const int i = u / nch, c = u - i * nch, col = c * 64 + lane;
-            const int v = col < nq ? vis_b[(size_t)i * nq + col] : 0;
-            const uint64_t m = __builtin_amdgcn_ballot_w64(v != 0);
-            if (lane == 0) {
-                sVis[i * VW + 2 * c] = (uint32_t)m;
-                if (2 * c + 1 < VW) sVis[i * VW + 2 * c + 1] = (uint32_t)(m >> 32);
+        } else {
+            // a large mask: each thread packs whole 32-column words, with the
+            // loads of four words in flight at once (addresses are clamped
+            // into the matrix and the bytes past the row end dropped)
+            const int nwords = nq * VW;
+            const size_t last = (size_t)nq * nq - 1;
+            for (int w0 = tid; w0 < nwords; w0 += C::NC * 64 * 4) {
+                uint32_t dw[4][8];
+                int cols[4];
+                if ((nq & 15) == 0) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int w = min(w0 + k * C::NC * 64, nwords - 1);
+                        const int i = w / VW, c32 = w - i * VW;
+                        cols[k] = min(32, nq - 32 * c32);
+                        const uint8_t* row = vis_b + (size_t)i * nq;
+                        const u32x4 lo = *(const u32x4*)(row + 32 * c32);
+                        const u32x4 hi = *(const u32x4*)(row + (cols[k] > 16 ? 32 * c32 + 16 : 32 * c32));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { dw[k][e] = lo[e]; dw[k][4 + e] = hi[e]; }
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        const int w = min(w0 + k * C::NC * 64, nwords - 1);
+                        const int i = w / VW, c32 = w - i * VW;
+                        cols[k] = min(32, nq - 32 * c32);
+                        const size_t b0 = (size_t)i * nq + 32 * c32;
+#pragma unroll
+                        for (int d = 0; d < 8; ++d) {
+                            uint32_t x = 0;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                x |= (uint32_t)vis_b[min(b0 + 4 * d + e, last)] << (8 * e);
+                            dw[k][d] = x;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const int w = w0 + k * C::NC * 64;
+                    if (w >= nwords) continue;
+                    uint32_t bits = 0u;
+#pragma unroll
+                    for (int d = 0; d < 8; ++d)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            bits |= (((dw[k][d] >> (8 * e)) & 0xffu) != 0u ? 1u : 0u) << (4 * d + e);
+                    if (cols[k] < 32) bits &= (1u << cols[k]) - 1u;
+                    sVis[w] = bits;
+                }
             }
         }
 

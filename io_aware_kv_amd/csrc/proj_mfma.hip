@@ -110,10 +110,12 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
 
     const int nk = a.d / BK;
     // Rows of X and W sit d_model elements apart, so one stage of every row
-    // falls in the same few L2 channels.  Each tile starts its d_model loop
-    // at its own stage (and wraps around), so the tiles that run together
-    // spread over the channels instead of all hitting the same ones.
-    const int krot = (2 * logical) % nk;
+    // falls in the same few L2 channels.  The d_model loop of a tile starts
+    // at its own stage and wraps around: tiles on one XCD (which share X rows
+    // and W rows through its L2) start within 8 stages of each other, so the
+    // shared data is still in the L2 when the later ones read it, while the
+    // XCDs start an eighth of the loop apart.
+    const int krot = ((blockIdx.x & 7) * (nk / 8) + (logical & 7)) % nk;
     auto kstage = [&](int t) { const int u = t + krot; return u >= nk ? u - nk : u; };
     const bf16* X = (const bf16*)a.X;
     const bf16* W = (const bf16*)a.W;

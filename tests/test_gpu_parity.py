@@ -83,6 +83,10 @@ SMALL = [
      dict(n_extra_rows=4, dup_frac=0.4)),
     ("many-rows", dict(B=1, N=257, d_model=256, H=16, Hkv=2, dh=128), 20, dict(masked_vis=True)),
     ("single-row", dict(B=2, N=70, d_model=128, H=2, Hkv=1, dh=128), 1, dict()),
+    ("large-mask-ragged", dict(B=2, N=700, d_model=256, H=4, Hkv=4, dh=128), 150,
+     dict(n_extra_rows=10, dup_frac=0.05, masked_vis=True)),
+    ("large-mask-aligned", dict(B=1, N=500, d_model=256, H=2, Hkv=2, dh=128), 208,
+     dict(n_extra_rows=16, dup_frac=0.05, masked_vis=True)),
     ("fp32-generic", dict(B=2, N=50, d_model=64, H=4, Hkv=2, dh=32, dtype=torch.float32), 7,
      dict(n_extra_rows=2, dup_frac=0.3, masked_vis=True)),
     ("fp32-dh64", dict(B=1, N=90, d_model=96, H=2, Hkv=2, dh=64, dtype=torch.float32), 5, dict()),
@@ -109,6 +113,18 @@ def test_forced_splits(splits, nq):
     assert g["plan"]["attn_splits"] == splits and g["plan"]["gemm_splitk"] == 1
     r = run_oracle(wl)
     compare(wl, g, r, "splits%d-nq%d" % (splits, nq))
+
+
+@pytest.mark.parametrize("choice", list(range(1, 9)))
+def test_forced_projection_tiles(choice, monkeypatch):
+    """Every projection tile configuration (FDLLM_PROJ_TILE) on a case with
+    ragged row tiles, GQA, duplicates and a mask."""
+    log("case: projection tile %d" % choice)
+    monkeypatch.setenv("FDLLM_PROJ_TILE", str(choice))
+    ls = LayerShape(B=3, N=400, d_model=512, H=4, Hkv=2, dh=128)
+    wl = make_random_case(ls, 70, seed=31, n_extra_rows=8, dup_frac=0.1, masked_vis=True, w_std=0.05)
+    g = run_gpu(wl)
+    compare(wl, g, run_oracle(wl), "proj-tile%d" % choice)
 
 
 def test_generic_family_on_bf16():
