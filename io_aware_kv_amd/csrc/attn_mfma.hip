@@ -479,27 +479,50 @@ attn_mfma_kernel(AttnArgs a)
                 const bool dup = it >= n_main;
                 const int tbase = dup ? (it - n_main) * C::TK : k0 + it * C::TK;
                 const int kend = dup ? ndup : k1;
-                if (dup || tbase + C::TK > kend) {
-                    const bool gate = vis_b != nullptr;
+                // this wave's 32 bits of the tile's written-key mask; with
+                // more than a few written keys the per-lane general path is
+                // cheaper than visiting them one at a time
+                uint32_t wm = vis_b && !dup ? __builtin_amdgcn_readfirstlane(sMask[2 * it + wk]) : 0u;
+                if (dup || tbase + C::TK > kend || __builtin_popcount(wm) > 2) {
+                    // branch-free: every lane reads its keys' owners and its
+                    // rows' visibility words at clamped (valid) indices
+                    if (vis_b != nullptr) {
+                        int jk[KB][4];
 #pragma unroll
-                    for (int kb = 0; kb < KB; ++kb)
+                        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int key = tbase + wk * C::KW + kb * 16 + lg * 4 + i;
-                            const bool in = key < kend;
-                            int j = -1;
-                            if (gate && in) j = dup ? sDup[key] : sSlot[key - k0];
-#pragma unroll
-                            for (int rg = 0; rg < RG; ++rg) {
-                                bool keep = in;
-                                if (j >= 0)
-                                    keep = keep && qrow[rg] >= 0 && ((sVis[qrow[rg] * VW + (j >> 5)] >> (j & 31)) & 1u);
-                                if (!keep) sc[rg][kb][i] = -INFINITY;
+                            for (int i = 0; i < 4; ++i) {
+                                const int key = tbase + wk * C::KW + kb * 16 + lg * 4 + i;
+                                const int kk = min(key, kend - 1);
+                                const int j = dup ? sDup[kk] : (int)sSlot[kk - k0];
+                                jk[kb][i] = key < kend ? j : -2;      // -2: past the end
                             }
-                        }
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int j = jk[kb][i];
+                                const int jc = max(j, 0);
+#pragma unroll
+                                for (int rg = 0; rg < RG; ++rg) {
+                                    const uint32_t w = sVis[max(qrow[rg], 0) * VW + (jc >> 5)];
+                                    const bool seen = qrow[rg] >= 0 && ((w >> (jc & 31)) & 1u);
+                                    const bool keep = j == -1 || (j >= 0 && seen);
+                                    sc[rg][kb][i] = keep ? sc[rg][kb][i] : -INFINITY;
+                                }
+                            }
+                    } else {
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int key = tbase + wk * C::KW + kb * 16 + lg * 4 + i;
+#pragma unroll
+                                for (int rg = 0; rg < RG; ++rg)
+                                    sc[rg][kb][i] = key < kend ? sc[rg][kb][i] : -INFINITY;
+                            }
+                    }
                 } else if (vis_b) {
-                    // this wave's 32 bits of the tile's written-key mask
-                    uint32_t wm = __builtin_amdgcn_readfirstlane(sMask[2 * it + wk]);
                     while (wm != 0u) {
                         const int k = __builtin_ctz(wm);          // key wk*32 + k of the tile
                         wm &= wm - 1u;
