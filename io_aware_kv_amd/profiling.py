@@ -95,6 +95,9 @@ def write_workload_summary(workload: str, title: str, trace_dir: str, trace_cmd:
     for r in rows:
         lines.append("| `%s` | %d | %.2f | %.2f | %.2f |" % (short_name(r["name"]), r["calls"], r["avg_us"],
                                                               r["min_us"], r["max_us"]))
+    if any(r["name"].startswith("__amd_rocclr") for r in rows):
+        lines += ["", "`__amd_rocclr_*` are the runtime's own copy and fill kernels that load the seeded "
+                      "inputs and caches into the buffer sets, outside the timed steps."]
     lines += ["", "HBM traffic per launch from two counter passes (`FETCH_SIZE`, then `WRITE_SIZE`, KiB per "
               "dispatch), each scaled by what the same counter reads for a plain 1 GiB device copy "
               "(fetch x%.4f, write x%.4f):" % (cal["fetch_factor"], cal["write_factor"]), "",
