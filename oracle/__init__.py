@@ -56,6 +56,8 @@ def bind(path: str):
     lib.fdllm_oracle_step.restype = ctypes.c_int
     lib.fdllm_oracle_prefill.argtypes = [P, P, i32, P, P, P]
     lib.fdllm_oracle_prefill.restype = ctypes.c_int
+    lib.fdllm_oracle_key_scores.argtypes = [P, P, P, P, P, i32, P, P, P]
+    lib.fdllm_oracle_key_scores.restype = ctypes.c_int
     lib.fdllm_oracle_threads.argtypes = []
     lib.fdllm_oracle_threads.restype = ctypes.c_int
     return lib
@@ -190,3 +192,48 @@ def prefill(shape: Shape, X, W, round_mode: int):
     if rc != 0:
         raise ValueError("oracle prefill failed: %d" % rc)
     return Kc, Vc
+
+
+def _u8(a):
+    try:
+        import torch
+        if isinstance(a, torch.Tensor):
+            return np.ascontiguousarray(a.detach().to("cpu", torch.uint8).numpy())
+    except ImportError:  # pragma: no cover
+        pass
+    return np.ascontiguousarray(np.asarray(a, dtype=np.uint8))
+
+
+def key_scores(shape: Shape, q, Kc, LSE, pos_ids, vis, sel):
+    """Tracked-set scores a_p [B, N]: attention mass of the selected query rows
+    on each cache position (see fdllm_oracle.c).  q is the step's unrounded q,
+    Kc the cache after the step, LSE the step's."""
+    q, Kc, LSE = _f64(q), _f64(Kc), _f64(LSE)
+    Pi = _i32(pos_ids)
+    B, nq = Pi.shape
+    sel_a = _u8(sel)
+    vis_a = None if vis is None else _u8(vis)
+    out = np.empty((B, shape.N))
+    c = _cfg(shape, ROUND_EXACT)
+    rc = _load().fdllm_oracle_key_scores(ctypes.byref(c), _ptr(q), _ptr(Kc), _ptr(LSE), _ptr(Pi), nq,
+                                         _ptr(vis_a), _ptr(sel_a), _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle key scores failed: %d" % rc)
+    return out
+
+
+def select_top(scores, cand, k: int):
+    """Top-k candidate positions per sequence by score, highest first; equal
+    scores go to the lower position; -1 fills the rows with fewer than k
+    candidates.  The comparison is made on the scores as given (the caller
+    passes the precision the ranking is decided in)."""
+    sc = np.asarray(scores)
+    cd = np.asarray(cand).astype(bool)
+    B, N = sc.shape
+    out = np.full((B, k), -1, dtype=np.int32)
+    for b in range(B):
+        idx = [p for p in range(N) if cd[b, p]]
+        idx.sort(key=lambda p: (-sc[b, p], p))
+        for t, p in enumerate(idx[:k]):
+            out[b, t] = p
+    return out

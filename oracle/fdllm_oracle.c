@@ -43,6 +43,16 @@
  *     step (old content) plus every new row j with vis[b,i,j] != 0
  *     (vis == NULL means all visible).  An empty key set gives O = 0 and
  *     LSE = -inf.
+ *
+ * Tracked-set scores (the same review, "How It Works", Step 1: Cache
+ * selection, and the paragraph on Fig. 1b): the previously decoded tokens
+ * most attended by the masked query rows are kept.  Reading: the score of
+ * cache position p is the attention mass the selected query rows put on it in
+ * this layer, summed over their query heads,
+ *     a_p = sum_{i selected} sum_h exp(q_i,h . k_p / sqrt(dh) - LSE_i,h),
+ * over the keys row i may see (the visibility rule above, the key at p being
+ * the cache row after the step's write); rows that do not own their position
+ * are not cache positions and get no score.
  */
 #include <math.h>
 #include <omp.h>
@@ -293,5 +303,49 @@ int fdllm_oracle_prefill(const fdllm_oracle_cfg_t* cfg, const double* X, int32_t
                     memcpy(Vc + dst, v + src, sizeof(double) * dh);
                 }
     free(idx); free(q); free(k); free(v);
+    return err;
+}
+
+/* Tracked-set scores: a_p for every cache position p of every sequence.
+ * q [B,nq,H,dh] (the step's unrounded q), Kc [B,Hkv,N,dh] after the step's
+ * write, LSE [B,nq,H] of the step, sel [B,nq] (1: the row contributes),
+ * vis [B,nq,nq] or NULL.  scores [B,N]. */
+int fdllm_oracle_key_scores(const fdllm_oracle_cfg_t* cfg, const double* q, const double* Kc,
+                            const double* LSE, const int32_t* pos_ids, int32_t nq, const uint8_t* vis,
+                            const uint8_t* sel, double* scores)
+{
+    if (check_cfg(cfg) || !q || !Kc || !LSE || !pos_ids || !sel || !scores || nq < 0) return ORC_ERR_ARG;
+    const int B = cfg->B, N = cfg->N, H = cfg->H, Hkv = cfg->Hkv, dh = cfg->dh;
+    const double scale = 1.0 / sqrt((double)dh);
+    int err = ORC_OK;
+#pragma omp parallel for schedule(dynamic)
+    for (int b = 0; b < B; ++b) {
+        const int32_t* pb = pos_ids + (int64_t)b * nq;
+        int* owner = (int*)malloc(sizeof(int) * (size_t)N);
+        if (!owner) { err = ORC_ERR_ALLOC; continue; }
+        for (int p = 0; p < N; ++p) owner[p] = -1;
+        for (int j = 0; j < nq; ++j)
+            if (owner[pb[j]] < 0) owner[pb[j]] = j;
+        for (int p = 0; p < N; ++p) {
+            double a = 0.0;
+            for (int i = 0; i < nq; ++i) {
+                if (!sel[(int64_t)b * nq + i]) continue;
+                const int j = owner[p];
+                if (j >= 0 && vis && !vis[((int64_t)b * nq + i) * nq + j]) continue;
+                for (int h = 0; h < H; ++h) {
+                    const double lse = LSE[((int64_t)b * nq + i) * H + h];
+                    if (isinf(lse)) continue;
+                    const int g = (int)(((int64_t)h * Hkv) / H);
+                    const double* qi = q + (((int64_t)b * nq + i) * H + h) * dh;
+                    const double* kp = Kc + (((int64_t)b * Hkv + g) * N + p) * dh;
+                    double s = 0.0;
+                    for (int e = 0; e < dh; ++e) s += qi[e] * kp[e];
+                    a += exp(s * scale - lse);
+                }
+            }
+            scores[(int64_t)b * N + p] = a;
+        }
+        free(owner);
+    }
     return err;
 }

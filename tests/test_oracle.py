@@ -396,3 +396,97 @@ def test_tiny_fp32_layer_end_to_end_against_library_composition():
     O, L = _attn_reference(ls, q, k, v, wl.pos_ids, None, Kc, Vc)
     np.testing.assert_allclose(r["O"], O, atol=1e-11)
     np.testing.assert_allclose(r["LSE"], L, atol=1e-11)
+
+
+# --------------------------------------------------------------------------
+# tracked-set scores (next step after the path): attention mass per position
+# --------------------------------------------------------------------------
+
+def _mass_reference(ls, q, k, P, vis, sel, Kc_old):
+    """Per cache position, the summed softmax probability that the selected
+    rows give it, from torch.softmax over each row's explicit key set (old
+    positions not written this step, then the new rows j visible to i); a new
+    row counts toward its position only if it is the first row there."""
+    B, nq = P.shape
+    H, Hkv, dh, N = ls.H, ls.Hkv, ls.dh, ls.N
+    out = np.zeros((B, N))
+    for b in range(B):
+        pos = [int(p) for p in P[b].tolist()]
+        written = set(pos)
+        keep = [p for p in range(N) if p not in written]
+        first = [pos.index(pos[j]) == j for j in range(nq)]
+        for h in range(H):
+            g = h * Hkv // H
+            keys = torch.from_numpy(np.concatenate([Kc_old[b, g, keep], k[b, :, g]], axis=0))
+            for i in range(nq):
+                if not sel[b, i]:
+                    continue
+                s = keys @ torch.from_numpy(np.ascontiguousarray(q[b, i, h])) / math.sqrt(dh)
+                m = torch.ones(len(keep) + nq, dtype=torch.bool)
+                if vis is not None:
+                    m[len(keep):] = torch.from_numpy(vis[b, i].numpy().astype(bool))
+                if not m.any():
+                    continue
+                pr = torch.softmax(s.masked_fill(~m, float("-inf")), dim=0).numpy()
+                out[b, keep] += pr[:len(keep)]
+                for j in range(nq):
+                    if first[j]:
+                        out[b, pos[j]] += pr[len(keep) + j]
+    return out
+
+
+@pytest.mark.parametrize("dup,masked", [(0.0, False), (0.3, True), (0.3, False), (0.0, True)])
+def test_key_scores_match_softmax_columns(dup, masked):
+    ls = LayerShape(B=2, N=40, d_model=20, H=6, Hkv=2, dh=8, dtype=torch.float32)
+    wl = make_random_case(ls, nq=10, seed=21 + int(dup * 10) + masked, n_extra_rows=4,
+                          dup_frac=dup, masked_vis=masked, w_std=0.5)
+    sh = _shape(ls)
+    g = np.random.default_rng(22)
+    Kc = g.standard_normal((ls.B, ls.Hkv, ls.N, ls.dh))
+    Vc = g.standard_normal((ls.B, ls.Hkv, ls.N, ls.dh))
+    r = oracle.step(sh, wl.X, wl.Q_idx, wl.pos_ids, wl.vis, wl.W, Kc, Vc, ROUND_EXACT)
+    sel = (g.random((ls.B, 10)) < 0.6).astype(np.uint8)
+    a = oracle.key_scores(sh, r["q"], r["Kc"], r["LSE"], wl.pos_ids, wl.vis, sel)
+    q, k, _ = _proj_reference(ls, wl.X, wl.Q_idx, wl.pos_ids, wl.W)
+    ref = _mass_reference(ls, q, k, wl.pos_ids, wl.vis, sel, Kc)
+    np.testing.assert_allclose(a, ref, atol=1e-11, rtol=0)
+
+
+def test_key_scores_closed_forms():
+    """All rows selected, distinct positions, no mask: every row-head
+    distribution sums to one over the cache, so the scores sum to nq * H.
+    A mask hiding every new row leaves the written positions at zero."""
+    ls = LayerShape(B=2, N=30, d_model=16, H=4, Hkv=2, dh=8, dtype=torch.float32)
+    wl = make_random_case(ls, nq=6, seed=23, w_std=0.5)
+    sh = _shape(ls)
+    g = np.random.default_rng(24)
+    Kc = g.standard_normal((ls.B, ls.Hkv, ls.N, ls.dh))
+    Vc = g.standard_normal((ls.B, ls.Hkv, ls.N, ls.dh))
+    r = oracle.step(sh, wl.X, wl.Q_idx, wl.pos_ids, None, wl.W, Kc, Vc, ROUND_EXACT)
+    sel = np.ones((ls.B, 6), dtype=np.uint8)
+    a = oracle.key_scores(sh, r["q"], r["Kc"], r["LSE"], wl.pos_ids, None, sel)
+    np.testing.assert_allclose(a.sum(axis=1), 6 * ls.H, rtol=1e-12)
+    assert (a > 0).all()
+    hide = torch.zeros((ls.B, 6, 6), dtype=torch.uint8)
+    r2 = oracle.step(sh, wl.X, wl.Q_idx, wl.pos_ids, hide, wl.W, Kc, Vc, ROUND_EXACT)
+    a2 = oracle.key_scores(sh, r2["q"], r2["Kc"], r2["LSE"], wl.pos_ids, hide, sel)
+    for b in range(ls.B):
+        written = wl.pos_ids[b].numpy()
+        assert np.all(a2[b, written] == 0.0)
+        np.testing.assert_allclose(a2[b].sum(), 6 * ls.H, rtol=1e-12)
+    # one selected row: its scores are its own softmax, summed over heads
+    sel1 = np.zeros_like(sel)
+    sel1[0, 2] = 1
+    a1 = oracle.key_scores(sh, r["q"], r["Kc"], r["LSE"], wl.pos_ids, None, sel1)
+    assert np.all(a1[1] == 0.0)
+    np.testing.assert_allclose(a1[0].sum(), ls.H, rtol=1e-12)
+
+
+def test_select_top_by_hand():
+    sc = np.array([[0.5, 0.9, 0.9, 0.1, 0.7],
+                   [0.0, 0.0, 0.3, 0.0, 0.0]], dtype=np.float32)
+    cand = np.array([[1, 1, 1, 1, 1], [1, 1, 0, 1, 0]], dtype=np.uint8)
+    assert oracle.select_top(sc, cand, 3).tolist() == [[1, 2, 4], [0, 1, 3]]
+    cand2 = np.array([[1, 0, 1, 0, 0], [0, 0, 0, 0, 0]], dtype=np.uint8)
+    assert oracle.select_top(sc, cand2, 3).tolist() == [[2, 0, -1], [-1, -1, -1]]
+    assert oracle.select_top(sc, cand, 0).shape == (2, 0)

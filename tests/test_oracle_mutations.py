@@ -29,6 +29,11 @@ MUTATIONS = {
     "last_occurrence_wins": ("if (pos_b[jj] == pos_b[j]) return 0;", "if (0) return 0;"),
     "bf16_truncates": ("double r = ldexp(nearbyint(ldexp(x, -q)), q);", "double r = ldexp(trunc(ldexp(x, -q)), q);"),
     "lse_log2": ("*lse = m + log(l);", "*lse = m + log2(l);"),
+    "scores_without_lse": ("a += exp(s * scale - lse);", "a += exp(s * scale);"),
+    "scores_last_owner": ("if (owner[pb[j]] < 0) owner[pb[j]] = j;", "owner[pb[j]] = j;"),
+    "scores_vis_transposed": ("if (j >= 0 && vis && !vis[((int64_t)b * nq + i) * nq + j]) continue;",
+                              "if (j >= 0 && vis && !vis[((int64_t)b * nq + j) * nq + i]) continue;"),
+    "scores_unselected_rows": ("if (!sel[(int64_t)b * nq + i]) continue;", "if (0) continue;"),
 }
 
 PIN_TESTS = os.path.join(os.path.dirname(os.path.abspath(__file__)), "test_oracle.py")
