@@ -134,6 +134,54 @@ def cpu_oracle_baseline(wl, K0, V0, budget_s):
     return r, sum(times) / len(times), len(times), oracle.threads()
 
 
+def time_selection(fk, wl, sets, stream, iters):
+    """Time the tracked-set scores and the top-k selection that follow the
+    step (beta_t = 80), over the rotating buffer sets; the handle's q staging
+    holds the last step's q, and every set carries the same step inputs."""
+    import torch
+    from io_aware_kv_amd.workloads import selection_inputs
+    ls = wl.shape
+    dev = torch.device("cuda")
+    sel, cand = selection_inputs(wl)
+    sel_d, cand_d = sel.to(dev), cand.to(dev)
+    k = 80
+    n = len(sets)
+    scores = [torch.empty((ls.B, ls.N), dtype=torch.float32, device=dev) for _ in range(n)]
+    outs = [torch.empty((ls.B, k), dtype=torch.int32, device=dev) for _ in range(n)]
+
+    def run(i, evs=None):
+        st = sets[i % n]
+        if evs is not None:
+            evs[0].record(stream)
+        fk.tracked_scores(st["P"], st["vis"], sel_d, st["Kc"], st["LSE"], scores[i % n], stream=stream)
+        if evs is not None:
+            evs[1].record(stream)
+        fk.select_tracked(scores[i % n], cand_d, k, outs[i % n], stream=stream)
+        if evs is not None:
+            evs[2].record(stream)
+
+    for i in range(3):
+        run(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(iters)]
+    for i in range(iters):
+        run(i, evs[i])
+    torch.cuda.synchronize()
+    sc_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / iters
+    tk_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / iters
+    elt = 2 if ls.dtype == torch.bfloat16 else 4
+    G = ls.H // ls.Hkv
+    nsel = int(sel.sum())
+    # algorithmic bytes: the cache's K once, the selected rows' q and LSE,
+    # the positions, mask and selection flags, the scores written
+    nbytes = (ls.B * ls.Hkv * ls.N * ls.dh * elt + nsel * ls.H * ls.dh * 4 + nsel * ls.H * 4
+              + ls.B * wl.nq * 5 + (ls.B * wl.nq * wl.nq if wl.vis is not None else 0) + ls.B * ls.N * 4)
+    gbps = nbytes / (sc_ms * 1e-3) / 1e9
+    return {"k": k, "rows_selected": nsel, "scores_us": round(sc_ms * 1e3, 3), "select_us": round(tk_ms * 1e3, 3),
+            "scores_algorithmic_bytes": nbytes, "scores_GBps": round(gbps, 1),
+            "scores_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +190,7 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--sets", type=int, default=0, help="buffer sets in rotation (0: auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-select", action="store_true", help="skip timing the tracked-set selection")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--attn-splits", type=int, default=0)
     ap.add_argument("--gemm-splitk", type=int, default=0)
@@ -238,6 +287,12 @@ def main():
     torch.cuda.synchronize()
     warm_ms = ws.elapsed_time(we) / warm_iters
 
+    # the step after the path: tracked-set scores and top-k (not part of value)
+    selection = None
+    if not args.no_select:
+        selection = time_selection(fk, wl, sets, stream, min(args.steps, 50))
+        log("bench: tracked-set scores %.2f us, top-k %.2f us" % (selection["scores_us"], selection["select_us"]))
+
     # dominant kernel roofline
     dom = "attn" if attn_avg >= proj_avg else "proj"
     dom_ms = attn_avg if dom == "attn" else proj_avg
@@ -297,6 +352,7 @@ def main():
             "attn_hbm_frac": round(ab["attn"] / (attn_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         },
         "algorithmic_bytes_per_step": ab["total"],
+        "tracked_set_selection": selection,
         "roofline": roofline,
         "cpu_baseline": None,
     }

@@ -135,6 +135,39 @@ int fdllm_step_project(fdllm_handle_t h, const void* X, int32_t x_rows, const in
 int fdllm_step_attend(fdllm_handle_t h, const int32_t* pos_ids, int32_t nq, const uint8_t* vis_mask,
                       const void* Kc, const void* Vc, void* O, float* LSE, void* stream);
 
+/* Tracked-set scores, the step after the fused step (jaehun.me review, "How
+ * It Works: A Concrete Example", Step 1: Cache selection, with the paragraph
+ * on Fig. 1b): the previously decoded tokens most attended by the masked
+ * query rows are kept for the next step.  For every cache position p of
+ * every sequence b,
+ *     scores[b, p] = sum over rows i with sel_rows[b, i] != 0, over the
+ *                    query heads h:  exp(q_i,h . k_p / sqrt(dh) - LSE[b, i, h])
+ * with the step's q (fp32), the cache row k_p after the step's write, and the
+ * step's key-set rule: a position written this step counts for row i only if
+ * vis_mask[b, i, owner] != 0 (owner = the first row at that position; NULL =
+ * all visible); rows that do not own their position are no cache position
+ * and get no score; rows with an empty key set (LSE = -inf) add nothing.
+ * It must follow the fused step (or its project call) of the same nq on the
+ * same stream: it reads the step's q from the handle's workspace.
+ * sel_rows [B, nq] uint8, vis_mask [B, nq, nq] or NULL, Kc [B, Hkv, N, dh] in
+ * the cache dtype, LSE [B, nq, H] fp32 from the step, scores [B, N] fp32 out;
+ * all device pointers owned by the caller, 16-byte aligned (sel, vis, LSE:
+ * 4-byte).  Each kv head's partial sums are added in head order, so repeated
+ * calls give identical bits.  Statuses: ARG, SHAPE, ALIGN, UNSUPPORTED (a
+ * split of N does not fit in LDS), HIP. */
+int fdllm_tracked_scores(fdllm_handle_t h, const int32_t* pos_ids, int32_t nq, const uint8_t* vis_mask,
+                         const uint8_t* sel_rows, const void* Kc, const float* LSE, float* scores,
+                         void* stream);
+
+/* Top-k selection of the next tracked set: for every sequence b, out[b, :k]
+ * receives the k candidate positions (cand[b, p] != 0) with the highest
+ * scores[b, p], highest first; equal scores rank the lower position first;
+ * -1 fills the places past the number of candidates.  scores [B, N] fp32,
+ * cand [B, N] uint8, out [B, k] int32, device pointers owned by the caller.
+ * 0 <= k; N <= 16384.  Statuses: ARG, UNSUPPORTED (N > 16384), HIP. */
+int fdllm_select_tracked(fdllm_handle_t h, const float* scores, const uint8_t* cand, int32_t k,
+                         int32_t* out, void* stream);
+
 /* Set (tuning != NULL) or reset (NULL) the launch-shape overrides of h.
  * Statuses: ARG. */
 int fdllm_set_tuning(fdllm_handle_t h, const fdllm_tuning_t* tuning);

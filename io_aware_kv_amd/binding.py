@@ -64,13 +64,15 @@ def load():
     lib.fdllm_fused_step.argtypes = [P, P, i32, P, P, i32, P, P, P, P, P, P, P]
     lib.fdllm_step_project.argtypes = [P, P, i32, P, P, i32, P, P, P, P]
     lib.fdllm_step_attend.argtypes = [P, P, i32, P, P, P, P, P, P]
+    lib.fdllm_tracked_scores.argtypes = [P, P, i32, P, P, P, P, P, P]
+    lib.fdllm_select_tracked.argtypes = [P, P, P, i32, P, P]
     lib.fdllm_set_tuning.argtypes = [P, ctypes.POINTER(Tuning)]
     lib.fdllm_get_plan.argtypes = [P, i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.fdllm_cache_destroy.argtypes = [P]
     lib.fdllm_status_str.argtypes = [ctypes.c_int]
     lib.fdllm_status_str.restype = ctypes.c_char_p
     for name in ("fdllm_validate_config", "fdllm_cache_init", "fdllm_prefill", "fdllm_fused_step",
-                 "fdllm_step_project", "fdllm_step_attend",
+                 "fdllm_step_project", "fdllm_step_attend", "fdllm_tracked_scores", "fdllm_select_tracked",
                  "fdllm_set_tuning", "fdllm_get_plan", "fdllm_cache_destroy"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -187,6 +189,29 @@ class FusedKVCache:
         rc = load().fdllm_step_attend(self._h, _ptr(pos_ids), nq, _ptr(vis), _ptr(Kc), _ptr(Vc), _ptr(O),
                                       _ptr(LSE), _stream(stream))
         _check(rc, "fdllm_step_attend")
+
+    def tracked_scores(self, pos_ids, vis, sel, Kc, LSE, scores, stream=None):
+        """Attention mass of the selected rows (sel [B, nq] uint8) on every
+        cache position, after the step of the same nq: scores [B, N] fp32."""
+        c = self.cfg
+        nq = pos_ids.shape[1]
+        if sel.dtype != torch.uint8 or tuple(sel.shape) != (c.B, nq):
+            raise ValueError("sel must be uint8 [B, nq]")
+        if scores.dtype != torch.float32 or tuple(scores.shape) != (c.B, c.N):
+            raise ValueError("scores must be fp32 [B, N]")
+        rc = load().fdllm_tracked_scores(self._h, _ptr(pos_ids), nq, _ptr(vis), _ptr(sel), _ptr(Kc), _ptr(LSE),
+                                         _ptr(scores), _stream(stream))
+        _check(rc, "fdllm_tracked_scores")
+
+    def select_tracked(self, scores, cand, k, out, stream=None):
+        """Top-k candidate positions by score per sequence into out [B, k] int32."""
+        c = self.cfg
+        if cand.dtype != torch.uint8 or tuple(cand.shape) != (c.B, c.N):
+            raise ValueError("cand must be uint8 [B, N]")
+        if out.dtype != torch.int32 or tuple(out.shape) != (c.B, k):
+            raise ValueError("out must be int32 [B, k]")
+        rc = load().fdllm_select_tracked(self._h, _ptr(scores), _ptr(cand), k, _ptr(out), _stream(stream))
+        _check(rc, "fdllm_select_tracked")
 
     def set_tuning(self, attn_splits=0, gemm_splitk=0, kernel_family=0):
         t = Tuning(attn_splits, gemm_splitk, kernel_family)

@@ -31,6 +31,7 @@ struct fdllm_ctx {
     float* aml = nullptr;
     size_t apart_rows = 0;        // (B*Hkv) * splits * Rpad rows available
     uint32_t* aticket = nullptr;
+    float* mpart = nullptr;       // [B * Hkv, N] per kv head sums of the tracked-set scores
     fdllm_tuning_t tune{0, 0, 0};
 };
 
@@ -105,11 +106,13 @@ int hip_status(hipError_t e)
 
 void free_ws(fdllm_ctx* h)
 {
-    void* ptrs[] = {h->rope, h->qbuf, h->sideK, h->sideV, h->gpart, h->gticket, h->apart, h->aml, h->aticket};
+    void* ptrs[] = {h->rope, h->qbuf, h->sideK, h->sideV, h->gpart, h->gticket, h->apart, h->aml, h->aticket,
+                    h->mpart};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     h->rope = nullptr; h->qbuf = nullptr; h->sideK = h->sideV = nullptr;
     h->gpart = nullptr; h->gticket = nullptr; h->apart = h->aml = nullptr; h->aticket = nullptr;
+    h->mpart = nullptr;
 }
 
 // Size the split buffers for every nq the handle may see.
@@ -246,7 +249,8 @@ int fdllm_cache_init(fdllm_handle_t* out, const fdllm_config_t* cfg, const void*
               hipMalloc(&h->qbuf, qrows * c.dh * sizeof(float)) == hipSuccess &&
               hipMalloc(&h->sideK, srows * c.dh * h->elt) == hipSuccess &&
               hipMalloc(&h->sideV, srows * c.dh * h->elt) == hipSuccess &&
-              hipMalloc(&h->aticket, (size_t)c.B * c.Hkv * sizeof(uint32_t)) == hipSuccess;
+              hipMalloc(&h->aticket, (size_t)c.B * c.Hkv * sizeof(uint32_t)) == hipSuccess &&
+              hipMalloc(&h->mpart, (size_t)c.B * c.Hkv * c.N * sizeof(float)) == hipSuccess;
     if (!ok) { free_ws(h); delete h; return FDLLM_ERR_ALLOC; }
     if (hipMemset(h->aticket, 0, (size_t)c.B * c.Hkv * sizeof(uint32_t)) != hipSuccess) {
         free_ws(h); delete h; return FDLLM_ERR_HIP;
@@ -365,6 +369,62 @@ int fdllm_fused_step(fdllm_handle_t h, const void* X, int32_t x_rows, const int3
     int st = fdllm_step_project(h, X, x_rows, Q_idx, pos_ids, nq, W, Kc, Vc, stream);
     if (st) return st;
     return fdllm_step_attend(h, pos_ids, nq, vis, Kc, Vc, O, LSE, stream);
+}
+
+int fdllm_tracked_scores(fdllm_handle_t h, const int32_t* pos_ids, int32_t nq, const uint8_t* vis,
+                         const uint8_t* sel, const void* Kc, const float* LSE, float* scores, void* stream)
+{
+    if (!h) return FDLLM_ERR_ARG;
+    const fdllm_config_t& c = h->cfg;
+    if (nq < 0 || nq > c.q_max) return FDLLM_ERR_SHAPE;
+    if (!pos_ids || !sel || !Kc || !LSE || !scores) return FDLLM_ERR_ARG;
+    if (!aligned16(Kc) || (reinterpret_cast<uintptr_t>(LSE) & 3u) || (reinterpret_cast<uintptr_t>(scores) & 3u) ||
+        (reinterpret_cast<uintptr_t>(pos_ids) & 3u))
+        return FDLLM_ERR_ALIGN;
+    int st = set_device(h);
+    if (st) return st;
+    MassArgs a{};
+    a.qbuf = h->qbuf; a.Kc = Kc; a.pos_ids = pos_ids; a.vis = vis; a.sel = sel; a.LSE = LSE;
+    a.part = h->mpart; a.scores = scores;
+    a.B = c.B; a.N = c.N; a.H = c.H; a.Hkv = c.Hkv; a.dh = c.dh; a.G = h->G; a.nq = nq; a.q_max = c.q_max;
+    a.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.dh));
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e;
+    if (nq == 0) {
+        // no query row: every score is zero (the scalar form runs no row loop)
+        a.splits = 1; a.keys_per_split = c.N;
+        e = launch_key_mass_generic(a, c.dtype, s);
+        return hip_status(e);
+    }
+    if (c.dtype == FDLLM_BF16 && c.dh == 128) {
+        // (sequence, kv head) pairs x key splits: about one round of 256 CUs,
+        // each split a multiple of 16 keys whose owner table fits in LDS
+        const int bgs = c.B * c.Hkv;
+        int sp = std::max(1, (256 + bgs - 1) / bgs);
+        int kps = ((c.N + sp - 1) / sp + 15) / 16 * 16;
+        while (key_mass_lds_bytes(nq, kps) > 150 * 1024 && kps > 16) kps = (kps / 2 + 15) / 16 * 16;
+        if (key_mass_lds_bytes(nq, kps) > 150 * 1024) return FDLLM_ERR_UNSUPPORTED;
+        a.keys_per_split = kps;
+        a.splits = (c.N + kps - 1) / kps;
+        e = launch_key_mass(a, s);
+    } else {
+        a.splits = 1; a.keys_per_split = c.N;
+        e = launch_key_mass_generic(a, c.dtype, s);
+    }
+    return hip_status(e);
+}
+
+int fdllm_select_tracked(fdllm_handle_t h, const float* scores, const uint8_t* cand, int32_t k, int32_t* out,
+                         void* stream)
+{
+    if (!h) return FDLLM_ERR_ARG;
+    if (k < 0) return FDLLM_ERR_ARG;
+    if (k == 0) return FDLLM_OK;
+    if (!scores || !cand || !out) return FDLLM_ERR_ARG;
+    if (h->cfg.N > 16384) return FDLLM_ERR_UNSUPPORTED;
+    int st = set_device(h);
+    if (st) return st;
+    return hip_status(launch_select_top(scores, cand, h->cfg.B, h->cfg.N, k, out, (hipStream_t)stream));
 }
 
 int fdllm_cache_destroy(fdllm_handle_t h)

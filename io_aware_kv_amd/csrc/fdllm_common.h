@@ -58,6 +58,27 @@ struct AttnArgs {
     float scale_log2;       // log2(e) / sqrt(dh)
 };
 
+// Tracked-set scores after a step: attention mass of the selected query rows
+// on every cache position.
+struct MassArgs {
+    const float* qbuf;      // the step's q staging buffer
+    const void* Kc;         // [B, Hkv, N, dh] after the step
+    const int32_t* pos_ids; // [B, nq]
+    const uint8_t* vis;     // [B, nq, nq] or NULL
+    const uint8_t* sel;     // [B, nq] 1: the row contributes
+    const float* LSE;       // [B, nq, H] of the step
+    float* part;            // [B * Hkv, N] per kv head sums
+    float* scores;          // [B, N]
+    int B, N, H, Hkv, dh, G, nq, q_max;
+    int splits, keys_per_split;
+    float scale_log2;       // log2(e) / sqrt(dh)
+};
+hipError_t launch_key_mass(const MassArgs& a, hipStream_t s);
+hipError_t launch_key_mass_generic(const MassArgs& a, int dtype, hipStream_t s);
+size_t key_mass_lds_bytes(int nq, int keys_per_split);
+hipError_t launch_select_top(const float* scores, const uint8_t* cand, int B, int N, int k, int32_t* out,
+                             hipStream_t s);
+
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_proj_generic(const ProjArgs& a, int dtype, hipStream_t s);
 hipError_t launch_attn_generic(const AttnArgs& a, int dtype, hipStream_t s);

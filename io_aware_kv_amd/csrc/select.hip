@@ -1,0 +1,331 @@
+// select.hip -- tracked-set scores and top-k selection after the fused step
+// (gfx950, head width 128).
+//
+// Flash-dLLM keeps, as the tracked set of the next step, the previously
+// decoded tokens that the masked query rows attend to most (jaehun.me review,
+// "How It Works: A Concrete Example", Step 1: Cache selection, and the
+// paragraph on Fig. 1b: middle layers concentrate their attention on a few
+// tokens).  The score of cache position p is the attention mass that the
+// selected query rows put on it in this layer, summed over their query heads:
+//     a_p = sum_{i selected} sum_h 2^(s2_{i,h,p} - L2_{i,h}),
+// with s2 the step's score in log2 units and L2 the step's LSE in log2 units,
+// over the keys row i may see (positions written this step are the owner
+// row's key, gated by the visibility mask).
+//
+//  * key_mass_kernel: one workgroup per (sequence, kv head, key split).  The
+//    selected rows' q (fp32 in the step's staging buffer, as bf16 hi + lo
+//    parts) are the MFMA A operand, 16-key blocks of K loaded straight into B
+//    fragments (16 B per lane) the B operand, so a lane ends with 4 query
+//    rows of one key: the per-key sum is four in-lane adds and two row-swap
+//    permutes.  Each kv head's partial sums go to a workspace row.
+//  * key_mass_sum_kernel: a_p = sum over kv heads in head order (a fixed
+//    order, so repeated runs agree bit for bit).
+//  * select_top_kernel: one workgroup per sequence sorts 64-bit keys
+//    (order-preserving score bits, then the inverted position so equal
+//    scores rank the lower position first) with a bitonic network in LDS and
+//    keeps the first k candidates.
+#include "fdllm_common.h"
+
+namespace fdllm {
+
+namespace {
+
+constexpr int kDH = 128;
+constexpr int kMassWaves = 4;
+constexpr int kMassRowBlocks = 4;     // row blocks of 16 held in registers at a time
+
+__device__ __forceinline__ float sum4x(float x)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    const auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
+// LDS layout (dynamic): sSel[nq] int, sOwner[kps] int, sVis[nq * VW] u32
+__global__ void __launch_bounds__(kMassWaves * 64) key_mass_kernel(MassArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __shared__ int sNsel;
+    const int nq = a.nq, G = a.G;
+    const int VW = (nq + 31) >> 5;
+    int* sSel = (int*)smem;
+    int* sOwner = sSel + nq;
+    uint32_t* sVis = (uint32_t*)(sOwner + a.keys_per_split);
+
+    const int split = blockIdx.x % a.splits;
+    const int bg = blockIdx.x / a.splits;
+    const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+    const int k0 = split * a.keys_per_split;
+    const int k1 = min(a.N, k0 + a.keys_per_split);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int32_t* pos_b = a.pos_ids + (size_t)b * nq;
+    const uint8_t* sel_b = a.sel + (size_t)b * nq;
+    const uint8_t* vis_b = a.vis ? a.vis + (size_t)b * nq * nq : nullptr;
+
+    // selected rows in Q order (wave 0, 64 rows per ballot)
+    if (wave == 0) {
+        int n = 0;
+        for (int c = 0; c < nq; c += 64) {
+            const int j = c + lane;
+            const bool s = j < nq && sel_b[j] != 0;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(s);
+            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (s) sSel[n + below] = j;
+            n += __builtin_popcountll(m);
+        }
+        if (lane == 0) sNsel = n;
+    }
+    // owner row of each position of the split: the first row in Q order
+    for (int k = tid; k < k1 - k0; k += kMassWaves * 64) sOwner[k] = 0x7fffffff;
+    __syncthreads();
+    for (int j = tid; j < nq; j += kMassWaves * 64) {
+        const int p = pos_b[j];
+        if (p >= k0 && p < k1) atomicMin(&sOwner[p - k0], j);
+    }
+    const int nsel = sNsel;
+    // visibility bits of the selected rows (word w covers owner rows 32w..)
+    if (vis_b) {
+        for (int t = tid; t < nsel * VW; t += kMassWaves * 64) {
+            const int s = t / VW, w = t - s * VW;
+            const uint8_t* row = vis_b + (size_t)sSel[s] * nq;
+            uint32_t bits = 0u;
+            for (int e = 0; e < 32 && 32 * w + e < nq; ++e) bits |= (row[32 * w + e] != 0 ? 1u : 0u) << e;
+            sVis[t] = bits;
+        }
+    }
+    __syncthreads();
+
+    const int R = nsel * G;                          // (selected row, head) pairs
+    // row of selected slot s (clamped; with no selected row, row 0 stands in
+    // and every score is dropped through L2 = +inf)
+    auto selrow = [&](int s) { return nsel > 0 ? sSel[min(s, nsel - 1)] : 0; };
+    const float* qbase = a.qbuf + (size_t)bg * a.q_max * G * kDH;
+    float* part = a.part + (size_t)bg * a.N;
+    const bf16* Kg = (const bf16*)a.Kc + (size_t)bg * a.N * kDH;
+    const int nkb = (k1 - k0 + 15) >> 4;
+    const float kLog2e = 1.4426950408889634f;
+
+    for (int r0 = 0; r0 < max(R, 1); r0 += 16 * kMassRowBlocks) {
+        // q fragments of up to four row blocks (rows past R: zero q, L2 = +inf)
+        bf16x8 qh[kMassRowBlocks][4], ql[kMassRowBlocks][4];
+        float l2[kMassRowBlocks][4];
+        int srow[kMassRowBlocks][4];
+#pragma unroll
+        for (int rb = 0; rb < kMassRowBlocks; ++rb) {
+            const int row = r0 + rb * 16 + lr;
+            const bool ok = row < R;
+            const int rr = ok ? row : 0;
+            const int s = rr / G, hl = rr - s * G;
+            const float* qp = qbase + ((size_t)selrow(s) * G + hl) * kDH;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const f32x4 x0 = *(const f32x4*)(qp + 32 * c + 8 * lg);
+                const f32x4 x1 = *(const f32x4*)(qp + 32 * c + 8 * lg + 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = ok ? (e < 4 ? x0[e] : x1[e - 4]) * a.scale_log2 : 0.f;
+                    const bf16 hi = (bf16)x;
+                    qh[rb][c][e] = hi;
+                    ql[rb][c][e] = (bf16)(x - (float)hi);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rowi = r0 + rb * 16 + 4 * lg + i;
+                const bool oki = rowi < R;
+                const int ri = oki ? rowi : 0;
+                const int si = ri / G, hli = ri - si * G;
+                const int qi = selrow(si);
+                const float lse = a.LSE[((size_t)b * nq + qi) * a.H + g * G + hli];
+                // an empty key set (-inf) or a padding row contributes nothing
+                l2[rb][i] = (oki && lse > -INFINITY) ? lse * kLog2e : INFINITY;
+                srow[rb][i] = oki ? si : -1;
+            }
+        }
+        for (int kb = wave; kb < nkb; kb += kMassWaves) {
+            const int key = k0 + kb * 16 + lr;
+            const int kc = min(key, k1 - 1);
+            bf16x8 kf[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) kf[c] = *(const bf16x8*)(Kg + (size_t)kc * kDH + 32 * c + 8 * lg);
+            const int own = sOwner[kc - k0];
+            const int owner = own == 0x7fffffff ? -1 : own;
+            const bool gated = vis_b != nullptr && owner >= 0;
+            float colsum = 0.f;
+#pragma unroll
+            for (int rb = 0; rb < kMassRowBlocks; ++rb) {
+                f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[rb][c], kf[c], sc, 0, 0, 0);
+                    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[rb][c], kf[c], sc, 0, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    bool keep = key < k1;
+                    if (gated) {
+                        const int s = max(srow[rb][i], 0);
+                        keep = keep && ((sVis[s * VW + (owner >> 5)] >> (owner & 31)) & 1u);
+                    }
+                    const float pv = __builtin_amdgcn_exp2f(sc[i] - l2[rb][i]);   // 2^-inf = 0
+                    colsum += keep ? pv : 0.f;
+                }
+            }
+            colsum = sum4x(colsum);
+            if (lg == 0 && key < k1) {
+                if (r0 == 0) part[key] = colsum;
+                else part[key] += colsum;
+            }
+        }
+    }
+}
+
+// Scalar form for the fp32 layers and head widths other than 128: one thread
+// per (sequence, kv head, position), fp32 dot products.
+template <typename T>
+__global__ void __launch_bounds__(256) key_mass_generic_kernel(MassArgs a)
+{
+    const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (size_t)a.B * a.Hkv * a.N) return;
+    const int p = (int)(t % a.N);
+    const int bg = (int)(t / a.N);
+    const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+    const int nq = a.nq, G = a.G, dh = a.dh;
+    const int32_t* pos_b = a.pos_ids + (size_t)b * nq;
+    int owner = -1;
+    for (int j = 0; j < nq && owner < 0; ++j)
+        if (pos_b[j] == p) owner = j;
+    const T* kp = (const T*)a.Kc + ((size_t)bg * a.N + p) * dh;
+    const float* qb = a.qbuf + (size_t)bg * a.q_max * G * dh;
+    const float kLog2e = 1.4426950408889634f;
+    float acc = 0.f;
+    for (int i = 0; i < nq; ++i) {
+        if (!a.sel[(size_t)b * nq + i]) continue;
+        if (owner >= 0 && a.vis && !a.vis[((size_t)b * nq + i) * nq + owner]) continue;
+        for (int hl = 0; hl < G; ++hl) {
+            const float lse = a.LSE[((size_t)b * nq + i) * a.H + g * G + hl];
+            if (!(lse > -INFINITY)) continue;
+            const float* q = qb + ((size_t)i * G + hl) * dh;
+            float s = 0.f;
+            for (int e = 0; e < dh; ++e) s += q[e] * to_f32(kp[e]);
+            acc += exp2f(s * a.scale_log2 - lse * kLog2e);
+        }
+    }
+    a.part[t] = acc;
+}
+
+// a_p = sum over kv heads of the partial sums, in head order
+__global__ void __launch_bounds__(256) key_mass_sum_kernel(const float* __restrict__ part, float* __restrict__ scores,
+                                                           int B, int Hkv, int N)
+{
+    const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (t >= (size_t)B * N) return;
+    const size_t b = t / N, p = t - b * N;
+    const float* src = part + b * Hkv * (size_t)N + p;
+    float s = 0.f;
+    for (int g = 0; g < Hkv; ++g) s += src[(size_t)g * N];
+    scores[t] = s;
+}
+
+// Order-preserving unsigned image of a float (-0 folded onto +0).
+__device__ __forceinline__ uint32_t ordered_bits(float x)
+{
+    const uint32_t u = __float_as_uint(x + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kTopThreads = 1024;
+
+// One workgroup per sequence; LDS holds n2 (a power of two >= N) 64-bit keys.
+__global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __restrict__ scores,
+                                                                 const uint8_t* __restrict__ cand, int N, int n2,
+                                                                 int k, int32_t* __restrict__ out)
+{
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint64_t* key = (uint64_t*)smem;
+    const int b = blockIdx.x;
+    const float* sc = scores + (size_t)b * N;
+    const uint8_t* cd = cand + (size_t)b * N;
+    for (int p = threadIdx.x; p < n2; p += kTopThreads) {
+        uint64_t v = 0;   // padding and non-candidates sort last
+        if (p < N && cd[p]) v = ((uint64_t)ordered_bits(sc[p]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)p);
+        key[p] = v;
+    }
+    __syncthreads();
+    // bitonic network, descending overall
+    for (int size = 2; size <= n2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int t = threadIdx.x; t < n2 / 2; t += kTopThreads) {
+                const int lo = 2 * t - (t & (stride - 1));
+                const int hi = lo + stride;
+                const bool desc = (lo & size) == 0;
+                const uint64_t x = key[lo], y = key[hi];
+                if ((x < y) == desc) { key[lo] = y; key[hi] = x; }
+            }
+            __syncthreads();
+        }
+    }
+    for (int t = threadIdx.x; t < k; t += kTopThreads) {
+        const uint64_t v = t < n2 ? key[t] : 0;
+        out[(size_t)b * k + t] = v == 0 ? -1 : (int32_t)(0xffffffffu - (uint32_t)(v & 0xffffffffu));
+    }
+}
+
+}  // namespace
+
+size_t key_mass_lds_bytes(int nq, int keys_per_split)
+{
+    const int VW = (nq + 31) >> 5;
+    return (size_t)nq * 4 + (size_t)keys_per_split * 4 + (size_t)nq * VW * 4;
+}
+
+hipError_t launch_key_mass(const MassArgs& a, hipStream_t s)
+{
+    if (a.B * a.Hkv == 0 || a.N == 0) return hipSuccess;
+    const size_t shm = key_mass_lds_bytes(a.nq, a.keys_per_split);
+    if (shm > 150 * 1024) return hipErrorInvalidValue;
+    (void)hipFuncSetAttribute((const void*)key_mass_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(key_mass_kernel, dim3(a.B * a.Hkv * a.splits), dim3(kMassWaves * 64), shm, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t n = (size_t)a.B * a.N;
+    hipLaunchKernelGGL(key_mass_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.part, a.scores,
+                       a.B, a.Hkv, a.N);
+    return hipGetLastError();
+}
+
+hipError_t launch_key_mass_generic(const MassArgs& a, int dtype, hipStream_t s)
+{
+    const size_t n = (size_t)a.B * a.Hkv * a.N;
+    if (n == 0) return hipSuccess;
+    if (dtype == 1)
+        hipLaunchKernelGGL(key_mass_generic_kernel<bf16>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL(key_mass_generic_kernel<float>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t m = (size_t)a.B * a.N;
+    hipLaunchKernelGGL(key_mass_sum_kernel, dim3((unsigned)((m + 255) / 256)), dim3(256), 0, s, a.part, a.scores,
+                       a.B, a.Hkv, a.N);
+    return hipGetLastError();
+}
+
+hipError_t launch_select_top(const float* scores, const uint8_t* cand, int B, int N, int k, int32_t* out,
+                             hipStream_t s)
+{
+    if (B == 0 || k == 0) return hipSuccess;
+    int n2 = 1;
+    while (n2 < N) n2 <<= 1;
+    const size_t shm = (size_t)n2 * sizeof(uint64_t);
+    if (shm > 128 * 1024) return hipErrorInvalidValue;
+    (void)hipFuncSetAttribute((const void*)select_top_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(select_top_kernel, dim3(B), dim3(kTopThreads), shm, s, scores, cand, N, n2, k, out);
+    return hipGetLastError();
+}
+
+}  // namespace fdllm

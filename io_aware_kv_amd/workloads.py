@@ -324,3 +324,27 @@ def initial_cache(wl: Workload):
         shape = (ls.B, ls.Hkv, ls.N, ls.dh)
         wl.meta[key] = (_randn(g, shape, std, ls.dtype), _randn(g, shape, std, ls.dtype))
     return wl.meta[key]
+
+
+def selection_inputs(wl: Workload):
+    """Inputs of the tracked-set selection that follows the step: sel [B, nq]
+    uint8 marks the masked query rows (the [MASK] group where the workload
+    names groups, else the rows at or past the decoded prefix, else every
+    other row); cand [B, N] uint8 marks the decoded positions (before the
+    prefix end where there is one, else every position no query row writes)."""
+    B, nq, N = wl.shape.B, wl.nq, wl.shape.N
+    sel = torch.zeros((B, nq), dtype=torch.uint8)
+    cand = torch.ones((B, N), dtype=torch.uint8)
+    Ls = wl.meta.get("decoded_prefix")
+    for b in range(B):
+        if "groups" in wl.meta:
+            sel[b] = torch.tensor([1 if t == "mask" else 0 for t in wl.meta["groups"][b]], dtype=torch.uint8)
+        elif Ls is not None:
+            sel[b] = (wl.pos_ids[b] >= Ls[b]).to(torch.uint8)
+        else:
+            sel[b, ::2] = 1
+        if Ls is not None:
+            cand[b, Ls[b]:] = 0
+        else:
+            cand[b, wl.pos_ids[b].long()] = 0
+    return sel, cand

@@ -1,0 +1,143 @@
+"""GPU parity of the tracked-set scores and the top-k selection that follow
+the fused step (jaehun.me review, "How It Works: A Concrete Example", Step 1:
+Cache selection), through the C ABI, against the fp64 oracle.
+
+Bar.  A score is a sum of exp(s - LSE) terms; the step's LSE meets 1e-3
+absolute and its scores carry the fp32 error of q and the stored k rows, so
+each term is within a factor exp(+-2e-3) of the oracle's: elementwise
+|gpu - oracle| <= 3e-3 * oracle + 1e-6 * max(oracle).  The top-k of given
+fp32 scores is an integer result and must match the oracle's ranking of the
+same fp32 values exactly; against the oracle's own scores the selected set
+must be a valid top-k up to that tolerance (near-equal scores may swap).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from io_aware_kv_amd.binding import FusedKVCache
+from io_aware_kv_amd.workloads import (LayerShape, initial_cache, make_random_case, make_workload,
+                                       selection_inputs)
+from parity_util import log, run_oracle, shape_of
+
+pytestmark = pytest.mark.gpu
+
+RTOL, ATOL_REL = 3e-3, 1e-6
+
+
+def masked_rows(wl):
+    return selection_inputs(wl)[0].numpy()
+
+
+def decoded_candidates(wl):
+    return selection_inputs(wl)[1].numpy()
+
+
+def run_gpu_selection(wl, sel, cand, k, repeat=1):
+    ls = wl.shape
+    dev = torch.device("cuda")
+    K0, V0 = initial_cache(wl)
+    Kc, Vc = K0.to(dev).contiguous(), V0.to(dev).contiguous()
+    fk = FusedKVCache(ls.B, ls.N, ls.d_model, ls.H, ls.Hkv, ls.dh, max(1, wl.nq), ls.dtype, ls.rope_base)
+    X, W = wl.X.to(dev), wl.W.to(dev)
+    Q, P = wl.Q_idx.to(dev), wl.pos_ids.to(dev)
+    vis = wl.vis.to(dev) if wl.vis is not None else None
+    O = torch.empty((ls.B, wl.nq, ls.H, ls.dh), dtype=ls.dtype, device=dev)
+    LSE = torch.empty((ls.B, wl.nq, ls.H), dtype=torch.float32, device=dev)
+    fk.step(X, Q, P, vis, W, Kc, Vc, O, LSE)
+    sel_d = torch.from_numpy(sel).to(dev)
+    cand_d = torch.from_numpy(cand).to(dev)
+    runs = []
+    for _ in range(repeat):
+        scores = torch.full((ls.B, ls.N), float("nan"), dtype=torch.float32, device=dev)
+        out = torch.full((ls.B, k), -7, dtype=torch.int32, device=dev)
+        fk.tracked_scores(P, vis, sel_d, Kc, LSE, scores)
+        fk.select_tracked(scores, cand_d, k, out)
+        torch.cuda.synchronize()
+        runs.append((scores.cpu(), out.cpu()))
+    fk.close()
+    return runs
+
+
+def check_selection(wl, label, k=80):
+    sel = masked_rows(wl)
+    cand = decoded_candidates(wl)
+    runs = run_gpu_selection(wl, sel, cand, k, repeat=2)
+    sg, og = runs[-1]
+    r = run_oracle(wl)
+    ref = oracle.key_scores(shape_of(wl.shape), r["q"], r["Kc"], r["LSE"], wl.pos_ids, wl.vis, sel)
+    g = sg.double().numpy()
+    assert np.isfinite(g).all(), label + ": non-finite scores"
+    err = np.abs(g - ref)
+    bound = RTOL * ref + ATOL_REL * max(ref.max(), 1e-30)
+    log("%s scores: max rel err %.2e (max score %.3g, %d rows selected)" %
+        (label, float((err / np.maximum(ref, 1e-30)).max()), ref.max(), int(sel.sum())))
+    assert (err <= bound).all(), "%s: scores off, worst %.3e" % (label, float((err - bound).max()))
+    # same bits on a second call
+    assert torch.equal(runs[0][0].view(torch.int32), sg.view(torch.int32))
+    assert torch.equal(runs[0][1], og)
+    # top-k of the GPU's own fp32 scores: exactly the oracle's ranking
+    want = oracle.select_top(sg.numpy(), cand, k)
+    assert np.array_equal(og.numpy(), want), label + ": top-k differs from the ranking of the same scores"
+    # against the oracle's scores: a valid top-k up to the score tolerance
+    for b in range(wl.shape.B):
+        chosen = [p for p in og[b].tolist() if p >= 0]
+        assert len(chosen) == min(k, int(cand[b].sum()))
+        rest = np.setdiff1d(np.nonzero(cand[b])[0], chosen)
+        if chosen and rest.size:
+            lo = ref[b, chosen].min()
+            hi = ref[b, rest].max()
+            assert lo >= hi - 2 * (RTOL * hi + ATOL_REL * ref.max()), label + ": selection not a top-k"
+
+
+@pytest.mark.parametrize("cid", [2, 3, 6, 7, 1])
+def test_tracked_scores_layer_workloads(cid):
+    log("case: tracked scores, workload %d" % cid)
+    check_selection(make_workload(cid), "workload%d" % cid, k=80 if cid != 1 else 5)
+
+
+def test_tracked_scores_gqa_duplicates_mask():
+    log("case: tracked scores, GQA with duplicates and a mask")
+    ls = LayerShape(B=3, N=700, d_model=256, H=8, Hkv=2, dh=128)
+    wl = make_random_case(ls, 40, seed=41, n_extra_rows=8, dup_frac=0.2, masked_vis=True, w_std=0.05)
+    check_selection(wl, "gqa-dups-mask", k=33)
+
+
+def test_tracked_scores_many_rows_two_groups():
+    """More than 64 selected (row, head) pairs: the rows go through the
+    registers in two groups."""
+    log("case: tracked scores, 100 selected rows x G=2")
+    ls = LayerShape(B=2, N=300, d_model=128, H=4, Hkv=2, dh=128)
+    wl = make_random_case(ls, 120, seed=42, masked_vis=True, w_std=0.05)
+    check_selection(wl, "two-row-groups", k=50)
+
+
+def test_select_top_ties_and_short_candidate_lists():
+    """Hand-made fp32 scores with many exact ties, N not a power of two,
+    k larger than some sequences' candidate counts."""
+    log("case: top-k ties")
+    B, N, k = 3, 5000, 40
+    rng = np.random.default_rng(43)
+    sc = (rng.integers(0, 30, size=(B, N)) / 8.0).astype(np.float32)
+    cand = (rng.random((B, N)) < 0.5).astype(np.uint8)
+    cand[2] = 0
+    cand[2, [5, 4999, 17]] = 1
+    dev = torch.device("cuda")
+    fk = FusedKVCache(B, N, 128, 2, 2, 128, 4, torch.bfloat16)
+    out = torch.full((B, k), -7, dtype=torch.int32, device=dev)
+    fk.select_tracked(torch.from_numpy(sc).to(dev), torch.from_numpy(cand).to(dev), k, out)
+    torch.cuda.synchronize()
+    fk.close()
+    assert np.array_equal(out.cpu().numpy(), oracle.select_top(sc, cand, k))
+    assert out[2, 3:].eq(-1).all()
+
+
+def test_tracked_scores_no_rows_selected():
+    log("case: tracked scores, nothing selected")
+    wl = make_workload(2)
+    sel = np.zeros((wl.shape.B, wl.nq), dtype=np.uint8)
+    cand = decoded_candidates(wl)
+    (sg, og), = run_gpu_selection(wl, sel, cand, 10)
+    assert torch.all(sg == 0)
+    # all scores equal: the lowest candidate positions, in order
+    assert og[0].tolist() == np.nonzero(cand[0])[0][:10].tolist()
