@@ -32,7 +32,7 @@ namespace {
 
 constexpr int kDH = 128;
 constexpr int kMassWaves = 4;
-constexpr int kMassRowBlocks = 4;     // row blocks of 16 held in registers at a time
+constexpr int kMassUnroll = 4;        // 16-key blocks a wave loads before computing
 
 __device__ __forceinline__ float sum4x(float x)
 {
@@ -42,9 +42,14 @@ __device__ __forceinline__ float sum4x(float x)
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// LDS layout (dynamic): sSel[nq] int, sOwner[kps] int, sVis[nq * VW] u32
+// LDS layout (dynamic): sSel[nq] int, sOwner[kps] int, sVis[nq * VW] u32.
+// Up to four row blocks of 16 (selected row, head) pairs are held in
+// registers at a time (blocks past the selection are skipped); a wave takes
+// kMassUnroll consecutive 16-key blocks per round with all their K loads in
+// flight.
 __global__ void __launch_bounds__(kMassWaves * 64) key_mass_kernel(MassArgs a)
 {
+    constexpr int kMassRowBlocks = 4;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ int sNsel;
     const int nq = a.nq, G = a.G;
@@ -145,39 +150,48 @@ __global__ void __launch_bounds__(kMassWaves * 64) key_mass_kernel(MassArgs a)
                 srow[rb][i] = oki ? si : -1;
             }
         }
-        for (int kb = wave; kb < nkb; kb += kMassWaves) {
-            const int key = k0 + kb * 16 + lr;
-            const int kc = min(key, k1 - 1);
-            bf16x8 kf[4];
+        for (int kb0 = wave * kMassUnroll; kb0 < nkb; kb0 += kMassWaves * kMassUnroll) {
+            bf16x8 kf[kMassUnroll][4];
+            int keyu[kMassUnroll], ownu[kMassUnroll];
 #pragma unroll
-            for (int c = 0; c < 4; ++c) kf[c] = *(const bf16x8*)(Kg + (size_t)kc * kDH + 32 * c + 8 * lg);
-            const int own = sOwner[kc - k0];
-            const int owner = own == 0x7fffffff ? -1 : own;
-            const bool gated = vis_b != nullptr && owner >= 0;
-            float colsum = 0.f;
+            for (int u = 0; u < kMassUnroll; ++u) {
+                keyu[u] = k0 + (kb0 + u) * 16 + lr;
+                const int kc = min(keyu[u], k1 - 1);
 #pragma unroll
-            for (int rb = 0; rb < kMassRowBlocks; ++rb) {
-                f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[rb][c], kf[c], sc, 0, 0, 0);
-                    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[rb][c], kf[c], sc, 0, 0, 0);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    bool keep = key < k1;
-                    if (gated) {
-                        const int s = max(srow[rb][i], 0);
-                        keep = keep && ((sVis[s * VW + (owner >> 5)] >> (owner & 31)) & 1u);
-                    }
-                    const float pv = __builtin_amdgcn_exp2f(sc[i] - l2[rb][i]);   // 2^-inf = 0
-                    colsum += keep ? pv : 0.f;
-                }
+                for (int c = 0; c < 4; ++c) kf[u][c] = *(const bf16x8*)(Kg + (size_t)kc * kDH + 32 * c + 8 * lg);
+                ownu[u] = sOwner[kc - k0];
             }
-            colsum = sum4x(colsum);
-            if (lg == 0 && key < k1) {
-                if (r0 == 0) part[key] = colsum;
-                else part[key] += colsum;
+#pragma unroll
+            for (int u = 0; u < kMassUnroll; ++u) {
+                const int key = keyu[u];
+                const int owner = ownu[u] == 0x7fffffff ? -1 : ownu[u];
+                const bool gated = vis_b != nullptr && owner >= 0;
+                float colsum = 0.f;
+#pragma unroll
+                for (int rb = 0; rb < kMassRowBlocks; ++rb) {
+                    if (r0 + rb * 16 >= R) break;          // (uniform: no selected pair left)
+                    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[rb][c], kf[u][c], sc, 0, 0, 0);
+                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[rb][c], kf[u][c], sc, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        bool keep = key < k1;
+                        if (gated) {
+                            const int sr = max(srow[rb][i], 0);
+                            keep = keep && ((sVis[sr * VW + (owner >> 5)] >> (owner & 31)) & 1u);
+                        }
+                        const float pv = __builtin_amdgcn_exp2f(sc[i] - l2[rb][i]);   // 2^-inf = 0
+                        colsum += keep ? pv : 0.f;
+                    }
+                }
+                colsum = sum4x(colsum);
+                if (lg == 0 && key < k1) {
+                    if (r0 == 0) part[key] = colsum;
+                    else part[key] += colsum;
+                }
             }
         }
     }
