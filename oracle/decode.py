@@ -24,6 +24,8 @@ from __future__ import annotations
 
 from typing import Dict, List, Sequence, Tuple
 
+import numpy as np
+
 
 def front_masks(masked: Sequence[int], beta_m: int) -> List[int]:
     """M_t^{beta_m}: the first beta_m still-masked positions (ascending)."""
@@ -141,3 +143,24 @@ def block_tv(c_tilde_accepted: Sequence[float]) -> float:
 def tv_bounds(m: int, gamma: float) -> Tuple[float, float]:
     """The two upper bounds of the block TV distance: (1 - gamma^m, m (1 - gamma))."""
     return 1.0 - gamma ** m, m * (1.0 - gamma)
+
+
+def softmax_fp64(logits) -> np.ndarray:
+    """Softmax over the last axis in fp64 (the distribution behind a row of logits)."""
+    x = np.asarray(logits, dtype=np.float64)
+    e = np.exp(x - x.max(axis=-1, keepdims=True))
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def confidences(logits, mask_id: int | None):
+    """(pred, conf) for every row of logits [..., V]: the softmax over all ids
+    in fp64, then, over the non-[MASK] ids, the first largest probability (the
+    lowest id among equal ones) and its value -- ``confidence`` applied to each
+    row, with numpy doing the per-row work."""
+    p = softmax_fp64(logits)
+    if mask_id is not None and 0 <= mask_id < p.shape[-1]:
+        p = p.copy()
+        p[..., mask_id] = -np.inf
+    pred = np.argmax(p, axis=-1)          # first occurrence: lowest id on ties
+    conf = np.take_along_axis(p, pred[..., None], axis=-1)[..., 0]
+    return pred.astype(np.int64), conf

@@ -101,3 +101,36 @@ def test_tv_bound_chain_holds_for_random_accepted_blocks():
         tv = decode.block_tv(cs)
         b1, b2 = decode.tv_bounds(m, gamma)
         assert 0.0 <= tv <= b1 + 1e-12 and b1 <= b2 + 1e-12
+
+
+# --------------------------------------------------------------------------
+# confidences from logits (the form the device decision kernel takes)
+# --------------------------------------------------------------------------
+
+def test_confidences_from_log_probs_reproduce_the_example(ex):
+    """Logits = log of the example's probabilities: the softmax gives them
+    back, so prediction, confidence and the eps split are the page's."""
+    import numpy as np
+    rows = [ex["draft_probs"]["2"], ex["draft_probs"]["3"], ex["verify_mask_view_probs"]["3"]]
+    pred, conf = decode.confidences(np.log(np.array(rows)), ex["mask_id"])
+    assert [ex["vocab"][i] for i in pred] == ["A", "A", "A"]
+    assert conf == pytest.approx([0.92, 0.70, 0.85])
+    assert [c >= ex["eps"] for c in conf[:2]] == [True, False]
+    assert conf[2] >= ex["gamma"]
+
+
+def test_confidences_equal_the_row_loop_and_are_shift_invariant():
+    import numpy as np
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((40, 37)) * 3
+    x[3, [4, 9]] = x[3].max() + 1.0          # a tie at the top: the lower id wins
+    x[5, 0] = x[5].max() + 5.0               # the [MASK] id on top: excluded
+    pred, conf = decode.confidences(x, 0)
+    p = decode.softmax_fp64(x)
+    for r in range(40):
+        t, c = decode.confidence(list(p[r]), 0)
+        assert pred[r] == t and conf[r] == pytest.approx(c, rel=1e-15)
+    assert pred[3] == 4 and pred[5] != 0
+    pred2, conf2 = decode.confidences(x + 123.0, 0)
+    assert (pred2 == pred).all() and np.allclose(conf2, conf, rtol=1e-12)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=1e-14)
