@@ -182,6 +182,53 @@ def time_selection(fk, wl, sets, stream, iters):
             "scores_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
+def time_decision(wl, stream, iters):
+    """Time the draft-pass decisions for the step's masked rows over the
+    synthetic vocabulary: per-row prediction and confidence with the eps
+    split, then the sequential acceptance over the same rows."""
+    import torch
+    from io_aware_kv_amd import binding
+    from io_aware_kv_amd.workloads import SYNTH_VOCAB, decision_logits, selection_inputs
+    sel, _ = selection_inputs(wl)
+    rows = max(1, int(sel.sum()))
+    V = SYNTH_VOCAB
+    dev = torch.device("cuda")
+    host = decision_logits(rows, V, seed=wl.seed)
+    bufs = [host.to(dev) for _ in range(2)]   # alternate, so no call finds its rows cached
+    pred = torch.empty((rows,), dtype=torch.int32, device=dev)
+    conf = torch.empty((rows,), dtype=torch.float32, device=dev)
+    over = torch.empty((rows,), dtype=torch.uint8, device=dev)
+    B = wl.shape.B
+    S = max(1, rows // B)
+    n_acc = torch.empty((B,), dtype=torch.int32, device=dev)
+
+    def run(i, evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        binding.confidence(bufs[i % 2], 126, 0.9, pred, conf, over, stream=stream)
+        if evs is not None:
+            evs[1].record(stream)
+        binding.accept(pred[:B * S].view(B, S), pred[:B * S].view(B, S), conf[:B * S].view(B, S), 0.8, n_acc,
+                       stream=stream)
+        if evs is not None:
+            evs[2].record(stream)
+
+    for i in range(3):
+        run(i)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(iters)]
+    for i in range(iters):
+        run(i, evs[i])
+    torch.cuda.synchronize()
+    c_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / iters
+    a_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / iters
+    nbytes = rows * V * 2 + rows * 9
+    gbps = nbytes / (c_ms * 1e-3) / 1e9
+    return {"rows": rows, "vocab": V, "confidence_us": round(c_ms * 1e3, 3), "accept_us": round(a_ms * 1e3, 3),
+            "confidence_algorithmic_bytes": nbytes, "confidence_GBps": round(gbps, 1),
+            "confidence_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -292,6 +339,11 @@ def main():
     if not args.no_select:
         selection = time_selection(fk, wl, sets, stream, min(args.steps, 50))
         log("bench: tracked-set scores %.2f us, top-k %.2f us" % (selection["scores_us"], selection["select_us"]))
+        decision = time_decision(wl, stream, min(args.steps, 50))
+        log("bench: decisions over %d rows x %d ids: %.2f us (%.0f GB/s), acceptance %.2f us" %
+            (decision["rows"], decision["vocab"], decision["confidence_us"], decision["confidence_GBps"],
+             decision["accept_us"]))
+        selection["decision"] = decision
 
     # dominant kernel roofline
     dom = "attn" if attn_avg >= proj_avg else "proj"

@@ -168,6 +168,32 @@ int fdllm_tracked_scores(fdllm_handle_t h, const int32_t* pos_ids, int32_t nq, c
 int fdllm_select_tracked(fdllm_handle_t h, const float* scores, const uint8_t* cand, int32_t k,
                          int32_t* out, void* stream);
 
+/* Flash-Verify decisions on the device (jaehun.me review, "Flash-Verify:
+ * Cache-Based Draft-Verification Parallel Decoding" and "How It Works: A
+ * Concrete Example", Step 1: Draft / Verification).  They take no handle.
+ *
+ * fdllm_confidence: for each of `rows` rows of logits [rows, V] (dtype
+ * FDLLM_BF16 or FDLLM_F32, 16-byte aligned), pred[r] = the argmax over the ids
+ * other than mask_id (equal logits: the lowest id; mask_id < 0 excludes
+ * none), conf[r] = that id's probability under the softmax over all V ids
+ * (fp32), and, if over != NULL, over[r] = (conf[r] >= thr): with thr = eps
+ * this is the split of the draft pass into the confident set (1) and the
+ * exploratory set (0); with thr = gamma it is the mask view's confidence test.
+ * At least one logit of a row must be finite.  pred int32 [rows], conf fp32
+ * [rows], over uint8 [rows], caller-owned device pointers.
+ * Statuses: ARG (NULL pointer, V < 1, rows < 0, dtype), ALIGN, HIP. */
+int fdllm_confidence(const void* logits, int32_t dtype, int64_t rows, int32_t V, int32_t mask_id, float thr,
+                     int32_t* pred, float* conf, uint8_t* over, void* stream);
+
+/* Sequential acceptance of the verification pass: for each sequence b, the
+ * exploratory positions in decoding order are rows 0..S-1 of x_hat (draft
+ * predictions), x_tilde and c_tilde (the [MASK] view's predictions and
+ * confidences), all [B, S]; n_accept[b] = the number of leading rows with
+ * x_tilde == x_hat and c_tilde >= gamma (acceptance stops at the first
+ * failure).  Statuses: ARG, HIP. */
+int fdllm_accept(const int32_t* x_hat, const int32_t* x_tilde, const float* c_tilde, int32_t B, int32_t S,
+                 float gamma, int32_t* n_accept, void* stream);
+
 /* Set (tuning != NULL) or reset (NULL) the launch-shape overrides of h.
  * Statuses: ARG. */
 int fdllm_set_tuning(fdllm_handle_t h, const fdllm_tuning_t* tuning);

@@ -66,6 +66,8 @@ def load():
     lib.fdllm_step_attend.argtypes = [P, P, i32, P, P, P, P, P, P]
     lib.fdllm_tracked_scores.argtypes = [P, P, i32, P, P, P, P, P, P]
     lib.fdllm_select_tracked.argtypes = [P, P, P, i32, P, P]
+    lib.fdllm_confidence.argtypes = [P, i32, ctypes.c_int64, i32, i32, ctypes.c_float, P, P, P, P]
+    lib.fdllm_accept.argtypes = [P, P, P, i32, i32, ctypes.c_float, P, P]
     lib.fdllm_set_tuning.argtypes = [P, ctypes.POINTER(Tuning)]
     lib.fdllm_get_plan.argtypes = [P, i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.fdllm_cache_destroy.argtypes = [P]
@@ -73,6 +75,7 @@ def load():
     lib.fdllm_status_str.restype = ctypes.c_char_p
     for name in ("fdllm_validate_config", "fdllm_cache_init", "fdllm_prefill", "fdllm_fused_step",
                  "fdllm_step_project", "fdllm_step_attend", "fdllm_tracked_scores", "fdllm_select_tracked",
+                 "fdllm_confidence", "fdllm_accept",
                  "fdllm_set_tuning", "fdllm_get_plan", "fdllm_cache_destroy"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -106,6 +109,35 @@ def _dtype_code(dtype: torch.dtype) -> int:
     if dtype == torch.float32:
         return FDLLM_F32
     raise ValueError("dtype must be bfloat16 or float32")
+
+
+def confidence(logits: torch.Tensor, mask_id: int, thr: float, pred: torch.Tensor, conf: torch.Tensor,
+               over: Optional[torch.Tensor] = None, stream=None):
+    """Per-row prediction and confidence of logits [..., V] (see fdllm.h);
+    pred int32, conf fp32 and over uint8 hold one value per row."""
+    V = logits.shape[-1]
+    rows = logits.numel() // V
+    for name, t, dt in (("pred", pred, torch.int32), ("conf", conf, torch.float32)):
+        if t.dtype != dt or t.numel() != rows:
+            raise ValueError("%s must be %s with one value per row" % (name, dt))
+    if over is not None and (over.dtype != torch.uint8 or over.numel() != rows):
+        raise ValueError("over must be uint8 with one value per row")
+    _check(load().fdllm_confidence(_ptr(logits), _dtype_code(logits.dtype), rows, V, mask_id, float(thr),
+                                   _ptr(pred), _ptr(conf), _ptr(over), _stream(stream)), "fdllm_confidence")
+
+
+def accept(x_hat: torch.Tensor, x_tilde: torch.Tensor, c_tilde: torch.Tensor, gamma: float,
+           n_accept: torch.Tensor, stream=None):
+    """Sequential acceptance over [B, S] rows in decoding order into n_accept [B] int32."""
+    B, S = x_hat.shape
+    if x_hat.dtype != torch.int32 or x_tilde.dtype != torch.int32 or c_tilde.dtype != torch.float32:
+        raise ValueError("x_hat, x_tilde int32 and c_tilde fp32 [B, S]")
+    if tuple(x_tilde.shape) != (B, S) or tuple(c_tilde.shape) != (B, S):
+        raise ValueError("x_tilde and c_tilde must be [B, S]")
+    if n_accept.dtype != torch.int32 or n_accept.numel() != B:
+        raise ValueError("n_accept must be int32 [B]")
+    _check(load().fdllm_accept(_ptr(x_hat), _ptr(x_tilde), _ptr(c_tilde), B, S, float(gamma), _ptr(n_accept),
+                               _stream(stream)), "fdllm_accept")
 
 
 def make_config(B, N, d_model, H, Hkv, dh, q_max, dtype=torch.bfloat16, rope_base=10000.0) -> Config:

@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "libfdllm.so")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["fdllm_api.hip", "generic_kernels.hip", "proj_mfma.hip", "attn_mfma.hip", "select.hip"]
+SOURCES = ["fdllm_api.hip", "generic_kernels.hip", "proj_mfma.hip", "attn_mfma.hip", "select.hip", "decide.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

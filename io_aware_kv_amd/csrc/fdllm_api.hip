@@ -427,6 +427,28 @@ int fdllm_select_tracked(fdllm_handle_t h, const float* scores, const uint8_t* c
     return hip_status(launch_select_top(scores, cand, h->cfg.B, h->cfg.N, k, out, (hipStream_t)stream));
 }
 
+int fdllm_confidence(const void* logits, int32_t dtype, int64_t rows, int32_t V, int32_t mask_id, float thr,
+                     int32_t* pred, float* conf, uint8_t* over, void* stream)
+{
+    if (rows < 0 || V < 1 || (dtype != FDLLM_BF16 && dtype != FDLLM_F32)) return FDLLM_ERR_ARG;
+    if (rows == 0) return FDLLM_OK;
+    if (!logits || !pred || !conf) return FDLLM_ERR_ARG;
+    if (rows > 0x7fffffff) return FDLLM_ERR_ARG;
+    if (!aligned16(logits) || (reinterpret_cast<uintptr_t>(pred) & 3u) || (reinterpret_cast<uintptr_t>(conf) & 3u))
+        return FDLLM_ERR_ALIGN;
+    return hip_status(launch_confidence(logits, dtype, rows, V, mask_id, thr, pred, conf, over,
+                                        (hipStream_t)stream));
+}
+
+int fdllm_accept(const int32_t* x_hat, const int32_t* x_tilde, const float* c_tilde, int32_t B, int32_t S,
+                 float gamma, int32_t* n_accept, void* stream)
+{
+    if (B < 0 || S < 0) return FDLLM_ERR_ARG;
+    if (B == 0) return FDLLM_OK;
+    if (!n_accept || (S > 0 && (!x_hat || !x_tilde || !c_tilde))) return FDLLM_ERR_ARG;
+    return hip_status(launch_accept(x_hat, x_tilde, c_tilde, B, S, gamma, n_accept, (hipStream_t)stream));
+}
+
 int fdllm_cache_destroy(fdllm_handle_t h)
 {
     if (!h) return FDLLM_OK;

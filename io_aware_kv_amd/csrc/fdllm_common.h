@@ -79,6 +79,11 @@ size_t key_mass_lds_bytes(int nq, int keys_per_split);
 hipError_t launch_select_top(const float* scores, const uint8_t* cand, int B, int N, int k, int32_t* out,
                              hipStream_t s);
 
+hipError_t launch_confidence(const void* logits, int dtype, int64_t rows, int V, int mask_id, float thr,
+                             int32_t* pred, float* conf, uint8_t* over, hipStream_t s);
+hipError_t launch_accept(const int32_t* x_hat, const int32_t* x_tilde, const float* c_tilde, int B, int S,
+                         float gamma, int32_t* n_accept, hipStream_t s);
+
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_proj_generic(const ProjArgs& a, int dtype, hipStream_t s);
 hipError_t launch_attn_generic(const AttnArgs& a, int dtype, hipStream_t s);

@@ -348,3 +348,18 @@ def selection_inputs(wl: Workload):
         else:
             cand[b, wl.pos_ids[b].long()] = 0
     return sel, cand
+
+
+SYNTH_VOCAB = 131072   # synthetic vocabulary size (the pages name none)
+
+
+def decision_logits(rows: int, V: int = SYNTH_VOCAB, seed: int = 7, dtype: torch.dtype = torch.bfloat16):
+    """Seeded logits [rows, V] for the decision kernels: N(0, 2^2) noise with
+    one raised id per row (raise drawn from U[0, 24]), so the confidences of
+    the rows spread from near zero to near one."""
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((rows, V), generator=g, dtype=torch.float32) * 2.0
+    top = torch.randint(0, V, (rows,), generator=g)
+    lift = torch.rand((rows,), generator=g) * 24.0
+    x[torch.arange(rows), top] += lift
+    return x.to(dtype)

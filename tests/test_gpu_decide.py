@@ -1,0 +1,109 @@
+"""GPU parity of the Flash-Verify decision kernels (per-row prediction and
+confidence, the eps / gamma threshold flags, sequential acceptance) through
+the C ABI against the oracle (oracle.decode), on the review's worked example
+("How It Works: A Concrete Example", Step 1: Draft / Verification) and on
+seeded logits over a synthetic vocabulary.
+
+Bar: predictions and acceptance counts are integers decided from the same
+input values on both sides and must match exactly; the confidence is an fp32
+softmax probability (relative error <= 1e-5 against fp64); a threshold flag
+must equal (gpu conf >= thr) and the oracle's decision wherever the oracle's
+confidence is more than 1e-5 (relative) away from the threshold.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from io_aware_kv_amd import binding
+from io_aware_kv_amd.workloads import decision_logits
+from oracle import decode
+from parity_util import log
+
+pytestmark = pytest.mark.gpu
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def gpu_confidence(logits, mask_id, thr):
+    dev = torch.device("cuda")
+    x = logits.to(dev).contiguous()
+    rows = x.numel() // x.shape[-1]
+    pred = torch.full((rows,), -7, dtype=torch.int32, device=dev)
+    conf = torch.full((rows,), float("nan"), dtype=torch.float32, device=dev)
+    over = torch.full((rows,), 7, dtype=torch.uint8, device=dev)
+    binding.confidence(x, mask_id, thr, pred, conf, over)
+    torch.cuda.synchronize()
+    return pred.cpu().numpy(), conf.cpu().numpy(), over.cpu().numpy()
+
+
+def test_worked_example_on_the_device():
+    log("case: worked example on the device")
+    with open(os.path.join(HERE, "golden", "worked_example.json")) as f:
+        ex = json.load(f)
+    rows = [ex["draft_probs"]["2"], ex["draft_probs"]["3"]]
+    logits = torch.tensor(np.log(np.array(rows)), dtype=torch.float32)
+    pred, conf, over = gpu_confidence(logits, ex["mask_id"], ex["eps"])
+    assert [ex["vocab"][i] for i in pred] == ["A", "A"]
+    assert conf == pytest.approx([0.92, 0.70], rel=1e-6)
+    D = [p for p, o in zip(ex["expected_Q"], over) if o]
+    S = [p for p, o in zip(ex["expected_Q"], over) if not o]
+    assert D == ex["expected_D"] and S == ex["expected_S"]
+    mv = torch.tensor(np.log(np.array([ex["verify_mask_view_probs"]["3"]])), dtype=torch.float32)
+    xt, ct, ot = gpu_confidence(mv, ex["mask_id"], ex["gamma"])
+    assert ct == pytest.approx([0.85], rel=1e-6) and ot.tolist() == [1]
+    dev = torch.device("cuda")
+    n = torch.full((1,), -7, dtype=torch.int32, device=dev)
+    binding.accept(torch.tensor([[pred[1]]], dtype=torch.int32, device=dev),
+                   torch.tensor([[xt[0]]], dtype=torch.int32, device=dev),
+                   torch.tensor([[ct[0]]], dtype=torch.float32, device=dev), ex["gamma"], n)
+    torch.cuda.synchronize()
+    assert S[:int(n.item())] == ex["expected_accepted"]
+
+
+@pytest.mark.parametrize("rows,V,dtype,mask_id", [
+    (512, 131072, torch.bfloat16, 126),     # the synthetic vocabulary, vector loads
+    (64, 1001, torch.float32, 1000),        # ragged vocabulary, scalar loads
+    (33, 4096, torch.float32, -1),          # no [MASK] id excluded
+])
+def test_confidence_matches_oracle(rows, V, dtype, mask_id):
+    log("case: confidence rows=%d V=%d %s" % (rows, V, dtype))
+    x = decision_logits(rows, V, seed=rows + V, dtype=dtype)
+    if dtype == torch.float32:
+        # exact ties at the top of some rows: the lower id wins on both sides
+        x[0, 10] = x[0].max() + 1.0
+        x[0, 20] = x[0, 10]
+    thr = 0.5
+    pred, conf, over = gpu_confidence(x, mask_id, thr)
+    rp, rc = decode.confidences(x.double().numpy(), mask_id if mask_id >= 0 else None)
+    assert np.array_equal(pred, rp), "predictions differ"
+    rel = np.abs(conf - rc) / np.maximum(rc, 1e-30)
+    log("conf max rel err %.2e, %d of %d rows over %.2f" % (rel.max(), int(over.sum()), rows, thr))
+    assert rel.max() <= 1e-5
+    assert np.array_equal(over.astype(bool), conf >= thr)
+    decided = np.abs(rc - thr) > 1e-5 * thr
+    assert np.array_equal(over.astype(bool)[decided], (rc >= thr)[decided])
+    if dtype == torch.float32:
+        assert pred[0] == 10
+
+
+def test_accept_matches_oracle():
+    log("case: sequential acceptance")
+    rng = np.random.default_rng(11)
+    B, S = 200, 32
+    x_hat = rng.integers(0, 5, size=(B, S)).astype(np.int32)
+    x_tilde = np.where(rng.random((B, S)) < 0.9, x_hat, (x_hat + 1) % 5).astype(np.int32)
+    c_tilde = rng.random((B, S)).astype(np.float32) * 0.4 + 0.6
+    gamma = float(np.float32(0.7))   # the threshold both sides compare against
+    dev = torch.device("cuda")
+    n = torch.full((B,), -7, dtype=torch.int32, device=dev)
+    binding.accept(torch.from_numpy(x_hat).to(dev), torch.from_numpy(x_tilde).to(dev),
+                   torch.from_numpy(c_tilde).to(dev), gamma, n)
+    torch.cuda.synchronize()
+    got = n.cpu().numpy()
+    for b in range(B):
+        acc = decode.accept(list(range(S)), dict(enumerate(x_hat[b].tolist())),
+                            dict(enumerate(x_tilde[b].tolist())), dict(enumerate(c_tilde[b].tolist())), gamma)
+        assert got[b] == len(acc)
+    assert 0 < got.mean() < S
