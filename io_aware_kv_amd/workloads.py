@@ -363,3 +363,44 @@ def decision_logits(rows: int, V: int = SYNTH_VOCAB, seed: int = 7, dtype: torch
     lift = torch.rand((rows,), generator=g) * 24.0
     x[torch.arange(rows), top] += lift
     return x.to(dtype)
+
+
+def paged_layout(wl: Workload, block_size: int, seed: int = 99, ragged: bool = True, spare_blocks: int = 7):
+    """Seeded block table and per-sequence lengths for serving the workload's
+    cache from a pool of blocks: each sequence gets its own blocks in a
+    random order (plus spare blocks nobody uses), a valid length covering
+    every position its rows write (when ragged: drawn up to N, else N), and a
+    query count (when ragged: at least one row, else nq).  The pools start
+    from the workload's initial cache placed through the table; spare
+    blocks hold seeded values.  Returns table [B, max_blocks], Kpool, Vpool
+    [blocks, Hkv, block_size, dh], seq_len [B], nq_seq [B] (int32 tensors)."""
+    ls = wl.shape
+    B, N, Hkv, dh = ls.B, ls.N, ls.Hkv, ls.dh
+    g = torch.Generator().manual_seed(wl.seed * 31 + seed)
+    max_blocks = (N + block_size - 1) // block_size
+    nblocks = B * max_blocks + spare_blocks
+    order = torch.randperm(nblocks, generator=g)
+    table = order[:B * max_blocks].reshape(B, max_blocks).to(torch.int32)
+    K0, V0 = initial_cache(wl)
+    std = wl.meta.get("w_std", 0.02) * float(ls.d_model) ** 0.5
+    Kpool = _randn(g, (nblocks, Hkv, block_size, dh), std, ls.dtype)
+    Vpool = _randn(g, (nblocks, Hkv, block_size, dh), std, ls.dtype)
+    for b in range(B):
+        for k in range(max_blocks):
+            p0, p1 = k * block_size, min(N, (k + 1) * block_size)
+            blk = int(table[b, k])
+            Kpool[blk, :, :p1 - p0] = K0[b, :, p0:p1]
+            Vpool[blk, :, :p1 - p0] = V0[b, :, p0:p1]
+    nq = wl.nq
+    if ragged:
+        nq_seq = torch.tensor([_randint(g, 1, nq) if nq > 0 else 0 for _ in range(B)], dtype=torch.int32)
+        lens = []
+        for b in range(B):
+            live = wl.pos_ids[b, :int(nq_seq[b])]
+            lo = int(live.max()) + 1 if live.numel() else 1
+            lens.append(_randint(g, lo, N))
+        seq_len = torch.tensor(lens, dtype=torch.int32)
+    else:
+        nq_seq = torch.full((B,), nq, dtype=torch.int32)
+        seq_len = torch.full((B,), N, dtype=torch.int32)
+    return table, Kpool, Vpool, seq_len, nq_seq

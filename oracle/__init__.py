@@ -237,3 +237,48 @@ def select_top(scores, cand, k: int):
         for t, p in enumerate(idx[:k]):
             out[b, t] = p
     return out
+
+
+def step_paged(shape: Shape, X, Q_idx, pos_ids, nq_seq, vis, W, Kpool, Vpool, table, block_size: int, seq_len,
+               round_mode: int):
+    """The step over a paged cache with per-sequence lengths and query counts,
+    by its definition: sequence b's cache is the rows p < seq_len[b] gathered
+    from its blocks (position p in block table[b, p // block_size], row
+    p % block_size of pools [blocks, Hkv, block_size, dh]); its live query
+    rows are j < nq_seq[b]; ``step`` runs on that flat cache alone and the
+    written rows go back to their blocks.  Padding rows get O = 0, LSE = -inf.
+    Returns dict with O, LSE and the updated pools (copies)."""
+    X = _f64(X)
+    Qi, Pi = _i32(Q_idx), _i32(pos_ids)
+    B, nq = Qi.shape
+    Kp = _f64(Kpool).copy()
+    Vp = _f64(Vpool).copy()
+    tab = _i32(table)
+    L = _i32(seq_len) if seq_len is not None else np.full(B, shape.N, dtype=np.int32)
+    nb = _i32(nq_seq) if nq_seq is not None else np.full(B, nq, dtype=np.int32)
+    vis_a = None
+    if vis is not None:
+        try:
+            import torch
+            if isinstance(vis, torch.Tensor):
+                vis = vis.detach().cpu().numpy()
+        except ImportError:  # pragma: no cover
+            pass
+        vis_a = np.asarray(vis, dtype=np.uint8)
+    O = np.zeros((B, nq, shape.H, shape.dh))
+    LSE = np.full((B, nq, shape.H), -np.inf)
+    for b in range(B):
+        Lb, n = int(L[b]), int(nb[b])
+        blk = np.array([tab[b, p // block_size] for p in range(Lb)], dtype=np.int64)
+        row = np.arange(Lb) % block_size
+        Kb = Kp[blk, :, row, :].transpose(1, 0, 2)[None]        # [1, Hkv, Lb, dh]
+        Vb = Vp[blk, :, row, :].transpose(1, 0, 2)[None]
+        if n > 0:
+            sh = Shape(1, Lb, shape.d_model, shape.H, shape.Hkv, shape.dh, shape.rope_base)
+            vb = None if vis_a is None else vis_a[b:b + 1, :n, :n]
+            r = step(sh, X[b:b + 1], Qi[b:b + 1, :n], Pi[b:b + 1, :n], vb, W, Kb, Vb, round_mode)
+            O[b, :n], LSE[b, :n] = r["O"][0], r["LSE"][0]
+            Kb, Vb = r["Kc"], r["Vc"]
+        Kp[blk, :, row, :] = Kb[0].transpose(1, 0, 2)
+        Vp[blk, :, row, :] = Vb[0].transpose(1, 0, 2)
+    return {"O": O, "LSE": LSE, "Kpool": Kp, "Vpool": Vp}

@@ -490,3 +490,65 @@ def test_select_top_by_hand():
     cand2 = np.array([[1, 0, 1, 0, 0], [0, 0, 0, 0, 0]], dtype=np.uint8)
     assert oracle.select_top(sc, cand2, 3).tolist() == [[2, 0, -1], [-1, -1, -1]]
     assert oracle.select_top(sc, cand, 0).shape == (2, 0)
+
+
+# --------------------------------------------------------------------------
+# paged cache and ragged sequences (serving variant)
+# --------------------------------------------------------------------------
+
+def test_paged_step_equals_flat_step_and_moves_rows_with_the_table():
+    """Full lengths and row counts: the paged step is the flat step with the
+    cache rows found through the table; the pool rows it writes are the flat
+    step's rows at their blocks, every other pool row is untouched."""
+    from io_aware_kv_amd.workloads import initial_cache, paged_layout
+    ls = LayerShape(B=2, N=40, d_model=16, H=4, Hkv=2, dh=8, dtype=torch.float32)
+    wl = make_random_case(ls, nq=6, seed=51, n_extra_rows=2, dup_frac=0.3, masked_vis=True, w_std=0.5)
+    sh = _shape(ls)
+    table, Kp, Vp, L, nb = paged_layout(wl, block_size=16, ragged=False)
+    K0, V0 = initial_cache(wl)
+    flat = oracle.step(sh, wl.X, wl.Q_idx, wl.pos_ids, wl.vis, wl.W, K0, V0, ROUND_FP32)
+    pg = oracle.step_paged(sh, wl.X, wl.Q_idx, wl.pos_ids, nb, wl.vis, wl.W, Kp, Vp, table, 16, L, ROUND_FP32)
+    np.testing.assert_array_equal(pg["O"], flat["O"])
+    np.testing.assert_array_equal(pg["LSE"], flat["LSE"])
+    Kp0 = Kp.double().numpy()
+    used = np.zeros(Kp0.shape[0], dtype=bool)
+    for b in range(ls.B):
+        for p in range(ls.N):
+            blk, row = int(table[b, p // 16]), p % 16
+            used[blk] = True
+            np.testing.assert_array_equal(pg["Kpool"][blk, :, row], flat["Kc"][b, :, p])
+    np.testing.assert_array_equal(pg["Kpool"][~used], Kp0[~used])
+
+
+def test_ragged_rows_are_padding_and_short_sequences_see_only_their_keys():
+    """A sequence with fewer rows and a shorter length is the same step run
+    on its live rows over its first seq_len positions; padding rows give
+    zero output and -inf LSE."""
+    from io_aware_kv_amd.workloads import initial_cache
+    ls = LayerShape(B=2, N=40, d_model=16, H=4, Hkv=2, dh=8, dtype=torch.float32)
+    wl = make_random_case(ls, nq=6, seed=52, w_std=0.5, positions=[[3, 9, 1, 30, 31, 39], [5, 6, 7, 8, 0, 2]])
+    sh = _shape(ls)
+    K0, V0 = initial_cache(wl)
+    table = torch.arange(2 * 3, dtype=torch.int32).reshape(2, 3)
+    Kp = torch.zeros((6, 2, 16, 8))
+    Vp = torch.zeros((6, 2, 16, 8))
+    for b in range(2):
+        for k in range(3):
+            n = min(16, 40 - 16 * k)
+            Kp[3 * b + k, :, :n] = K0[b, :, 16 * k:16 * k + n]
+            Vp[3 * b + k, :, :n] = V0[b, :, 16 * k:16 * k + n]
+    L = torch.tensor([40, 12], dtype=torch.int32)
+    nb = torch.tensor([6, 4], dtype=torch.int32)
+    pg = oracle.step_paged(sh, wl.X, wl.Q_idx, wl.pos_ids, nb, None, wl.W, Kp, Vp, table, 16, L, ROUND_EXACT)
+    # sequence 1 alone: 4 rows over 12 positions
+    sh1 = Shape(1, 12, ls.d_model, ls.H, ls.Hkv, ls.dh, ls.rope_base)
+    r1 = oracle.step(sh1, wl.X[1:2], wl.Q_idx[1:2, :4], wl.pos_ids[1:2, :4], None, wl.W, K0[1:2, :, :12],
+                     V0[1:2, :, :12], ROUND_EXACT)
+    np.testing.assert_allclose(pg["O"][1, :4], r1["O"][0], rtol=0, atol=0)
+    assert np.all(pg["O"][1, 4:] == 0) and np.all(np.isneginf(pg["LSE"][1, 4:]))
+    # the short sequence's keys stop at 12: positions 12.. of its cache are unused
+    q, k, v = _proj_reference(ls, wl.X[1:2], wl.Q_idx[1:2, :4], wl.pos_ids[1:2, :4], wl.W)
+    O, Lr = _attn_reference(LayerShape(B=1, N=12, d_model=16, H=4, Hkv=2, dh=8, dtype=torch.float32), q, k, v,
+                            wl.pos_ids[1:2, :4], None, K0[1:2, :, :12].double().numpy(),
+                            V0[1:2, :, :12].double().numpy())
+    np.testing.assert_allclose(pg["LSE"][1, :4], Lr[0], atol=1e-11, rtol=0)
