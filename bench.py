@@ -229,6 +229,41 @@ def time_decision(wl, stream, iters):
             "confidence_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
+def time_paged(fk, wl, stream, iters, block_size=16):
+    """Time the fused step over a paged cache (blocks of 16 positions in a
+    seeded random order, full lengths and row counts) on two pool sets."""
+    import torch
+    from io_aware_kv_amd.workloads import paged_layout
+    ls = wl.shape
+    dev = torch.device("cuda")
+    table, Kpool, Vpool, L, nb = paged_layout(wl, block_size, ragged=False)
+    sets = []
+    for _ in range(2):
+        sets.append(dict(K=Kpool.to(dev), V=Vpool.to(dev),
+                         O=torch.empty((ls.B, wl.nq, ls.H, ls.dh), dtype=ls.dtype, device=dev),
+                         LSE=torch.empty((ls.B, wl.nq, ls.H), dtype=torch.float32, device=dev)))
+    X, W = wl.X.to(dev), wl.W.to(dev)
+    Q, P = wl.Q_idx.to(dev), wl.pos_ids.to(dev)
+    vis = wl.vis.to(dev) if wl.vis is not None else None
+    tab, Ld, nbd = table.to(dev), L.to(dev), nb.to(dev)
+
+    def run(i):
+        st = sets[i % 2]
+        fk.step_paged(X, Q, P, vis, W, st["K"], st["V"], st["O"], st["LSE"], block_table=tab,
+                      block_size=block_size, num_blocks=Kpool.shape[0], seq_len=Ld, nq_seq=nbd, stream=stream)
+
+    for i in range(3):
+        run(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(iters):
+        run(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return {"block_size": block_size, "step_us": round(e0.elapsed_time(e1) / iters * 1e3, 3)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -237,7 +272,8 @@ def main():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--sets", type=int, default=0, help="buffer sets in rotation (0: auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
-    ap.add_argument("--no-select", action="store_true", help="skip timing the tracked-set selection")
+    ap.add_argument("--no-select", action="store_true",
+                    help="skip timing the steps after the path (selection, decisions) and the paged variant")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--attn-splits", type=int, default=0)
     ap.add_argument("--gemm-splitk", type=int, default=0)
@@ -305,17 +341,24 @@ def main():
     torch.cuda.synchronize()
     log("bench: warmup done, timing %d steps" % args.steps)
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # the timed steps run back to back with nothing between the launches
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record(stream)
     for i in range(args.steps):
-        step(sets[i % n_sets], evs[i])
+        step(sets[i % n_sets])
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(end) / args.steps
+    # phase times from a second pass with an event around each launch (the
+    # events add a small gap between the launches, so they stay out of the
+    # timed steps above)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(sets[i % n_sets], evs[i])
+    torch.cuda.synchronize()
     proj_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
     attn_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
     proj_avg = sum(proj_ms) / len(proj_ms)
@@ -344,6 +387,9 @@ def main():
             (decision["rows"], decision["vocab"], decision["confidence_us"], decision["confidence_GBps"],
              decision["accept_us"]))
         selection["decision"] = decision
+        paged = time_paged(fk, wl, stream, min(args.steps, 50))
+        log("bench: paged cache (blocks of %d) step %.2f us" % (paged["block_size"], paged["step_us"]))
+        selection["paged_step"] = paged
 
     # dominant kernel roofline
     dom = "attn" if attn_avg >= proj_avg else "proj"
@@ -404,7 +450,7 @@ def main():
             "attn_hbm_frac": round(ab["attn"] / (attn_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         },
         "algorithmic_bytes_per_step": ab["total"],
-        "tracked_set_selection": selection,
+        "next_rows": selection,
         "roofline": roofline,
         "cpu_baseline": None,
     }

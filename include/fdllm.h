@@ -135,6 +135,33 @@ int fdllm_step_project(fdllm_handle_t h, const void* X, int32_t x_rows, const in
 int fdllm_step_attend(fdllm_handle_t h, const int32_t* pos_ids, int32_t nq, const uint8_t* vis_mask,
                       const void* Kc, const void* Vc, void* O, float* LSE, void* stream);
 
+/* The fused step over a paged cache, with per-sequence valid lengths and
+ * query counts, for batched serving (jaehun.me review, "System-Level
+ * Metrics": throughput grows with the batch; "What's Next?: Future
+ * Directions": a block table under a paged serving stack).  Same step and conventions as
+ * fdllm_fused_step, except:
+ *   - block_table != NULL: Kpool/Vpool are pools of blocks
+ *     [num_blocks, Hkv, block_size, dh]; position p of sequence b lives in
+ *     block block_table[b * max_blocks + p / block_size], row p % block_size.
+ *     block_size is a power of two in [16, 1024].  block_table == NULL: the
+ *     flat layout [B, Hkv, N, dh] (block_size, max_blocks, num_blocks unused).
+ *   - seq_len [B] (or NULL = N for all): sequence b has positions
+ *     0 .. seq_len[b]-1 (1 <= seq_len[b] <= N and <= max_blocks * block_size);
+ *     keys past it are not attended, and every position the step writes must
+ *     be below it.
+ *   - nq_seq [B] (or NULL = nq for all): rows j >= nq_seq[b] of sequence b
+ *     are padding: their Q_idx/pos_ids are ignored, nothing is written for
+ *     them, they are no keys, and their O rows are 0 and LSE rows -inf.
+ * Table entries of blocks past a sequence's length are not read.
+ * FDLLM_VALIDATE=1 checks lengths, indices of the live rows and the used
+ * table entries (< num_blocks) on the host.
+ * Statuses: ARG, SHAPE, ALIGN, INDEX (FDLLM_VALIDATE=1 only), HIP. */
+int fdllm_fused_step_paged(fdllm_handle_t h, const void* X, int32_t x_rows, const int32_t* Q_idx,
+                           const int32_t* pos_ids, int32_t nq, const int32_t* nq_seq, const uint8_t* vis_mask,
+                           const void* W_qkv, void* Kpool, void* Vpool, const int32_t* block_table,
+                           int32_t block_size, int32_t max_blocks, int32_t num_blocks, const int32_t* seq_len,
+                           void* O, float* LSE, void* stream);
+
 /* Tracked-set scores, the step after the fused step (jaehun.me review, "How
  * It Works: A Concrete Example", Step 1: Cache selection, with the paragraph
  * on Fig. 1b): the previously decoded tokens most attended by the masked

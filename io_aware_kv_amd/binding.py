@@ -64,6 +64,7 @@ def load():
     lib.fdllm_fused_step.argtypes = [P, P, i32, P, P, i32, P, P, P, P, P, P, P]
     lib.fdllm_step_project.argtypes = [P, P, i32, P, P, i32, P, P, P, P]
     lib.fdllm_step_attend.argtypes = [P, P, i32, P, P, P, P, P, P]
+    lib.fdllm_fused_step_paged.argtypes = [P, P, i32, P, P, i32, P, P, P, P, P, P, i32, i32, i32, P, P, P, P]
     lib.fdllm_tracked_scores.argtypes = [P, P, i32, P, P, P, P, P, P]
     lib.fdllm_select_tracked.argtypes = [P, P, P, i32, P, P]
     lib.fdllm_confidence.argtypes = [P, i32, ctypes.c_int64, i32, i32, ctypes.c_float, P, P, P, P]
@@ -75,7 +76,7 @@ def load():
     lib.fdllm_status_str.restype = ctypes.c_char_p
     for name in ("fdllm_validate_config", "fdllm_cache_init", "fdllm_prefill", "fdllm_fused_step",
                  "fdllm_step_project", "fdllm_step_attend", "fdllm_tracked_scores", "fdllm_select_tracked",
-                 "fdllm_confidence", "fdllm_accept",
+                 "fdllm_confidence", "fdllm_accept", "fdllm_fused_step_paged",
                  "fdllm_set_tuning", "fdllm_get_plan", "fdllm_cache_destroy"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
@@ -206,6 +207,30 @@ class FusedKVCache:
                                      _ptr(vis), _ptr(W), _ptr(Kc), _ptr(Vc), _ptr(O), _ptr(LSE),
                                      _stream(stream))
         _check(rc, "fdllm_fused_step")
+
+    def step_paged(self, X, Q_idx, pos_ids, vis, W, Kpool, Vpool, O, LSE, block_table=None, block_size=0,
+                   num_blocks=0, seq_len=None, nq_seq=None, stream=None):
+        """The fused step over a paged cache (block_table [B, max_blocks]
+        int32, pools [num_blocks, Hkv, block_size, dh]) or the flat layout
+        (block_table None), with optional seq_len [B] and nq_seq [B] int32."""
+        c = self.cfg
+        nq = Q_idx.shape[1]
+        for name, t in (("seq_len", seq_len), ("nq_seq", nq_seq)):
+            if t is not None and (t.dtype != torch.int32 or tuple(t.shape) != (c.B,)):
+                raise ValueError("%s must be int32 [B]" % name)
+        max_blocks = 0
+        if block_table is not None:
+            if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != c.B:
+                raise ValueError("block_table must be int32 [B, max_blocks]")
+            max_blocks = block_table.shape[1]
+            for t in (Kpool, Vpool):
+                if tuple(t.shape) != (num_blocks, c.Hkv, block_size, c.dh) or t.dtype != self.dtype:
+                    raise ValueError("pools must be [num_blocks, Hkv, block_size, dh] of the layer dtype")
+        rc = load().fdllm_fused_step_paged(self._h, _ptr(X), X.shape[1], _ptr(Q_idx), _ptr(pos_ids), nq,
+                                           _ptr(nq_seq), _ptr(vis), _ptr(W), _ptr(Kpool), _ptr(Vpool),
+                                           _ptr(block_table), block_size, max_blocks, num_blocks, _ptr(seq_len),
+                                           _ptr(O), _ptr(LSE), _stream(stream))
+        _check(rc, "fdllm_fused_step_paged")
 
     def project(self, X, Q_idx, pos_ids, W, Kc, Vc, stream=None):
         """First launch of the step (gather, projection, rotary, k/v write)."""

@@ -136,17 +136,26 @@ __device__ __forceinline__ bf16x8 read_vt_frag(const unsigned char* p0, const un
 // repeat its last key and are masked later), K then V, as 1 KB DMA blocks of
 // 4 rows; chunk c of row r lands in slot c ^ (r & 15).  Producer p issues
 // blocks p, p + NPROD, ...
+// Cache row of key `key` in bytes: the (sequence, kv head) slab of the flat
+// layout, or through the block table staged in LDS (sTab != NULL).
+__device__ __forceinline__ size_t key_offset(int key, const int* sTab, int bits, int Hkv, int g)
+{
+    if (!sTab) return (size_t)key * kRowB;
+    return (((((size_t)sTab[key >> bits] * Hkv + g) << bits) + (key & ((1 << bits) - 1)))) * kRowB;
+}
+
 template <int TK, int DMA, int NPROD>
-__device__ __forceinline__ void issue_main(unsigned char* st, int base, int k1, const unsigned char* Kg,
-                                           const unsigned char* Vg, int p, int lane)
+__device__ __forceinline__ void issue_main(unsigned char* st, int base, int klast, const unsigned char* Kg,
+                                           const unsigned char* Vg, int p, int lane, const int* sTab, int bits,
+                                           int Hkv, int g)
 {
     const int srow = lane >> 4, slot = lane & 15;
 #pragma unroll
     for (int ii = 0; ii < DMA / 2 / NPROD; ++ii) {
         const int i = ii * NPROD + p;
         const int row = 4 * i + srow;
-        const int key = min(base + row, k1 - 1);
-        const size_t src = (size_t)key * kRowB + ((slot ^ (row & 15)) << 4);
+        const int key = min(base + row, klast);
+        const size_t src = key_offset(key, sTab, bits, Hkv, g) + ((slot ^ (row & 15)) << 4);
         dma16(Kg + src, st + i * 1024);
         dma16(Vg + src, st + TK * kRowB + i * 1024);
     }
@@ -186,6 +195,7 @@ attn_mfma_kernel(AttnArgs a)
     uint32_t* sVis = sMask + 2 * tiles_max;         // [nq][VW] visibility bits
     int* sDup = (int*)(sVis + (size_t)nq * VW);     // [nq] rows that do not own their position
     int* sMisc = sDup + nq;                         // [0] number of such rows
+    int* sTabLds = sMisc + 1;                       // [max_blocks] block table of the sequence (paged)
 
     const int total = a.B * a.Hkv * a.splits;
     const int logical = xcd_remap(blockIdx.x, total);
@@ -194,9 +204,17 @@ attn_mfma_kernel(AttnArgs a)
     const int split = logical - bg * a.splits;
     const int b = bg / a.Hkv;
     const int g = bg - b * a.Hkv;
+    // valid positions and query rows of this sequence (all N and nq unless
+    // the caller passes per-sequence lengths); a split past the valid
+    // positions streams one masked tile of valid rows
+    const int L = a.seq_len ? min(a.seq_len[b], a.N) : a.N;
+    const int nqb = a.nq_seq ? a.nq_seq[b] : nq;
     const int k0 = split * kps;
-    const int k1 = min(a.N, k0 + kps);
-    const int n_main = (k1 - k0 + C::TK - 1) / C::TK;
+    const int k1 = min(L, k0 + kps);
+    const int klast = k1 > k0 ? k1 - 1 : L - 1;
+    const int n_main = k1 > k0 ? (k1 - k0 + C::TK - 1) / C::TK : 1;
+    const bool paged = a.map.table != nullptr;
+    const int* sTab = paged ? sTabLds : nullptr;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -207,7 +225,7 @@ attn_mfma_kernel(AttnArgs a)
     const int wk = wave % NWK, wr = wave / NWK;    // consumer coordinates
     const int nch = (nq + 63) >> 6;                 // 64-row chunks of the query set
 
-    const size_t cache_off = (size_t)bg * a.N * kDH;
+    const size_t cache_off = paged ? 0 : (size_t)bg * a.N * kDH;
     const unsigned char* Kg = (const unsigned char*)((const bf16*)a.Kc + cache_off);
     const unsigned char* Vg = (const unsigned char*)((const bf16*)a.Vc + cache_off);
     const unsigned char* SKg = (const unsigned char*)((const bf16*)a.sideK + (size_t)bg * a.q_max * kDH);
@@ -251,6 +269,10 @@ attn_mfma_kernel(AttnArgs a)
             for (int k = tid; k < kps; k += C::NC * 64) sSlot[k] = -1;
             for (int t = tid; t < 2 * n_main; t += C::NC * 64) sMask[t] = 0u;
         }
+        if (paged) {
+            const int32_t* tb = a.map.table + (size_t)b * a.map.max_blocks;
+            for (int t = tid; t < a.map.max_blocks; t += C::NC * 64) sTabLds[t] = tb[t];
+        }
     }
     // a plain barrier: the LDS writes above must land, but the loads stay in
     // flight (a full __syncthreads would wait for them before the stream starts)
@@ -271,7 +293,8 @@ attn_mfma_kernel(AttnArgs a)
         const int p = wave - C::NC;
         int issued = 0;
         for (; issued < min(C::NS - 1, n_main); ++issued)
-            issue_main<C::TK, C::DMA, NPROD>(smem + (issued % C::NS) * C::STAGE, k0 + issued * C::TK, k1, Kg, Vg, p, lane);
+            issue_main<C::TK, C::DMA, NPROD>(smem + (issued % C::NS) * C::STAGE, k0 + issued * C::TK, klast, Kg, Vg, p,
+                                             lane, sTab, a.map.bits, a.Hkv, g);
         int ntot = n_main;
         int ndup = 0;
         for (int t = 0;; ++t) {
@@ -285,7 +308,8 @@ attn_mfma_kernel(AttnArgs a)
             for (; issued < ntot && issued < t + C::NS; ++issued) {
                 unsigned char* st = smem + (issued % C::NS) * C::STAGE;
                 if (issued < n_main)
-                    issue_main<C::TK, C::DMA, NPROD>(st, k0 + issued * C::TK, k1, Kg, Vg, p, lane);
+                    issue_main<C::TK, C::DMA, NPROD>(st, k0 + issued * C::TK, klast, Kg, Vg, p, lane, sTab,
+                                                     a.map.bits, a.Hkv, g);
                 else
                     issue_dup<C::TK, C::DMA, NPROD>(st, (issued - n_main) * C::TK, ndup, sDup, SKg, SVg, p, lane);
             }
@@ -301,7 +325,7 @@ attn_mfma_kernel(AttnArgs a)
             for (int c = 0; c < kMaxChunks; ++c) {
                 if (64 * c >= nq) break;
                 const int j = 64 * c + lane;
-                if (j >= nq) posr[c] = -1;   // padding lanes (their load repeated the last row)
+                if (j >= nqb) posr[c] = -1;  // padding lanes and rows (their load repeated the last row)
                 bool own = true;
 #pragma unroll
                 for (int cq = 0; cq <= c; ++cq) {
@@ -311,7 +335,7 @@ attn_mfma_kernel(AttnArgs a)
                         own = own && !(pq == posr[c] && 64 * cq + t < j);
                     }
                 }
-                const bool valid = j < nq;
+                const bool valid = j < nqb;
                 const uint64_t dm = __builtin_amdgcn_ballot_w64(valid && !own);
                 const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(dm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)dm, 0u));
                 if (valid && !own) sDup[ndup + below] = j;
@@ -404,7 +428,7 @@ attn_mfma_kernel(AttnArgs a)
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
             const int row = (wr * RG + rg) * 16 + lr;
-            qrow[rg] = row < a.R ? row / G : -1;
+            qrow[rg] = (row < a.R && row / G < nqb) ? row / G : -1;
 #pragma unroll
             for (int c = 0; c < 4; ++c)
 #pragma unroll
@@ -493,7 +517,7 @@ attn_mfma_kernel(AttnArgs a)
 #pragma unroll
                             for (int i = 0; i < 4; ++i) {
                                 const int key = tbase + wk * C::KW + kb * 16 + lg * 4 + i;
-                                const int kk = min(key, kend - 1);
+                                const int kk = max(min(key, kend - 1), dup ? 0 : k0);
                                 const int j = dup ? sDup[kk] : (int)sSlot[kk - k0];
                                 jk[kb][i] = key < kend ? j : -2;      // -2: past the end
                             }
@@ -652,6 +676,11 @@ attn_mfma_kernel(AttnArgs a)
                 if (row >= a.R) continue;
                 const int j = row / G, hl = row - j * G;
                 const size_t orow = ((size_t)b * nq + j) * a.H + g * G + hl;
+                if (j >= nqb) {   // padding row of a shorter sequence: zero output
+                    l_run[rg] = 0.f;
+#pragma unroll
+                    for (int db = 0; db < 8; ++db) o[rg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
                 const float inv = l_run[rg] > 0.f ? 1.f / l_run[rg] : 0.f;
                 bf16* op = (bf16*)a.O + orow * kDH;
 #pragma unroll
@@ -747,6 +776,10 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a)
     if (row >= a.R) return;
     const int b = bg / a.Hkv, g = bg - b * a.Hkv;
     const int j = row / a.G, hl = row - j * a.G;
+    if (a.nq_seq && j >= a.nq_seq[b]) {     // padding row of a shorter sequence
+        acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        L = 0.f;
+    }
     const size_t orow = ((size_t)b * a.nq + j) * a.H + g * a.G + hl;
     const float inv = L > 0.f ? 1.f / L : 0.f;
     bf16x4v v;
@@ -764,7 +797,7 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s)
     const int VW = (a.nq + 31) / 32;
     const int tiles = (a.keys_per_split + C::TK - 1) / C::TK;
     const size_t book = 2 * (size_t)((a.keys_per_split + 1) & ~1) + 8 * (size_t)tiles + 4 * (size_t)a.nq * VW +
-                        4 * ((size_t)a.nq + 1);
+                        4 * ((size_t)a.nq + 1) + (a.map.table ? 4 * (size_t)a.map.max_blocks : 0);
     if (C::SCRATCH + book > 160 * 1024) return hipErrorInvalidValue;
     const size_t shm = C::SCRATCH + book;
     const int total = a.B * a.Hkv * a.splits;

@@ -177,6 +177,78 @@ ProjArgs proj_args(const fdllm_ctx* h, const void* X, int x_rows, const int32_t*
 
 }  // namespace
 
+namespace {
+
+// The projection launch of a step, for the flat or the paged layout, with
+// optional per-sequence query counts.
+int project_impl(fdllm_ctx* h, const void* X, int32_t x_rows, const int32_t* Q_idx, const int32_t* pos_ids,
+                 int32_t nq, const void* W, void* Kc, void* Vc, const CacheMap& map, const int32_t* nq_seq,
+                 void* stream, bool validated = false)
+{
+    if (!h) return FDLLM_ERR_ARG;
+    const fdllm_config_t& c = h->cfg;
+    if (nq < 0 || nq > c.q_max || x_rows < 1) return FDLLM_ERR_SHAPE;
+    if (nq == 0) return FDLLM_OK;
+    if (!X || !Q_idx || !pos_ids || !W || !Kc || !Vc) return FDLLM_ERR_ARG;
+    if (!aligned16(X) || !aligned16(W) || !aligned16(Kc) || !aligned16(Vc) ||
+        (reinterpret_cast<uintptr_t>(Q_idx) & 3u) || (reinterpret_cast<uintptr_t>(pos_ids) & 3u))
+        return FDLLM_ERR_ALIGN;
+    int st = set_device(h);
+    if (st) return st;
+    hipStream_t s = (hipStream_t)stream;
+    if (!validated && env_int("FDLLM_VALIDATE", 0)) {
+        std::vector<int32_t> qi((size_t)c.B * nq), pi((size_t)c.B * nq);
+        if (hipMemcpyAsync(qi.data(), Q_idx, qi.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipMemcpyAsync(pi.data(), pos_ids, pi.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
+            hipStreamSynchronize(s) != hipSuccess)
+            return FDLLM_ERR_HIP;
+        for (size_t t = 0; t < qi.size(); ++t)
+            if (qi[t] < 0 || qi[t] >= x_rows || pi[t] < 0 || pi[t] >= c.N) return FDLLM_ERR_INDEX;
+    }
+    const Plan p = make_plan(h, nq);
+    ProjArgs pa = proj_args(h, X, x_rows, Q_idx, pos_ids, nq, W, Kc, Vc, 0, p.splitk);
+    pa.map = map;
+    pa.nq_seq = nq_seq;
+    hipError_t e = p.proj_family == FAMILY_MFMA ? launch_proj_mfma(pa, s) : launch_proj_generic(pa, c.dtype, s);
+    return hip_status(e);
+}
+
+// The attention launch(es) of a step, for the flat or the paged layout, with
+// optional per-sequence valid lengths and query counts.
+int attend_impl(fdllm_ctx* h, const int32_t* pos_ids, int32_t nq, const uint8_t* vis, const void* Kc,
+                const void* Vc, void* O, float* LSE, const CacheMap& map, const int32_t* seq_len,
+                const int32_t* nq_seq, void* stream)
+{
+    if (!h) return FDLLM_ERR_ARG;
+    const fdllm_config_t& c = h->cfg;
+    if (nq < 0 || nq > c.q_max) return FDLLM_ERR_SHAPE;
+    if (nq == 0) return FDLLM_OK;
+    if (!pos_ids || !Kc || !Vc || !O || !LSE) return FDLLM_ERR_ARG;
+    if (!aligned16(Kc) || !aligned16(Vc) || !aligned16(O) || (reinterpret_cast<uintptr_t>(LSE) & 3u) ||
+        (reinterpret_cast<uintptr_t>(pos_ids) & 3u))
+        return FDLLM_ERR_ALIGN;
+    int st = set_device(h);
+    if (st) return st;
+    hipStream_t s = (hipStream_t)stream;
+    const Plan p = make_plan(h, nq);
+    if (p.attn_family == FAMILY_MFMA && p.splits > 1 && (size_t)c.B * c.Hkv * p.splits * p.Rpad > h->apart_rows)
+        return FDLLM_ERR_ALLOC;   // not reached: the workspace is sized for every nq
+    AttnArgs aa{};
+    aa.qbuf = h->qbuf; aa.Kc = Kc; aa.Vc = Vc; aa.sideK = h->sideK; aa.sideV = h->sideV;
+    aa.pos_ids = pos_ids; aa.vis = vis; aa.O = O; aa.LSE = LSE;
+    aa.apart = h->apart; aa.aml = h->aml; aa.aticket = h->aticket;
+    aa.B = c.B; aa.N = c.N; aa.H = c.H; aa.Hkv = c.Hkv; aa.dh = c.dh; aa.G = h->G; aa.nq = nq; aa.q_max = c.q_max;
+    aa.R = p.R; aa.Rpad = p.Rpad; aa.splits = p.splits; aa.keys_per_split = p.keys_per_split;
+    aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.dh));
+    aa.map = map;
+    aa.seq_len = seq_len;
+    aa.nq_seq = nq_seq;
+    hipError_t e = p.attn_family == FAMILY_MFMA ? launch_attn_mfma(aa, s) : launch_attn_generic(aa, c.dtype, s);
+    return hip_status(e);
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* fdllm_status_str(int status)
@@ -302,58 +374,69 @@ int fdllm_get_plan(fdllm_handle_t h, int32_t nq, int32_t* attn_splits, int32_t* 
 int fdllm_step_project(fdllm_handle_t h, const void* X, int32_t x_rows, const int32_t* Q_idx,
                        const int32_t* pos_ids, int32_t nq, const void* W, void* Kc, void* Vc, void* stream)
 {
-    if (!h) return FDLLM_ERR_ARG;
-    const fdllm_config_t& c = h->cfg;
-    if (nq < 0 || nq > c.q_max || x_rows < 1) return FDLLM_ERR_SHAPE;
-    if (nq == 0) return FDLLM_OK;
-    if (!X || !Q_idx || !pos_ids || !W || !Kc || !Vc) return FDLLM_ERR_ARG;
-    if (!aligned16(X) || !aligned16(W) || !aligned16(Kc) || !aligned16(Vc) ||
-        (reinterpret_cast<uintptr_t>(Q_idx) & 3u) || (reinterpret_cast<uintptr_t>(pos_ids) & 3u))
-        return FDLLM_ERR_ALIGN;
-    int st = set_device(h);
-    if (st) return st;
-    hipStream_t s = (hipStream_t)stream;
-    if (env_int("FDLLM_VALIDATE", 0)) {
-        std::vector<int32_t> qi((size_t)c.B * nq), pi((size_t)c.B * nq);
-        if (hipMemcpyAsync(qi.data(), Q_idx, qi.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
-            hipMemcpyAsync(pi.data(), pos_ids, pi.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
-            hipStreamSynchronize(s) != hipSuccess)
-            return FDLLM_ERR_HIP;
-        for (size_t t = 0; t < qi.size(); ++t)
-            if (qi[t] < 0 || qi[t] >= x_rows || pi[t] < 0 || pi[t] >= c.N) return FDLLM_ERR_INDEX;
-    }
-    const Plan p = make_plan(h, nq);
-    ProjArgs pa = proj_args(h, X, x_rows, Q_idx, pos_ids, nq, W, Kc, Vc, 0, p.splitk);
-    hipError_t e = p.proj_family == FAMILY_MFMA ? launch_proj_mfma(pa, s) : launch_proj_generic(pa, c.dtype, s);
-    return hip_status(e);
+    return project_impl(h, X, x_rows, Q_idx, pos_ids, nq, W, Kc, Vc, CacheMap{nullptr, 0, 0}, nullptr, stream);
 }
 
 int fdllm_step_attend(fdllm_handle_t h, const int32_t* pos_ids, int32_t nq, const uint8_t* vis,
                       const void* Kc, const void* Vc, void* O, float* LSE, void* stream)
 {
+    return attend_impl(h, pos_ids, nq, vis, Kc, Vc, O, LSE, CacheMap{nullptr, 0, 0}, nullptr, nullptr, stream);
+}
+
+int fdllm_fused_step_paged(fdllm_handle_t h, const void* X, int32_t x_rows, const int32_t* Q_idx,
+                           const int32_t* pos_ids, int32_t nq, const int32_t* nq_seq, const uint8_t* vis,
+                           const void* W, void* Kpool, void* Vpool, const int32_t* block_table,
+                           int32_t block_size, int32_t max_blocks, int32_t num_blocks, const int32_t* seq_len,
+                           void* O, float* LSE, void* stream)
+{
     if (!h) return FDLLM_ERR_ARG;
     const fdllm_config_t& c = h->cfg;
-    if (nq < 0 || nq > c.q_max) return FDLLM_ERR_SHAPE;
+    if (nq < 0 || nq > c.q_max || x_rows < 1) return FDLLM_ERR_SHAPE;
     if (nq == 0) return FDLLM_OK;
-    if (!pos_ids || !Kc || !Vc || !O || !LSE) return FDLLM_ERR_ARG;
-    if (!aligned16(Kc) || !aligned16(Vc) || !aligned16(O) || (reinterpret_cast<uintptr_t>(LSE) & 3u) ||
-        (reinterpret_cast<uintptr_t>(pos_ids) & 3u))
-        return FDLLM_ERR_ALIGN;
+    if (!X || !Q_idx || !pos_ids || !W || !Kpool || !Vpool || !O || !LSE) return FDLLM_ERR_ARG;
+    if (!aligned16(O) || (reinterpret_cast<uintptr_t>(LSE) & 3u)) return FDLLM_ERR_ALIGN;
+    CacheMap map{nullptr, 0, 0};
+    if (block_table) {
+        int bits = 0;
+        while ((1 << bits) < block_size && bits < 11) ++bits;
+        if (block_size < 16 || block_size > 1024 || (1 << bits) != block_size || max_blocks < 1 || num_blocks < 1)
+            return FDLLM_ERR_ARG;
+        if ((int64_t)max_blocks * block_size < 1) return FDLLM_ERR_ARG;
+        if (reinterpret_cast<uintptr_t>(block_table) & 3u) return FDLLM_ERR_ALIGN;
+        map = CacheMap{block_table, bits, max_blocks};
+    }
     int st = set_device(h);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    const Plan p = make_plan(h, nq);
-    if (p.attn_family == FAMILY_MFMA && p.splits > 1 && (size_t)c.B * c.Hkv * p.splits * p.Rpad > h->apart_rows)
-        return FDLLM_ERR_ALLOC;   // not reached: the workspace is sized for every nq
-    AttnArgs aa{};
-    aa.qbuf = h->qbuf; aa.Kc = Kc; aa.Vc = Vc; aa.sideK = h->sideK; aa.sideV = h->sideV;
-    aa.pos_ids = pos_ids; aa.vis = vis; aa.O = O; aa.LSE = LSE;
-    aa.apart = h->apart; aa.aml = h->aml; aa.aticket = h->aticket;
-    aa.B = c.B; aa.N = c.N; aa.H = c.H; aa.Hkv = c.Hkv; aa.dh = c.dh; aa.G = h->G; aa.nq = nq; aa.q_max = c.q_max;
-    aa.R = p.R; aa.Rpad = p.Rpad; aa.splits = p.splits; aa.keys_per_split = p.keys_per_split;
-    aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.dh));
-    hipError_t e = p.attn_family == FAMILY_MFMA ? launch_attn_mfma(aa, s) : launch_attn_generic(aa, c.dtype, s);
-    return hip_status(e);
+    if (env_int("FDLLM_VALIDATE", 0)) {
+        // host copies of the lengths, indices and table: every row a sequence
+        // uses must point inside its valid positions and allocated blocks
+        std::vector<int32_t> qi((size_t)c.B * nq), pi((size_t)c.B * nq), nb(c.B, nq), L(c.B, c.N);
+        std::vector<int32_t> tab(block_table ? (size_t)c.B * max_blocks : 0);
+        bool ok = hipMemcpyAsync(qi.data(), Q_idx, qi.size() * 4, hipMemcpyDeviceToHost, s) == hipSuccess &&
+                  hipMemcpyAsync(pi.data(), pos_ids, pi.size() * 4, hipMemcpyDeviceToHost, s) == hipSuccess;
+        if (ok && nq_seq) ok = hipMemcpyAsync(nb.data(), nq_seq, nb.size() * 4, hipMemcpyDeviceToHost, s) == hipSuccess;
+        if (ok && seq_len) ok = hipMemcpyAsync(L.data(), seq_len, L.size() * 4, hipMemcpyDeviceToHost, s) == hipSuccess;
+        if (ok && block_table)
+            ok = hipMemcpyAsync(tab.data(), block_table, tab.size() * 4, hipMemcpyDeviceToHost, s) == hipSuccess;
+        if (!ok || hipStreamSynchronize(s) != hipSuccess) return FDLLM_ERR_HIP;
+        for (int b = 0; b < c.B; ++b) {
+            const int cap = block_table ? std::min<int64_t>(c.N, (int64_t)max_blocks * block_size) : c.N;
+            if (nb[b] < 0 || nb[b] > nq || L[b] < 1 || L[b] > cap) return FDLLM_ERR_INDEX;
+            for (int j = 0; j < nb[b]; ++j) {
+                const size_t t = (size_t)b * nq + j;
+                if (qi[t] < 0 || qi[t] >= x_rows || pi[t] < 0 || pi[t] >= L[b]) return FDLLM_ERR_INDEX;
+            }
+            if (block_table)
+                for (int k = 0; k < (L[b] + block_size - 1) / block_size; ++k) {
+                    const int32_t e = tab[(size_t)b * max_blocks + k];
+                    if (e < 0 || e >= num_blocks) return FDLLM_ERR_INDEX;
+                }
+        }
+    }
+    st = project_impl(h, X, x_rows, Q_idx, pos_ids, nq, W, Kpool, Vpool, map, nq_seq, stream, true);
+    if (st) return st;
+    return attend_impl(h, pos_ids, nq, vis, Kpool, Vpool, O, LSE, map, seq_len, nq_seq, stream);
 }
 
 int fdllm_fused_step(fdllm_handle_t h, const void* X, int32_t x_rows, const int32_t* Q_idx,

@@ -13,6 +13,22 @@ typedef __bf16 bf16x4v __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// Where cache row (b, g, p) lives: the flat layout [B, Hkv, N, dh] when
+// table is NULL, else a pool of blocks [blocks, Hkv, 2^bits, dh] with
+// table[b * max_blocks + (p >> bits)] naming the block of position p.
+struct CacheMap {
+    const int32_t* table;
+    int bits;               // log2 of the block size
+    int max_blocks;         // table entries per sequence
+};
+
+__device__ __forceinline__ size_t cache_row(const CacheMap& c, int b, int g, int p, int Hkv, int N)
+{
+    if (!c.table) return ((size_t)b * Hkv + g) * N + p;
+    const int blk = c.table[(size_t)b * c.max_blocks + (p >> c.bits)];
+    return (((size_t)blk * Hkv + g) << c.bits) + (p & ((1 << c.bits) - 1));
+}
+
 // Everything a launch of the projection kernels needs.  Rows of the
 // projection are m = b * rows_per_seq + j.
 struct ProjArgs {
@@ -35,6 +51,8 @@ struct ProjArgs {
     int prefill;            // 1: k/v heads only, no q, no side buffer
     int splitk;
     int tile_choice;        // 0: default tile configuration for the row count
+    CacheMap map;           // cache layout (flat when map.table is NULL)
+    const int32_t* nq_seq;  // [B] query rows of each sequence (rows j >= nq_seq[b] are padding) or NULL
 };
 
 struct AttnArgs {
@@ -56,6 +74,9 @@ struct AttnArgs {
     int splits;
     int keys_per_split;     // multiple of the kernel's tile width
     float scale_log2;       // log2(e) / sqrt(dh)
+    CacheMap map;           // cache layout (flat when map.table is NULL)
+    const int32_t* seq_len; // [B] valid cache positions of each sequence (>= 1) or NULL (all N)
+    const int32_t* nq_seq;  // [B] query rows of each sequence or NULL (all nq)
 };
 
 // Tracked-set scores after a step: attention mass of the selected query rows

@@ -35,6 +35,16 @@ __global__ void __launch_bounds__(kGenThreads) proj_generic_kernel(ProjArgs a)
     const int b = m / a.rows_per_seq;
     const int j = m - b * a.rows_per_seq;
     const int head = a.prefill ? a.H + (int)blockIdx.y : (int)blockIdx.y;
+    if (!a.prefill && a.nq_seq && j >= a.nq_seq[b]) {
+        // a padding row of a shorter sequence: no cache write; its q staging
+        // row is cleared so the attention reads defined values
+        if (head < a.H) {
+            const int g = head / a.G, hl = head - g * a.G;
+            float* qz = a.qbuf + (((size_t)b * a.Hkv + g) * a.q_max * a.G + (size_t)j * a.G + hl) * a.dh;
+            for (int c = threadIdx.x; c < a.dh; c += kGenThreads) qz[c] = 0.f;
+        }
+        return;
+    }
     const int xrow = a.prefill ? j : a.Q_idx[m];
     const int pos = a.prefill ? j : a.pos_ids[m];
 
@@ -57,7 +67,7 @@ __global__ void __launch_bounds__(kGenThreads) proj_generic_kernel(ProjArgs a)
         const bool isk = head < a.H + a.Hkv;
         const int g = head - a.H - (isk ? 0 : a.Hkv);
         if (s_first)
-            dst = (T*)(isk ? a.Kc : a.Vc) + (((size_t)b * a.Hkv + g) * a.N + pos) * a.dh;
+            dst = (T*)(isk ? a.Kc : a.Vc) + cache_row(a.map, b, g, pos, a.Hkv, a.N) * a.dh;
         else
             dst = (T*)(isk ? a.sideK : a.sideV) + (((size_t)b * a.Hkv + g) * a.q_max + j) * a.dh;
     }
@@ -113,6 +123,15 @@ __global__ void __launch_bounds__(kGenThreads) attn_generic_kernel(AttnArgs a)
     const int b = bid / (a.H * a.nq);
     const int g = h / a.G, hl = h - g * a.G;
     const int t = threadIdx.x;
+    const int nqb = a.nq_seq ? a.nq_seq[b] : a.nq;     // rows of this sequence
+    const int L = a.seq_len ? a.seq_len[b] : a.N;      // its valid cache positions
+    if (i >= nqb) {
+        // padding row: no keys, zero output
+        T* oz = (T*)a.O + (((size_t)b * a.nq + i) * a.H + h) * a.dh;
+        for (int e = t; e < a.dh; e += kGenThreads) oz[e] = from_f32<T>(0.f);
+        if (t == 0) a.LSE[((size_t)b * a.nq + i) * a.H + h] = -INFINITY;
+        return;
+    }
 
     extern __shared__ float smem[];
     float* sq = smem;                       // [dh]
@@ -122,9 +141,9 @@ __global__ void __launch_bounds__(kGenThreads) attn_generic_kernel(AttnArgs a)
     int* sown = spos + a.nq;                // [nq] first row at that position
 
     const int32_t* pos_b = a.pos_ids + (size_t)b * a.nq;
-    for (int jj = t; jj < a.nq; jj += kGenThreads) spos[jj] = pos_b[jj];
+    for (int jj = t; jj < nqb; jj += kGenThreads) spos[jj] = pos_b[jj];
     __syncthreads();
-    for (int jj = t; jj < a.nq; jj += kGenThreads) {
+    for (int jj = t; jj < nqb; jj += kGenThreads) {
         int f = jj;
         for (int q = 0; q < jj; ++q)
             if (spos[q] == spos[jj]) { f = q; break; }
@@ -134,30 +153,31 @@ __global__ void __launch_bounds__(kGenThreads) attn_generic_kernel(AttnArgs a)
     for (int e = t; e < a.dh; e += kGenThreads) sq[e] = qrow[e];
     __syncthreads();
 
-    const T* Kb = (const T*)a.Kc + ((size_t)b * a.Hkv + g) * a.N * a.dh;
-    const T* Vb = (const T*)a.Vc + ((size_t)b * a.Hkv + g) * a.N * a.dh;
+    const T* Kp = (const T*)a.Kc;
+    const T* Vp = (const T*)a.Vc;
     const T* SKb = (const T*)a.sideK + ((size_t)b * a.Hkv + g) * a.q_max * a.dh;
     const T* SVb = (const T*)a.sideV + ((size_t)b * a.Hkv + g) * a.q_max * a.dh;
     const uint8_t* vis_i = a.vis ? a.vis + ((size_t)b * a.nq + i) * a.nq : nullptr;
 
     float m = -INFINITY, l = 0.f;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};   // dh <= 256: dims t, t+64, t+128, t+192
-    const int nkeys = a.N + a.nq;
+    const int nkeys = L + nqb;
     for (int base = 0; base < nkeys; base += kGenThreads) {
         const int kk = base + t;
         float s = -INFINITY;
         int src = -1;   // >= 0: cache position; < -1: side row -(src+2)
-        if (kk < a.N) {
+        if (kk < L) {
             int owner = -1;
-            for (int q = 0; q < a.nq; ++q)
+            for (int q = 0; q < nqb; ++q)
                 if (spos[q] == kk) { owner = q; break; }
             if (owner < 0 || !vis_i || vis_i[owner]) src = kk;
         } else if (kk < nkeys) {
-            const int jj = kk - a.N;
+            const int jj = kk - L;
             if (sown[jj] != jj && (!vis_i || vis_i[jj])) src = -(jj + 2);
         }
         if (src != -1) {
-            const T* krow = src >= 0 ? Kb + (size_t)src * a.dh : SKb + (size_t)(-(src + 2)) * a.dh;
+            const T* krow = src >= 0 ? Kp + cache_row(a.map, b, g, src, a.Hkv, a.N) * a.dh
+                                     : SKb + (size_t)(-(src + 2)) * a.dh;
             float d = 0.f;
             for (int e = 0; e < a.dh; ++e) d = fmaf(sq[e], to_f32(krow[e]), d);
             s = d * a.scale_log2;
@@ -177,7 +197,8 @@ __global__ void __launch_bounds__(kGenThreads) attn_generic_kernel(AttnArgs a)
             const float pc = sp[c];
             if (pc == 0.f) continue;
             const int sc = skey[c];
-            const T* vrow = sc >= 0 ? Vb + (size_t)sc * a.dh : SVb + (size_t)(-(sc + 2)) * a.dh;
+            const T* vrow = sc >= 0 ? Vp + cache_row(a.map, b, g, sc, a.Hkv, a.N) * a.dh
+                                    : SVb + (size_t)(-(sc + 2)) * a.dh;
             for (int r = 0; r < 4; ++r) {
                 const int e = t + r * kGenThreads;
                 if (e < a.dh) acc[r] = fmaf(pc, to_f32(vrow[e]), acc[r]);

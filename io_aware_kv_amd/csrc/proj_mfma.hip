@@ -99,12 +99,16 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
     for (int r = tid; r < BM; r += C::NT) {
         int m = m0 + r;
         const bool valid = m < M;
-        if (!valid) m = m0;                          // padding rows read a valid row, then are dropped
+        if (!valid) m = m0;                          // rows past M read row 0 of a sequence, then are dropped
         const int b = m / a.rows_per_seq, j = m - b * a.rows_per_seq;
-        const int xr = a.prefill ? j : a.Q_idx[m];
+        // rows past a shorter sequence's own count are padding: they read X
+        // row 0 and write only a zero q row
+        const bool pad = valid && !a.prefill && a.nq_seq && j >= a.nq_seq[b];
+        const bool live = valid && !pad;
+        const int xr = a.prefill ? j : (live ? a.Q_idx[m] : 0);
         sXoff[r] = ((size_t)b * a.x_rows + xr) * a.d;
-        sPos[r] = valid ? (a.prefill ? j : a.pos_ids[m]) : 0;
-        sDst[r] = valid ? 1 : -1;
+        sPos[r] = live ? (a.prefill ? j : a.pos_ids[m]) : 0;
+        sDst[r] = live ? 1 : (pad ? -2 : -1);
     }
     __syncthreads();
 
@@ -166,7 +170,7 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
             // position unless an earlier row of its sequence has the same one
             for (int r = tid; r < BM; r += C::NCW * 64) {
                 const int m = m0 + r;
-                if (m >= M) continue;
+                if (m >= M || sDst[r] < 0) continue;
                 const int b = m / a.rows_per_seq, j = m - b * a.rows_per_seq;
                 const int32_t* pb = a.pos_ids + (size_t)b * a.rows_per_seq;
                 const int p = sPos[r];
@@ -268,13 +272,14 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
         constexpr int CPR = BN / 4;                  // 16 B chunks per row
         for (int c = tid; c < BM * CPR; c += C::NT) {
             const int row = c / CPR, part = c - row * CPR;
-            if (sDst[row] < 0) continue;
+            const int kind = sDst[row];
+            if (kind == -1) continue;
             const int m = m0 + row;
             const int b = m / a.rows_per_seq, j = m - b * a.rows_per_seq;
             const int tcol = part * 4;                                   // tile column
             const int hcol = tcol < BN / 2 ? p0 * 16 + tcol : 64 + p0 * 16 + (tcol - BN / 2);
             float* dst = a.qbuf + (((size_t)b * a.Hkv + g) * a.q_max * G + (size_t)j * G + hl) * kDH + hcol;
-            *(f32x4*)dst = *(const f32x4*)&sOut[row * RS + tcol];
+            *(f32x4*)dst = kind == -2 ? f32x4{0.f, 0.f, 0.f, 0.f} : *(const f32x4*)&sOut[row * RS + tcol];
         }
         return;
     }
@@ -305,7 +310,7 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
         const int hcol = tcol < BN / 2 ? p0 * 16 + tcol : 64 + p0 * 16 + (tcol - BN / 2);
         bf16* dst;
         if (kind == 1)
-            dst = (bf16*)(isk ? a.Kc : a.Vc) + (((size_t)b * a.Hkv + g) * a.N + sPos[row]) * kDH;
+            dst = (bf16*)(isk ? a.Kc : a.Vc) + cache_row(a.map, b, g, sPos[row], a.Hkv, a.N) * kDH;
         else
             dst = (bf16*)(isk ? a.sideK : a.sideV) + (((size_t)b * a.Hkv + g) * a.q_max + j) * kDH;
         *(u32x4*)(dst + hcol) = *(const u32x4*)&sOut[row * RS + tcol];
