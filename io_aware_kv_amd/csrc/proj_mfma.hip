@@ -29,12 +29,24 @@ namespace {
 
 constexpr int kDH = 128;          // head width
 
-// BK: d_model depth per stage (64 or 128: a staged row is 128 or 256 B);
-// NPROD producer waves split each stage's 1 KB DMA blocks, so up to NPROD x 63
-// blocks can be in flight per workgroup.
-template <int BM, int NCB, int NRW, int NPW, int NSMAX, int BK, int NPROD>
+// BK: d_model depth per stage (64 or 128: a staged row is 128 or 256 B); NPROD producer waves split each stage's 1 KB DMA blocks, so up to
+// NPROD x 63 blocks can be in flight per workgroup.  The ring takes as many
+// stages as fit beside the row bookkeeping in the CU's 160 KB of LDS, at most
+// NSMAX (which keeps two workgroups per CU for the narrow tiles): a CU's
+// stream is bound by the bytes it keeps in flight, NS - 1 stages.
+//
+// Consumer waves form NKW x NRW x NPW groups: NRW row groups x NPW column
+// groups of the tile, and NKW groups that split each stage's 32-deep MFMA
+// steps between them (their partial sums are added once, in LDS, after the
+// loop).  A wave reads its row and column fragments from LDS for every step
+// it runs; one wave draws only about 1 KB per 40 cycles from LDS, so the
+// layout keeps the MFMAs per fragment load high (a wave tile of r x c values
+// costs (r + c) / 16 loads for r * c / 256 MFMAs).
+template <int BM, int NCB, int NKW, int NRW, int NPW, int NSMAX, int BK, int NPROD>
 struct ProjCfg {
-    static constexpr int NCW = NRW * NPW;                 // consumer waves
+    static constexpr int NHW = NRW * NPW;                 // waves holding the tile after the k reduction
+    static constexpr int NCW = NKW * NHW;                 // consumer waves
+    static constexpr int KSW = BK / 32 / NKW;             // 32-deep steps per stage per consumer wave
     static constexpr int NT = (NCW + NPROD) * 64;
     static constexpr int BN = 16 * NCB;
     static constexpr int ROWB = BK * 2;                   // bytes per staged row
@@ -42,7 +54,7 @@ struct ProjCfg {
     static constexpr int CPR = BK / 8;                    // 16 B chunks per staged row
     static constexpr int ROWS = BM + BN;                  // staged rows per stage
     static constexpr int STAGE = ROWS * ROWB;
-    static constexpr int NS0 = (144 * 1024) / STAGE;      // the ring takes up to 144 KB of LDS
+    static constexpr int NS0 = (160 * 1024 - 16 * BM - 1024) / STAGE;
     static constexpr int NS = NS0 > NSMAX ? NSMAX : NS0;
     static constexpr int DMA = ROWS / RPD;                // 1 KB DMA blocks per stage
     static constexpr int DMAP = DMA / NPROD;              // per producer wave
@@ -52,6 +64,8 @@ struct ProjCfg {
     static_assert(BK == 64 || BK == 128, "stage depth");
     static_assert((NS - 2) * DMAP <= 63 || NS <= 2, "in-flight DMA blocks per producer");
     static_assert(BM % (16 * NRW) == 0 && PAIRS % NPW == 0 && NS >= 2, "tile shape");
+    static_assert(KSW >= 1 && KSW * NKW * 32 == BK, "k split");
+    static_assert((NKW - 1) * NHW * RBW * 2 * PPW * 1024 <= NS * STAGE, "k reduction staging");
     static_assert(DMA % NPROD == 0 && BM % RPD == 0, "DMA split");
     static_assert(BM * (BN + 4) * 4 <= NS * STAGE, "epilogue staging");
     static_assert(BM * PAIRS * 16 * 8 <= NS * STAGE, "rotary table staging");
@@ -67,11 +81,11 @@ __device__ __forceinline__ int chunk_swz(int row)
     return BK == 128 ? (row & 15) : ((row >> 1) & 7);
 }
 
-template <int BM, int NCB, int NRW, int NPW, int NSMAX, int BK, int NPROD>
-__global__ void __launch_bounds__((NRW * NPW + NPROD) * 64)
+template <int BM, int NCB, int NKW, int NRW, int NPW, int NSMAX, int BK, int NPROD>
+__global__ void __launch_bounds__((NKW * NRW * NPW + NPROD) * 64)
 proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
 {
-    using C = ProjCfg<BM, NCB, NRW, NPW, NSMAX, BK, NPROD>;
+    using C = ProjCfg<BM, NCB, NKW, NRW, NPW, NSMAX, BK, NPROD>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     __shared__ size_t sXoff[BM];   // element offset of the row's X row
     __shared__ int sPos[BM];
@@ -129,7 +143,8 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
     for (int r = 0; r < C::RBW; ++r)
 #pragma unroll
         for (int q = 0; q < 2 * C::PPW; ++q) acc[r][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int wr = wave / NPW, wp = wave % NPW;   // consumer coordinates
+    const int wk = wave / C::NHW;                 // consumer coordinates
+    const int wr = (wave % C::NHW) / NPW, wp = wave % NPW;
 
     if (wave >= C::NCW) {
         // ================= producer waves =================
@@ -191,7 +206,8 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
             ring_consumer_sync();
             const unsigned char* st = smem + (t % C::NS) * C::STAGE;
 #pragma unroll
-            for (int ks = 0; ks < BK / 32; ++ks) {
+            for (int kk = 0; kk < C::KSW; ++kk) {
+                const int ks = wk * C::KSW + kk;
                 bf16x8 af[C::RBW], bfr[2 * C::PPW];
 #pragma unroll
                 for (int r = 0; r < C::RBW; ++r) {
@@ -214,11 +230,37 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
     }
     __syncthreads();   // the ring is free: it stages the finished tile below
 
+    if constexpr (NKW > 1) {
+        // add the k groups' partial sums into the waves of group 0 (each
+        // accumulator block is one 1 KB row of 16 B per lane: conflict-free)
+        constexpr int BLK = C::RBW * 2 * C::PPW;
+        f32x4* sRed = (f32x4*)smem;
+        if (wk > 0 && wave < C::NCW) {
+            f32x4* dst = sRed + ((size_t)((wk - 1) * C::NHW + wave % C::NHW) * BLK) * 64 + lane;
+#pragma unroll
+            for (int r = 0; r < C::RBW; ++r)
+#pragma unroll
+                for (int q = 0; q < 2 * C::PPW; ++q) dst[(r * 2 * C::PPW + q) * 64] = acc[r][q];
+        }
+        __syncthreads();
+        if (wave < C::NHW) {
+#pragma unroll
+            for (int g = 1; g < NKW; ++g) {
+                const f32x4* src = sRed + ((size_t)((g - 1) * C::NHW + wave) * BLK) * 64 + lane;
+#pragma unroll
+                for (int r = 0; r < C::RBW; ++r)
+#pragma unroll
+                    for (int q = 0; q < 2 * C::PPW; ++q) acc[r][q] += src[(r * 2 * C::PPW + q) * 64];
+            }
+        }
+        __syncthreads();
+    }
+
     // rotary on q and k heads: lane holds tile column blk*16 + lr of each block
     // (head column cb*16 + lr) and rows 4*lg + i of each row block.  The
     // table rows of the tile's positions (first-half columns of its pairs)
     // are first staged in the free ring with all loads in flight at once.
-    const bool consumer = wave < C::NCW;
+    const bool consumer = wave < C::NHW;             // the waves that hold the finished tile
     const bool rotate = head < a.H + a.Hkv;
     if (rotate) {
         constexpr int PC = C::PAIRS * 16;                  // table columns of the tile
@@ -317,10 +359,10 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
     }
 }
 
-template <int BM, int NCB, int NRW, int NPW, int NSMAX, int BK, int NPROD>
+template <int BM, int NCB, int NKW, int NRW, int NPW, int NSMAX, int BK, int NPROD>
 hipError_t launch_tile(const ProjArgs& a, hipStream_t s)
 {
-    using C = ProjCfg<BM, NCB, NRW, NPW, NSMAX, BK, NPROD>;
+    using C = ProjCfg<BM, NCB, NKW, NRW, NPW, NSMAX, BK, NPROD>;
     const int M = a.B * a.rows_per_seq;
     const int m_tiles = (M + BM - 1) / BM;
     const int heads = a.prefill ? 2 * a.Hkv : a.H + 2 * a.Hkv;
@@ -328,7 +370,7 @@ hipError_t launch_tile(const ProjArgs& a, hipStream_t s)
     const int total = m_tiles * n_tiles;
     const int grid = ((total + 7) / 8) * 8;
     const size_t shm = (size_t)C::NS * C::STAGE;
-    auto kern = proj_mfma_kernel<BM, NCB, NRW, NPW, NSMAX, BK, NPROD>;
+    auto kern = proj_mfma_kernel<BM, NCB, NKW, NRW, NPW, NSMAX, BK, NPROD>;
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     (void)hipGetLastError();
     hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), shm, s, a, m_tiles, n_tiles);
@@ -340,13 +382,15 @@ hipError_t launch_tile(const ProjArgs& a, hipStream_t s)
 // Tile configurations (rows BM x 16-column blocks NCB): narrow tiles with a
 // 3-stage ring (two workgroups per CU) for a few rows, 64 x 64 tiles up to
 // 128 rows, and 128-column (one head) tiles beyond, as tall as needed to fit
-// every tile into a single round of the 256 CUs.  Measured on MI355X over the
-// layer workloads.
+// every tile into a single round of the 256 CUs; the tallest (208 rows) splits
+// each stage's MFMA steps between two wave groups (choice 9; choice 7 is the
+// same tile without the split).  Measured on MI355X over the layer workloads.
 struct ProjChoice { int bm, ncb; };
 static const ProjChoice kProjChoices[] = {
     {0, 0},
     {16, 2}, {32, 2}, {48, 2}, {64, 4},   // 1-4
     {128, 8}, {176, 8}, {208, 8}, {96, 8},  // 5-8
+    {208, 8},                             // 9
 };
 constexpr int kNumChoices = (int)(sizeof(kProjChoices) / sizeof(kProjChoices[0]));
 
@@ -356,7 +400,7 @@ static int default_choice(int M, int heads)
     if (M <= 32) return 2;
     if (M <= 48) return 3;
     if (M <= 128) return 4;
-    for (int c : {5, 6, 7})
+    for (int c : {5, 6, 9})
         if ((long)((M + kProjChoices[c].bm - 1) / kProjChoices[c].bm) * heads <= 256) return c;
     return 5;
 }
@@ -374,14 +418,15 @@ hipError_t launch_proj_mfma(const ProjArgs& a, hipStream_t s)
     if (a.d % 128 != 0) return hipErrorInvalidValue;
     const int heads = a.prefill ? 2 * a.Hkv : a.H + 2 * a.Hkv;
     switch (proj_mfma_tile(M, heads, a.tile_choice).choice) {
-        case 1: return launch_tile<16, 2, 1, 1, 3, 128, 2>(a, s);
-        case 2: return launch_tile<32, 2, 1, 1, 3, 128, 2>(a, s);
-        case 3: return launch_tile<48, 2, 1, 1, 3, 128, 2>(a, s);
-        case 4: return launch_tile<64, 4, 2, 2, 8, 128, 2>(a, s);
-        case 5: return launch_tile<128, 8, 2, 2, 8, 64, 2>(a, s);
-        case 6: return launch_tile<176, 8, 1, 4, 8, 64, 2>(a, s);
-        case 7: return launch_tile<208, 8, 1, 4, 8, 64, 2>(a, s);
-        case 8: return launch_tile<96, 8, 1, 4, 8, 64, 2>(a, s);
+        case 1: return launch_tile<16, 2, 1, 1, 1, 3, 128, 2>(a, s);
+        case 2: return launch_tile<32, 2, 1, 1, 1, 3, 128, 2>(a, s);
+        case 3: return launch_tile<48, 2, 1, 1, 1, 3, 128, 2>(a, s);
+        case 4: return launch_tile<64, 4, 1, 2, 2, 8, 128, 2>(a, s);
+        case 5: return launch_tile<128, 8, 1, 2, 2, 8, 64, 2>(a, s);
+        case 6: return launch_tile<176, 8, 1, 1, 4, 8, 64, 2>(a, s);
+        case 7: return launch_tile<208, 8, 1, 1, 4, 8, 64, 2>(a, s);
+        case 8: return launch_tile<96, 8, 1, 1, 4, 8, 64, 2>(a, s);
+        case 9: return launch_tile<208, 8, 2, 1, 2, 8, 64, 2>(a, s);
         default: return hipErrorInvalidValue;
     }
 }
