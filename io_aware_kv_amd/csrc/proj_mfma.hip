@@ -397,7 +397,9 @@ constexpr int kNumChoices = (int)(sizeof(kProjChoices) / sizeof(kProjChoices[0])
 static int default_choice(int M, int heads)
 {
     if (M <= 16) return 1;
-    if (M <= 32) return 2;
+    // a few rows past 32 (the draft pass's 1 + 32 rows) still run faster as
+    // two 32-row tiles than as one 48-row tile (measured at M = 33)
+    if (M <= 36) return 2;
     if (M <= 48) return 3;
     if (M <= 128) return 4;
     for (int c : {5, 6, 9})
