@@ -20,10 +20,12 @@
 //    permutes.  Each kv head's partial sums go to a workspace row.
 //  * key_mass_sum_kernel: a_p = sum over kv heads in head order (a fixed
 //    order, so repeated runs agree bit for bit).
-//  * select_top_kernel: one workgroup per sequence sorts 64-bit keys
-//    (order-preserving score bits, then the inverted position so equal
-//    scores rank the lower position first) with a bitonic network in LDS and
-//    keeps the first k candidates.
+//  * select_top_kernel: one workgroup per sequence ranks the candidates by
+//    64-bit keys (order-preserving score bits, then the inverted position so
+//    equal scores rank the lower position first): a radix select finds the
+//    k-th largest score, and only the k selected keys are sorted in LDS.
+#include <algorithm>
+
 #include "fdllm_common.h"
 
 namespace fdllm {
@@ -252,27 +254,204 @@ __device__ __forceinline__ uint32_t ordered_bits(float x)
 }
 
 constexpr int kTopThreads = 1024;
+constexpr int kTopWaves = kTopThreads / 64;
+constexpr int kTopPer = 16;           // consecutive positions per thread (N <= 16384)
 
-// One workgroup per sequence; LDS holds n2 (a power of two >= N) 64-bit keys.
+// Exclusive prefix sum of x over the workgroup in thread order; `total` gets
+// the sum.  sTmp holds kTopWaves + 1 ints.
+__device__ __forceinline__ int top_scan(int x, int* sTmp, int& total)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) sTmp[wave] = incl;
+    __syncthreads();
+    if (wave == 0) {
+        const int w = lane < kTopWaves ? sTmp[lane] : 0;
+        int wi = w;
+#pragma unroll
+        for (int o = 1; o < kTopWaves; o <<= 1) {
+            const int y = __shfl_up(wi, o);
+            if (lane >= o) wi += y;
+        }
+        if (lane < kTopWaves) sTmp[lane] = wi - w;
+        if (lane == kTopWaves - 1) sTmp[kTopWaves] = wi;
+    }
+    __syncthreads();
+    const int r = sTmp[wave] + incl - x;
+    total = sTmp[kTopWaves];
+    __syncthreads();
+    return r;
+}
+
+// One workgroup per sequence.  Candidate p has the key (ordered score bits,
+// then the inverted position), so larger keys rank first and equal scores
+// rank the lower position first.  The k-th largest score bits come from a
+// radix select (four 8-bit passes over per-wave LDS histograms); the
+// candidates above it, and the lowest-position ones equal to it, are
+// compacted in position order and only those (a power of two >= min(k, N)
+// slots) are sorted with a bitonic network in LDS.
 __global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __restrict__ scores,
                                                                  const uint8_t* __restrict__ cand, int N, int n2,
                                                                  int k, int32_t* __restrict__ out)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    // first the scores as order-preserving bits [N] and the candidate flags
+    // as bit words [N / 32], loaded coalesced; later, in the same space, the
+    // selected keys [n2]
+    uint32_t* sU = (uint32_t*)smem;
+    uint32_t* sValid = sU + ((N + 3) & ~3);
     uint64_t* key = (uint64_t*)smem;
+    __shared__ int sHist[kTopWaves][256];
+    __shared__ int sTmp[kTopWaves + 1];
+    __shared__ int sBin, sNeed, sCount;
     const int b = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* sc = scores + (size_t)b * N;
     const uint8_t* cd = cand + (size_t)b * N;
-    for (int p = threadIdx.x; p < n2; p += kTopThreads) {
-        uint64_t v = 0;   // padding and non-candidates sort last
-        if (p < N && cd[p]) v = ((uint64_t)ordered_bits(sc[p]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)p);
-        key[p] = v;
-    }
+
+    if (tid == 0) sCount = 0;
     __syncthreads();
-    // bitonic network, descending overall
-    for (int size = 2; size <= n2; size <<= 1) {
+    int cnt = 0;   // candidates seen by this wave
+    for (int base = 0; base < N; base += kTopThreads) {
+        const int p = base + tid;
+        const bool in = p < N && cd[min(p, N - 1)] != 0;
+        if (p < N) sU[p] = ordered_bits(sc[p]);
+        const uint64_t m = __builtin_amdgcn_ballot_w64(in);
+        cnt += __builtin_popcountll(m);
+        if (lane == 0) {
+            const int w0 = (base + wave * 64) >> 5;
+            if (base + wave * 64 < N) sValid[w0] = (uint32_t)m;
+            if (base + wave * 64 + 32 < N) sValid[w0 + 1] = (uint32_t)(m >> 32);
+        }
+    }
+    if (lane == 0) atomicAdd(&sCount, cnt);
+    __syncthreads();
+    // each thread then takes kTopPer consecutive positions
+    uint32_t u[kTopPer];
+    uint32_t valid = 0u;
+    {
+        const int p0 = tid * kTopPer;
+        if (p0 < N) valid = (sValid[p0 >> 5] >> (p0 & 31)) & 0xffffu;
+        if (p0 + kTopPer > N) valid &= p0 >= N ? 0u : (1u << (N - p0)) - 1u;
+#pragma unroll
+        for (int i = 0; i < kTopPer; ++i) u[i] = sU[min(p0 + i, N - 1)];
+    }
+    const int C = sCount;
+
+    // threshold: the k-th largest score bits among the candidates (when there
+    // are more than k), and how many candidates equal to it are taken
+    uint32_t thr = 0u;
+    int need = 0;
+    if (C > k) {
+        uint32_t pmask = 0u;
+        need = k;
+        for (int shift = 24; shift >= 0; shift -= 8) {
+            for (int t = tid; t < kTopWaves * 256; t += kTopThreads) (&sHist[0][0])[t] = 0;
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < kTopPer; ++i)
+                if (((valid >> i) & 1u) && (u[i] & pmask) == thr) atomicAdd(&sHist[wave][(u[i] >> shift) & 255u], 1);
+            __syncthreads();
+            if (tid < 256) {
+                int h = 0;
+#pragma unroll
+                for (int w = 0; w < kTopWaves; ++w) h += sHist[w][tid];
+                sHist[0][tid] = h;
+            }
+            __syncthreads();
+            if (wave == 0) {
+                // lane l holds bins 255 - 4l .. 252 - 4l; counts accumulate from the top bin down
+                int c[4], s4 = 0;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    c[j] = sHist[0][255 - 4 * lane - j];
+                    s4 += c[j];
+                }
+                int incl = s4;
+#pragma unroll
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int y = __shfl_up(incl, o);
+                    if (lane >= o) incl += y;
+                }
+                const int excl = incl - s4;
+                if (excl < need && need <= incl) {
+                    int acc = excl, bin = -1, rest = 0;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if (bin < 0 && acc + c[j] >= need) {
+                            bin = 255 - 4 * lane - j;
+                            rest = need - acc;
+                        }
+                        acc += c[j];
+                    }
+                    sBin = bin;
+                    sNeed = rest;
+                }
+            }
+            __syncthreads();
+            thr |= (uint32_t)sBin << shift;
+            pmask |= 255u << shift;
+            need = sNeed;
+            __syncthreads();
+        }
+    }
+
+    // the selected candidates, compacted in position order: all of them when
+    // there are at most k, else those above the threshold and the first
+    // `need` equal to it
+    uint32_t sel = valid;
+    if (C > k) {
+        uint32_t tie = 0u;
+#pragma unroll
+        for (int i = 0; i < kTopPer; ++i) tie |= ((((valid >> i) & 1u) && u[i] == thr) ? 1u : 0u) << i;
+        int ntie;
+        int r = top_scan(__builtin_popcount(tie), sTmp, ntie);
+        sel = 0u;
+#pragma unroll
+        for (int i = 0; i < kTopPer; ++i) {
+            const bool v = (valid >> i) & 1u;
+            const bool t = (tie >> i) & 1u;
+            const bool take = v && (u[i] > thr || (t && r < need));
+            r += t ? 1 : 0;
+            sel |= (take ? 1u : 0u) << i;
+        }
+    }
+    int nsel;
+    int w = top_scan(__builtin_popcount(sel), sTmp, nsel);
+#pragma unroll
+    for (int i = 0; i < kTopPer; ++i)
+        if ((sel >> i) & 1u) {
+            const uint32_t p = (uint32_t)(tid * kTopPer + i);
+            key[w++] = ((uint64_t)u[i] << 32) | (uint64_t)(0xffffffffu - p);
+        }
+    for (int t = nsel + tid; t < n2; t += kTopThreads) key[t] = 0;   // padding sorts last
+    __syncthreads();
+    if (n2 <= 256) {
+        // up to 256 keys (all distinct): the rank of a key is the number of
+        // larger keys, counted by 1024 / n2 threads per key; each key then
+        // goes to its rank
+        // (a power-of-two group of lanes of one wave per key)
+        const int tpk = min(min(n2, kTopThreads / n2), 64), per = n2 / tpk;
+        const int i = tid / tpk, sub = tid - i * tpk;
+        const bool live = i < n2;
+        const uint64_t mine = live ? key[i] : 0;
+        int rank = 0;
+        if (live)
+            for (int j = sub * per; j < (sub + 1) * per; ++j) rank += key[j] > mine ? 1 : 0;
+        for (int o = 1; o < tpk; o <<= 1) rank += __shfl_xor(rank, o);
+        __syncthreads();
+        if (live && sub == 0) key[rank] = mine;
+        __syncthreads();
+    }
+    // bitonic network over the n2 slots, descending overall (more than 256)
+    for (int size = 2; n2 > 256 && size <= n2; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            for (int t = threadIdx.x; t < n2 / 2; t += kTopThreads) {
+            for (int t = tid; t < n2 / 2; t += kTopThreads) {
                 const int lo = 2 * t - (t & (stride - 1));
                 const int hi = lo + stride;
                 const bool desc = (lo & size) == 0;
@@ -282,10 +461,8 @@ __global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __
             __syncthreads();
         }
     }
-    for (int t = threadIdx.x; t < k; t += kTopThreads) {
-        const uint64_t v = t < n2 ? key[t] : 0;
-        out[(size_t)b * k + t] = v == 0 ? -1 : (int32_t)(0xffffffffu - (uint32_t)(v & 0xffffffffu));
-    }
+    for (int t = tid; t < k; t += kTopThreads)
+        out[(size_t)b * k + t] = t < nsel ? (int32_t)(0xffffffffu - (uint32_t)(key[t] & 0xffffffffu)) : -1;
 }
 
 }  // namespace
@@ -332,10 +509,13 @@ hipError_t launch_select_top(const float* scores, const uint8_t* cand, int B, in
                              hipStream_t s)
 {
     if (B == 0 || k == 0) return hipSuccess;
+    if (N < 1 || N > kTopThreads * kTopPer) return hipErrorInvalidValue;
+    // slots for the selected keys: a power of two >= min(k, N)
+    const int m = std::min(k, N);
     int n2 = 1;
-    while (n2 < N) n2 <<= 1;
-    const size_t shm = (size_t)n2 * sizeof(uint64_t);
-    if (shm > 128 * 1024) return hipErrorInvalidValue;
+    while (n2 < m) n2 <<= 1;
+    const size_t staged = (size_t)((N + 3) & ~3) * 4 + (size_t)((N + 31) / 32) * 4;
+    const size_t shm = std::max((size_t)n2 * sizeof(uint64_t), staged);
     (void)hipFuncSetAttribute((const void*)select_top_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     (void)hipGetLastError();
     hipLaunchKernelGGL(select_top_kernel, dim3(B), dim3(kTopThreads), shm, s, scores, cand, N, n2, k, out);

@@ -132,6 +132,51 @@ def test_select_top_ties_and_short_candidate_lists():
     assert out[2, 3:].eq(-1).all()
 
 
+TOPK_CASES = [
+    # (label, B, N, k, pattern)
+    ("k-above-N", 2, 37, 45, "ties"),
+    ("max-N", 2, 16384, 80, "random"),
+    ("max-N-ties", 1, 16384, 300, "ties"),
+    ("ragged-N", 3, 1001, 17, "random"),
+    ("one-candidate", 2, 64, 5, "one"),
+    ("all-equal", 2, 3000, 50, "equal"),
+    ("signs-and-zeros", 2, 777, 64, "signed"),
+    ("k-one", 4, 2048, 1, "ties"),
+]
+
+
+@pytest.mark.parametrize("label,B,N,k,pattern", TOPK_CASES, ids=[c[0] for c in TOPK_CASES])
+def test_select_top_edge_cases(label, B, N, k, pattern):
+    """The top-k against the oracle's ranking of the same fp32 scores: k at
+    or past the candidate count, the largest N, N not a multiple of 16, a
+    single candidate, every score equal, negative scores and signed zeros."""
+    log("case: top-k %s" % label)
+    rng = np.random.default_rng(44 + N + k)
+    if pattern == "random":
+        sc = rng.standard_normal((B, N)).astype(np.float32)
+    elif pattern == "ties":
+        sc = (rng.integers(0, 12, size=(B, N)) / 4.0).astype(np.float32)
+    elif pattern == "equal":
+        sc = np.full((B, N), 0.375, dtype=np.float32)
+    elif pattern == "signed":
+        sc = (rng.integers(-6, 7, size=(B, N)) / 2.0).astype(np.float32)
+        sc[:, ::5] = -0.0
+        sc[:, 1::7] = 0.0
+    else:
+        sc = rng.standard_normal((B, N)).astype(np.float32)
+    cand = (rng.random((B, N)) < 0.6).astype(np.uint8)
+    if pattern == "one":
+        cand[:] = 0
+        cand[:, N // 3] = 1
+    dev = torch.device("cuda")
+    fk = FusedKVCache(B, N, 128, 2, 2, 128, 4, torch.bfloat16)
+    out = torch.full((B, k), -7, dtype=torch.int32, device=dev)
+    fk.select_tracked(torch.from_numpy(sc).to(dev), torch.from_numpy(cand).to(dev), k, out)
+    torch.cuda.synchronize()
+    fk.close()
+    assert np.array_equal(out.cpu().numpy(), oracle.select_top(sc, cand, k)), label
+
+
 def test_tracked_scores_no_rows_selected():
     log("case: tracked scores, nothing selected")
     wl = make_workload(2)
