@@ -24,6 +24,7 @@ namespace fdllm {
 namespace {
 
 constexpr int kConfThreads = 1024;
+constexpr int kConfLoads = 4;        // 16-byte loads per thread per round
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -61,7 +62,7 @@ __device__ __forceinline__ Best merge(const Best& a, const Best& b)
     return r;
 }
 
-template <typename T>
+template <typename T, int NL>
 __global__ void __launch_bounds__(kConfThreads) confidence_kernel(const T* __restrict__ logits, int V, int mask_id,
                                                                   float thr, int32_t* __restrict__ pred,
                                                                   float* __restrict__ conf, uint8_t* __restrict__ over)
@@ -73,38 +74,83 @@ __global__ void __launch_bounds__(kConfThreads) confidence_kernel(const T* __res
     const bool vec = (V % PER) == 0;
     const int tid = threadIdx.x;
     if (vec) {
-        // four 16-byte loads in flight per thread per round; per round one
-        // rescale to the round's max, then branch-free exp2 sums (ids grow
-        // along a thread's walk, so a strict compare keeps the lowest id)
-        for (int v0 = tid * PER; v0 < V; v0 += kConfThreads * PER * 4) {
-            u32x4 raw[4];
+        // kConfLoads 16-byte loads in flight per thread per round.  Per
+        // element only the raw max and the exp2 sum: the round's max of the
+        // raw logits gives the rescale (scaling by log2 e and rounding are
+        // monotonic, so it bounds every scaled logit of the round), and a
+        // lane keeps its best non-[MASK] logit with the raw data of the round
+        // that holds it; after the row the first id holding it is found in
+        // that copy (ids grow along a lane's walk, so the lowest id wins
+        // ties).  The [MASK] id is left out of the argmax only, by a check
+        // per load.
+        int bround = -1;                                // round of the lane's best logit
+        u32x4 keep[NL];                                 // ... and its raw logits
+        for (int v0 = tid * PER; v0 < V; v0 += kConfThreads * PER * NL) {
+            u32x4 raw[NL];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
+            for (int u = 0; u < NL; ++u) {
                 const int v = min(v0 + u * kConfThreads * PER, V - PER);
                 raw[u] = *(const u32x4*)(x + v);
             }
-            float xs[4 * PER];
-            float rm = -INFINITY;
+            float f[NL * PER];
+            float rmax = -INFINITY;
+            bool has_mask = false;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const bool in = v0 + u * kConfThreads * PER < V;
+            for (int u = 0; u < NL; ++u) {
+                const int base = v0 + u * kConfThreads * PER;
+                const bool in = base < V;
+                has_mask = has_mask || (in && mask_id >= base && mask_id < base + PER);
                 const T* e = (const T*)&raw[u];
 #pragma unroll
                 for (int k = 0; k < PER; ++k) {
-                    const float r = in ? to_f32(e[k]) : -INFINITY;
-                    const int id = v0 + u * kConfThreads * PER + k;
-                    if (in && id != mask_id && (r > b.bl || b.bi == 0x7fffffff)) { b.bl = r; b.bi = id; }
-                    xs[u * PER + k] = r * kLog2e;
-                    rm = fmaxf(rm, xs[u * PER + k]);
+                    f[u * PER + k] = in ? to_f32(e[k]) : -INFINITY;
+                    rmax = fmaxf(rmax, f[u * PER + k]);
                 }
             }
-            if (rm > -INFINITY) {
+            float amax = rmax;                          // best non-[MASK] logit of the round
+            if (has_mask) {
+                amax = -INFINITY;
+#pragma unroll
+                for (int u = 0; u < NL; ++u)
+#pragma unroll
+                    for (int k = 0; k < PER; ++k)
+                        if (v0 + u * kConfThreads * PER + k != mask_id) amax = fmaxf(amax, f[u * PER + k]);
+            }
+            // a new best for this lane: remember the round (its id is found
+            // after the row, from one re-read of that round)
+            // (a round's first load is in range, so it holds a non-[MASK] id)
+            const bool better = amax > b.bl || bround < 0;
+            if (better) {
+                b.bl = amax;
+                bround = v0;
+            }
+#pragma unroll
+            for (int u = 0; u < NL; ++u) keep[u] = better ? raw[u] : keep[u];
+            if (rmax > -INFINITY) {
+                const float rm = rmax * kLog2e;
                 if (rm > b.m) {
                     b.s *= __builtin_amdgcn_exp2f(b.m - rm);
                     b.m = rm;
                 }
+                const float nm = -b.m;
 #pragma unroll
-                for (int k = 0; k < 4 * PER; ++k) b.s += __builtin_amdgcn_exp2f(xs[k] - b.m);
+                for (int k = 0; k < NL * PER; ++k) b.s += __builtin_amdgcn_exp2f(__builtin_fmaf(f[k], kLog2e, nm));
+            }
+        }
+        if (bround >= 0) {
+            // the first in-range non-[MASK] id of that round holding the best
+            // logit (the round holds one when the best is -inf too)
+#pragma unroll
+            for (int u = 0; u < NL; ++u) {
+                const int base = bround + u * kConfThreads * PER;
+                if (base >= V) break;
+                const T* e = (const T*)&keep[u];
+#pragma unroll
+                for (int k = 0; k < PER; ++k) {
+                    const int id = base + k;
+                    const float fv = to_f32(e[k]);
+                    if (b.bi == 0x7fffffff && id != mask_id && (fv == b.bl || b.bl == -INFINITY)) b.bi = id;
+                }
             }
         }
     } else {
@@ -155,10 +201,10 @@ hipError_t launch_confidence(const void* logits, int dtype, int64_t rows, int V,
 {
     if (rows == 0) return hipSuccess;
     if (dtype == 1)
-        hipLaunchKernelGGL(confidence_kernel<bf16>, dim3((unsigned)rows), dim3(kConfThreads), 0, s,
+        hipLaunchKernelGGL((confidence_kernel<bf16, kConfLoads>), dim3((unsigned)rows), dim3(kConfThreads), 0, s,
                            (const bf16*)logits, V, mask_id, thr, pred, conf, over);
     else
-        hipLaunchKernelGGL(confidence_kernel<float>, dim3((unsigned)rows), dim3(kConfThreads), 0, s,
+        hipLaunchKernelGGL((confidence_kernel<float, kConfLoads>), dim3((unsigned)rows), dim3(kConfThreads), 0, s,
                            (const float*)logits, V, mask_id, thr, pred, conf, over);
     return hipGetLastError();
 }

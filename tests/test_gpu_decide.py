@@ -88,6 +88,39 @@ def test_confidence_matches_oracle(rows, V, dtype, mask_id):
         assert pred[0] == 10
 
 
+@pytest.mark.parametrize("dtype,V", [(torch.float32, 32768), (torch.bfloat16, 65536)])
+def test_confidence_argmax_corner_rows(dtype, V):
+    """Rows built to hit each step of the argmax: equal maxima in one lane's
+    consecutive rounds and in one round's different loads (a lane reads 16 B
+    at ids v, v + 1024 * e, ... with e elements per 16 B, four loads per
+    round), the [MASK] id holding the row's maximum, all but two logits -inf,
+    the maximum at the last id, and a row of equal logits."""
+    log("case: confidence argmax corner rows %s V=%d" % (dtype, V))
+    e = 16 // (4 if dtype == torch.float32 else 2)       # elements per 16-byte load
+    load, rnd = 1024 * e, 4 * 1024 * e                    # id stride of a load and of a round
+    mask_id = 126
+    x = decision_logits(6, V, seed=V + 5, dtype=torch.float32)
+    top = float(x.max()) + 1.0
+    x[0, 5] = top
+    x[0, 5 + rnd] = top                                   # same lane, next round: id 5 wins
+    x[1, 9] = top
+    x[1, 9 + 2 * load] = top                              # same lane and round, third load: id 9 wins
+    x[2, mask_id] = top + 4.0                             # the [MASK] id is the row's maximum
+    x[2, 3000] = top
+    x[3, :] = float("-inf")
+    x[3, 7] = 0.0
+    x[3, V - 3] = -1.0
+    x[4, V - 1] = top                                     # maximum at the last id
+    x[5, :] = 0.25
+    x = x.to(dtype)
+    pred, conf, over = gpu_confidence(x, mask_id, 0.5)
+    rp, rc = decode.confidences(x.double().numpy(), mask_id)
+    assert pred.tolist() == [5, 9, 3000, 7, V - 1, 0]
+    assert np.array_equal(pred, rp)
+    rel = np.abs(conf - rc) / np.maximum(rc, 1e-30)
+    assert rel.max() <= 1e-5
+
+
 def test_accept_matches_oracle():
     log("case: sequential acceptance")
     rng = np.random.default_rng(11)
