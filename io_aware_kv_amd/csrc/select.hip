@@ -12,12 +12,15 @@
 // over the keys row i may see (positions written this step are the owner
 // row's key, gated by the visibility mask).
 //
-//  * key_mass_kernel: one workgroup per (sequence, kv head, key split).  The
-//    selected rows' q (fp32 in the step's staging buffer, as bf16 hi + lo
-//    parts) are the MFMA A operand, 16-key blocks of K loaded straight into B
-//    fragments (16 B per lane) the B operand, so a lane ends with 4 query
-//    rows of one key: the per-key sum is four in-lane adds and two row-swap
-//    permutes.  Each kv head's partial sums go to a workspace row.
+//  * key_mass_ring_kernel / key_mass_kernel: one workgroup per (sequence, kv
+//    head, key split).  The selected rows' q (fp32 in the step's staging
+//    buffer, as bf16 hi + lo parts) are the MFMA A operand, 16-key blocks of
+//    K the B operand, so a lane ends with 4 query rows of one key: the
+//    per-key sum is four in-lane adds and two row-swap permutes.  With at
+//    most 48 possible (row, head) pairs K streams through an LDS ring (the
+//    pass is bound by HBM); with more, each wave loads its key blocks
+//    straight into MFMA fragments (the pass is bound by its MFMAs and
+//    exponentials).  Each kv head's partial sums go to a workspace row.
 //  * key_mass_sum_kernel: a_p = sum over kv heads in head order (a fixed
 //    order, so repeated runs agree bit for bit).
 //  * select_top_kernel: one workgroup per sequence ranks the candidates by
@@ -26,15 +29,18 @@
 //    k-th largest score, and only the k selected keys are sorted in LDS.
 #include <algorithm>
 
-#include "fdllm_common.h"
+#include "pipeline.h"
 
 namespace fdllm {
 
 namespace {
 
 constexpr int kDH = 128;
-constexpr int kMassWaves = 4;
-constexpr int kMassUnroll = 4;        // 16-key blocks a wave loads before computing
+constexpr int kMassWaves = 4;                 // consumer waves (one 16-key block of a tile each)
+constexpr int kMassTK = 16 * kMassWaves;      // keys per ring stage
+constexpr int kMassStage = kMassTK * 256;     // bytes per stage (K rows of 256 B)
+constexpr int kMassMinStages = 3;
+constexpr int kMassUnroll = 4;                // direct form: 16-key blocks a wave loads before computing
 
 __device__ __forceinline__ float sum4x(float x)
 {
@@ -44,11 +50,203 @@ __device__ __forceinline__ float sum4x(float x)
     return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
-// LDS layout (dynamic): sSel[nq] int, sOwner[kps] int, sVis[nq * VW] u32.
-// Up to four row blocks of 16 (selected row, head) pairs are held in
-// registers at a time (blocks past the selection are skipped); a wave takes
-// kMassUnroll consecutive 16-key blocks per round with all their K loads in
-// flight.
+// LDS layout (dynamic): the K ring [ns stages of kMassTK rows], then sSel[nq]
+// int, sOwner[kps] int, sVis[nq * VW] u32.  One producer wave streams K tiles
+// of kMassTK keys into the ring with global_load_lds (16 B chunks of a row
+// XOR-swizzled by the row, so the fragment reads below are conflict-free) and
+// releases each stage with a barrier once its own vmcnt shows it landed; the
+// consumer waves take one 16-key block of each tile each, against all the
+// selected (row, head) pairs: three 16-row blocks of q in registers (the
+// launcher takes this form only when at most 48 pairs can be selected).
+__global__ void __launch_bounds__((kMassWaves + 1) * 64) key_mass_ring_kernel(MassArgs a, int ns)
+{
+    constexpr int kMassRowBlocks = 3;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __shared__ int sNsel;
+    const int nq = a.nq, G = a.G;
+    const int VW = (nq + 31) >> 5;
+    int* sSel = (int*)(smem + (size_t)ns * kMassStage);
+    int* sOwner = sSel + nq;
+    uint32_t* sVis = (uint32_t*)(sOwner + a.keys_per_split);
+
+    const int split = blockIdx.x % a.splits;
+    const int bg = blockIdx.x / a.splits;
+    const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+    const int k0 = split * a.keys_per_split;
+    const int k1 = min(a.N, k0 + a.keys_per_split);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool producer = wave == kMassWaves;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int32_t* pos_b = a.pos_ids + (size_t)b * nq;
+    const uint8_t* sel_b = a.sel + (size_t)b * nq;
+    const uint8_t* vis_b = a.vis ? a.vis + (size_t)b * nq * nq : nullptr;
+
+    // selected rows in Q order (wave 0, 64 rows per ballot)
+    if (wave == 0) {
+        int n = 0;
+        for (int c = 0; c < nq; c += 64) {
+            const int j = c + lane;
+            const bool s = j < nq && sel_b[j] != 0;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(s);
+            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (s) sSel[n + below] = j;
+            n += __builtin_popcountll(m);
+        }
+        if (lane == 0) sNsel = n;
+    }
+    // owner row of each position of the split: the first row in Q order
+    for (int k = tid; k < k1 - k0; k += (kMassWaves + 1) * 64) sOwner[k] = 0x7fffffff;
+    __syncthreads();
+    for (int j = tid; j < nq; j += (kMassWaves + 1) * 64) {
+        const int p = pos_b[j];
+        if (p >= k0 && p < k1) atomicMin(&sOwner[p - k0], j);
+    }
+    const int nsel = sNsel;
+    // visibility bits of the selected rows (word w covers owner rows 32w..)
+    if (vis_b) {
+        for (int t = tid; t < nsel * VW; t += (kMassWaves + 1) * 64) {
+            const int s = t / VW, w = t - s * VW;
+            const uint8_t* row = vis_b + (size_t)sSel[s] * nq;
+            uint32_t bits = 0u;
+            for (int e = 0; e < 32 && 32 * w + e < nq; ++e) bits |= (row[32 * w + e] != 0 ? 1u : 0u) << e;
+            sVis[t] = bits;
+        }
+    }
+    __syncthreads();
+
+    const int R = min(nsel * G, 16 * kMassRowBlocks); // (selected row, head) pairs
+    const int ntile = (k1 - k0 + kMassTK - 1) / kMassTK;
+    const int total = ntile;
+    const unsigned char* Kg = (const unsigned char*)((const bf16*)a.Kc + (size_t)bg * a.N * kDH);
+
+    if (producer) {
+        // ================= producer wave: K tiles -> LDS ring =================
+        const int srow = lane >> 4, slot = lane & 15;
+        auto issue = [&](int t) {
+            unsigned char* st = smem + (size_t)(t % ns) * kMassStage;
+            const int kt = k0 + (t % ntile) * kMassTK;
+#pragma unroll
+            for (int i = 0; i < kMassTK / 4; ++i) {
+                const int row = 4 * i + srow;
+                const int key = min(kt + row, k1 - 1);       // rows past the split repeat its last key
+                __builtin_amdgcn_global_load_lds((glb_void*)(Kg + (size_t)key * 256 + ((slot ^ (row & 15)) << 4)),
+                                                 (lds_void*)(st + i * 1024), 16, 0, 0);
+            }
+        };
+        int issued = 0;
+        for (; issued < min(ns - 1, total); ++issued) issue(issued);
+        for (int t = 0; t < total; ++t) {
+            // stage t has landed once at most (issued - t - 1) younger stages
+            // of kMassTK / 4 loads each are in flight
+            ring_producer_sync((issued - t - 1) * (kMassTK / 4));
+            if (issued < total && issued < t + ns) issue(issued++);
+        }
+        return;
+    }
+
+    // ================= consumer waves =================
+    // row of selected slot s (clamped; with no selected row, row 0 stands in
+    // and every score is dropped through L2 = +inf)
+    auto selrow = [&](int s) { return nsel > 0 ? sSel[min(s, nsel - 1)] : 0; };
+    const float* qbase = a.qbuf + (size_t)bg * a.q_max * G * kDH;
+    float* part = a.part + (size_t)bg * a.N;
+    const float kLog2e = 1.4426950408889634f;
+    // this wave's 16 keys of a tile: row wave * 16 + lr, chunk c * 4 + lg
+    const int krow = wave * 16 + lr;
+    int kofs[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) kofs[c] = krow * 256 + (((c * 4 + lg) ^ (krow & 15)) << 4);
+
+    bf16x8 qh[kMassRowBlocks][4], ql[kMassRowBlocks][4];
+    float l2[kMassRowBlocks][4];
+    auto rowbase = [&](int j) { return j * 16; };
+    // q fragments as bf16 hi + lo parts (rows past R: zero q, L2 = +inf)
+#pragma unroll
+    for (int j = 0; j < kMassRowBlocks; ++j) {
+        const int row = rowbase(j) + lr;
+        const bool ok = row < R;
+        const int rr = ok ? row : 0;
+        const int s = rr / G, hl = rr - s * G;
+        const float* qp = qbase + ((size_t)selrow(s) * G + hl) * kDH;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const f32x4 x0 = *(const f32x4*)(qp + 32 * c + 8 * lg);
+            const f32x4 x1 = *(const f32x4*)(qp + 32 * c + 8 * lg + 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = ok ? (e < 4 ? x0[e] : x1[e - 4]) * a.scale_log2 : 0.f;
+                const bf16 hi = (bf16)x;
+                qh[j][c][e] = hi;
+                ql[j][c][e] = (bf16)(x - (float)hi);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rowi = rowbase(j) + 4 * lg + i;
+            const bool oki = rowi < R;
+            const int ri = oki ? rowi : 0;
+            const int si = ri / G, hli = ri - si * G;
+            const int qi = selrow(si);
+            const float lse = a.LSE[((size_t)b * nq + qi) * a.H + g * G + hli];
+            // an empty key set (-inf) or a padding row contributes nothing
+            l2[j][i] = (oki && lse > -INFINITY) ? lse * kLog2e : INFINITY;
+        }
+    }
+
+    // scores of this wave's 16 keys at LDS row krow of stage st against the
+    // register row blocks, masked, as 2^(s - L2), summed over the rows
+    auto colsum_of = [&](const unsigned char* st, int krow, int key) {
+        bf16x8 kf[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) kf[c] = *(const bf16x8*)(st + krow * 256 + (((c * 4 + lg) ^ (krow & 15)) << 4));
+        const int ow = sOwner[min(key, k1 - 1) - k0];
+        const int owner = ow == 0x7fffffff ? -1 : ow;
+        const bool gated = vis_b != nullptr && owner >= 0;
+        float cs = 0.f;
+#pragma unroll
+        for (int j = 0; j < kMassRowBlocks; ++j) {
+            const int rb0 = rowbase(j);
+            if (rb0 >= R && j > 0) break;                  // (uniform: no selected pair left)
+            f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[j][c], kf[c], sc, 0, 0, 0);
+                sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[j][c], kf[c], sc, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                bool keep = key < k1;
+                if (gated) {
+                    // selected slot of the lane's row (past R: slot 0, whose
+                    // term is zero through L2 anyway)
+                    const int rowi = rb0 + 4 * lg + i;
+                    const int sr = rowi < R ? rowi / G : 0;
+                    keep = keep && ((sVis[sr * VW + (owner >> 5)] >> (owner & 31)) & 1u);
+                }
+                const float pv = __builtin_amdgcn_exp2f(sc[i] - l2[j][i]);   // 2^-inf = 0
+                cs += keep ? pv : 0.f;
+            }
+        }
+        return sum4x(cs);
+    };
+
+    for (int t = 0; t < total; ++t) {
+        ring_consumer_sync();
+        const unsigned char* st = smem + (size_t)(t % ns) * kMassStage;
+        const int kt = k0 + (t % ntile) * kMassTK;
+        const int key = kt + wave * 16 + lr;
+        const float cs = colsum_of(st, wave * 16 + lr, key);
+        if (lg == 0 && key < k1) part[key] = cs;
+    }
+}
+
+// Direct form, for more than 64 possible (row, head) pairs.  LDS layout
+// (dynamic): sSel[nq] int, sOwner[kps] int, sVis[nq * VW] u32.  Up to four
+// row blocks of 16 (selected row, head) pairs are held in registers at a
+// time (blocks past the selection are skipped); a wave takes kMassUnroll
+// consecutive 16-key blocks per round, loaded straight into MFMA fragments,
+// with all their K loads in flight.
 __global__ void __launch_bounds__(kMassWaves * 64) key_mass_kernel(MassArgs a)
 {
     constexpr int kMassRowBlocks = 4;
@@ -467,21 +665,43 @@ __global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __
 
 }  // namespace
 
+// LDS of the bookkeeping plus the smallest ring
 size_t key_mass_lds_bytes(int nq, int keys_per_split)
 {
     const int VW = (nq + 31) >> 5;
-    return (size_t)nq * 4 + (size_t)keys_per_split * 4 + (size_t)nq * VW * 4;
+    return (size_t)kMassMinStages * kMassStage + (size_t)nq * 4 + (size_t)keys_per_split * 4 +
+           (size_t)nq * VW * 4;
 }
 
 hipError_t launch_key_mass(const MassArgs& a, hipStream_t s)
 {
     if (a.B * a.Hkv == 0 || a.N == 0) return hipSuccess;
-    const size_t shm = key_mass_lds_bytes(a.nq, a.keys_per_split);
-    if (shm > 150 * 1024) return hipErrorInvalidValue;
-    (void)hipFuncSetAttribute((const void*)key_mass_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
-    (void)hipGetLastError();
-    hipLaunchKernelGGL(key_mass_kernel, dim3(a.B * a.Hkv * a.splits), dim3(kMassWaves * 64), shm, s, a);
-    hipError_t e = hipGetLastError();
+    const size_t book = key_mass_lds_bytes(a.nq, a.keys_per_split) - (size_t)kMassMinStages * kMassStage;
+    // as many stages as fit (at most 8) beside the bookkeeping and the
+    // kernel's own few bytes; two workgroups per CU when there are more
+    // workgroups than CUs
+    const unsigned wgs = (unsigned)(a.B * a.Hkv * a.splits);
+    hipError_t e;
+    if ((long)a.nq * a.G <= 48) {
+        // at most 48 (row, head) pairs can be selected: the K stream through
+        // the LDS ring, all pairs in the registers of every wave
+        const size_t budget = (wgs > 256 ? 80 : 160) * 1024 - 256 - book;
+        int ns = (int)std::min<size_t>(8, budget / kMassStage);
+        if (ns < kMassMinStages) ns = (int)std::min<size_t>(8, (160 * 1024 - 256 - book) / kMassStage);
+        if (ns < kMassMinStages) return hipErrorInvalidValue;
+        const size_t shm = (size_t)ns * kMassStage + book;
+        (void)hipFuncSetAttribute((const void*)key_mass_ring_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)shm);
+        (void)hipGetLastError();
+        hipLaunchKernelGGL(key_mass_ring_kernel, dim3(wgs), dim3((kMassWaves + 1) * 64), shm, s, a, ns);
+    } else {
+        // more: the direct form keeps every pair's work in its own waves
+        (void)hipFuncSetAttribute((const void*)key_mass_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)book);
+        (void)hipGetLastError();
+        hipLaunchKernelGGL(key_mass_kernel, dim3(wgs), dim3(kMassWaves * 64), book, s, a);
+    }
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t n = (size_t)a.B * a.N;
     hipLaunchKernelGGL(key_mass_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a.part, a.scores,

@@ -103,6 +103,16 @@ def test_tracked_scores_gqa_duplicates_mask():
     check_selection(wl, "gqa-dups-mask", k=33)
 
 
+def test_tracked_scores_ring_form_gqa_splits():
+    """At most 48 (row, head) pairs (20 rows x G = 2): the form that streams K
+    through the LDS ring, here with GQA, duplicates, a mask and many key
+    splits of 32 keys, so every 64-key tile ends past its split."""
+    log("case: tracked scores, ring form, GQA with key splits")
+    ls = LayerShape(B=3, N=700, d_model=256, H=4, Hkv=2, dh=128)
+    wl = make_random_case(ls, 20, seed=47, n_extra_rows=4, dup_frac=0.2, masked_vis=True, w_std=0.05)
+    check_selection(wl, "ring-gqa-splits", k=21)
+
+
 def test_tracked_scores_many_rows_two_groups():
     """More than 64 selected (row, head) pairs: the rows go through the
     registers in two groups."""
