@@ -440,7 +440,16 @@ __global__ void __launch_bounds__(256) key_mass_sum_kernel(const float* __restri
     const size_t b = t / N, p = t - b * N;
     const float* src = part + b * Hkv * (size_t)N + p;
     float s = 0.f;
-    for (int g = 0; g < Hkv; ++g) s += src[(size_t)g * N];
+    int g = 0;
+    // eight loads in flight, added in head order
+    for (; g + 8 <= Hkv; g += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(g + u) * N];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; g < Hkv; ++g) s += src[(size_t)g * N];
     scores[t] = s;
 }
 
