@@ -23,14 +23,9 @@ struct fdllm_ctx {
     float* qbuf = nullptr;
     void* sideK = nullptr;
     void* sideV = nullptr;
-    float* gpart = nullptr;
-    size_t gpart_bytes = 0;
-    uint32_t* gticket = nullptr;
-    size_t gticket_n = 0;
     float* apart = nullptr;
     float* aml = nullptr;
     size_t apart_rows = 0;        // (B*Hkv) * splits * Rpad rows available
-    uint32_t* aticket = nullptr;
     float* mpart = nullptr;       // [B * Hkv, N] per kv head sums of the tracked-set scores
     fdllm_tuning_t tune{0, 0, 0};
 };
@@ -106,12 +101,11 @@ int hip_status(hipError_t e)
 
 void free_ws(fdllm_ctx* h)
 {
-    void* ptrs[] = {h->rope, h->qbuf, h->sideK, h->sideV, h->gpart, h->gticket, h->apart, h->aml, h->aticket,
-                    h->mpart};
+    void* ptrs[] = {h->rope, h->qbuf, h->sideK, h->sideV, h->apart, h->aml, h->mpart};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     h->rope = nullptr; h->qbuf = nullptr; h->sideK = h->sideV = nullptr;
-    h->gpart = nullptr; h->gticket = nullptr; h->apart = h->aml = nullptr; h->aticket = nullptr;
+    h->apart = h->aml = nullptr;
     h->mpart = nullptr;
 }
 
@@ -119,24 +113,11 @@ void free_ws(fdllm_ctx* h)
 int ensure_split_ws(fdllm_ctx* h)
 {
     const fdllm_config_t& c = h->cfg;
-    size_t gbytes = 0, gtickets = 0, arows = 0;
+    size_t arows = 0;
     for (int nq = 1; nq <= c.q_max; ++nq) {
         const Plan p = make_plan(h, nq);
         if (p.attn_family == FAMILY_MFMA && p.splits > 1)
             arows = std::max(arows, (size_t)c.B * c.Hkv * p.splits * p.Rpad);
-    }
-    if (gbytes > h->gpart_bytes) {
-        if (h->gpart) (void)hipFree(h->gpart);
-        h->gpart = nullptr;
-        if (hipMalloc(&h->gpart, gbytes) != hipSuccess) { h->gpart_bytes = 0; return FDLLM_ERR_ALLOC; }
-        h->gpart_bytes = gbytes;
-    }
-    if (gtickets > h->gticket_n) {
-        if (h->gticket) (void)hipFree(h->gticket);
-        h->gticket = nullptr;
-        if (hipMalloc(&h->gticket, gtickets * sizeof(uint32_t)) != hipSuccess) { h->gticket_n = 0; return FDLLM_ERR_ALLOC; }
-        if (hipMemset(h->gticket, 0, gtickets * sizeof(uint32_t)) != hipSuccess) return FDLLM_ERR_HIP;
-        h->gticket_n = gtickets;
     }
     if (arows > h->apart_rows) {
         if (h->apart) (void)hipFree(h->apart);
@@ -161,16 +142,15 @@ int set_device(const fdllm_ctx* h)
 }
 
 ProjArgs proj_args(const fdllm_ctx* h, const void* X, int x_rows, const int32_t* Q_idx, const int32_t* pos,
-                   int rows_per_seq, const void* W, void* Kc, void* Vc, int prefill, int splitk)
+                   int rows_per_seq, const void* W, void* Kc, void* Vc, int prefill)
 {
     const fdllm_config_t& c = h->cfg;
     ProjArgs a{};
     a.X = X; a.W = W; a.Q_idx = Q_idx; a.pos_ids = pos; a.rope = h->rope;
     a.Kc = Kc; a.Vc = Vc; a.qbuf = h->qbuf; a.sideK = h->sideK; a.sideV = h->sideV;
-    a.gpart = h->gpart; a.gticket = h->gticket;
     a.B = c.B; a.N = c.N; a.d = c.d_model; a.H = c.H; a.Hkv = c.Hkv; a.dh = c.dh; a.G = h->G;
     a.x_rows = x_rows; a.rows_per_seq = rows_per_seq; a.q_max = c.q_max;
-    a.prefill = prefill; a.splitk = splitk;
+    a.prefill = prefill;
     a.tile_choice = prefill ? 0 : env_int("FDLLM_PROJ_TILE", 0);
     return a;
 }
@@ -206,7 +186,7 @@ int project_impl(fdllm_ctx* h, const void* X, int32_t x_rows, const int32_t* Q_i
             if (qi[t] < 0 || qi[t] >= x_rows || pi[t] < 0 || pi[t] >= c.N) return FDLLM_ERR_INDEX;
     }
     const Plan p = make_plan(h, nq);
-    ProjArgs pa = proj_args(h, X, x_rows, Q_idx, pos_ids, nq, W, Kc, Vc, 0, p.splitk);
+    ProjArgs pa = proj_args(h, X, x_rows, Q_idx, pos_ids, nq, W, Kc, Vc, 0);
     pa.map = map;
     pa.nq_seq = nq_seq;
     hipError_t e = p.proj_family == FAMILY_MFMA ? launch_proj_mfma(pa, s) : launch_proj_generic(pa, c.dtype, s);
@@ -236,7 +216,7 @@ int attend_impl(fdllm_ctx* h, const int32_t* pos_ids, int32_t nq, const uint8_t*
     AttnArgs aa{};
     aa.qbuf = h->qbuf; aa.Kc = Kc; aa.Vc = Vc; aa.sideK = h->sideK; aa.sideV = h->sideV;
     aa.pos_ids = pos_ids; aa.vis = vis; aa.O = O; aa.LSE = LSE;
-    aa.apart = h->apart; aa.aml = h->aml; aa.aticket = h->aticket;
+    aa.apart = h->apart; aa.aml = h->aml;
     aa.B = c.B; aa.N = c.N; aa.H = c.H; aa.Hkv = c.Hkv; aa.dh = c.dh; aa.G = h->G; aa.nq = nq; aa.q_max = c.q_max;
     aa.R = p.R; aa.Rpad = p.Rpad; aa.splits = p.splits; aa.keys_per_split = p.keys_per_split;
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.dh));
@@ -292,7 +272,7 @@ int fdllm_prefill(fdllm_handle_t h, const void* X, int32_t x_rows, const void* W
     if (st) return st;
     const Plan p = make_plan(h, 1);
     hipStream_t s = (hipStream_t)stream;
-    ProjArgs a = proj_args(h, X, x_rows, nullptr, nullptr, h->cfg.N, W, Kc, Vc, 1, 1);
+    ProjArgs a = proj_args(h, X, x_rows, nullptr, nullptr, h->cfg.N, W, Kc, Vc, 1);
     hipError_t e = p.proj_family == FAMILY_MFMA ? launch_proj_mfma(a, s)
                                                 : launch_proj_generic(a, h->cfg.dtype, s);
     return hip_status(e);
@@ -321,12 +301,8 @@ int fdllm_cache_init(fdllm_handle_t* out, const fdllm_config_t* cfg, const void*
               hipMalloc(&h->qbuf, qrows * c.dh * sizeof(float)) == hipSuccess &&
               hipMalloc(&h->sideK, srows * c.dh * h->elt) == hipSuccess &&
               hipMalloc(&h->sideV, srows * c.dh * h->elt) == hipSuccess &&
-              hipMalloc(&h->aticket, (size_t)c.B * c.Hkv * sizeof(uint32_t)) == hipSuccess &&
               hipMalloc(&h->mpart, (size_t)c.B * c.Hkv * c.N * sizeof(float)) == hipSuccess;
     if (!ok) { free_ws(h); delete h; return FDLLM_ERR_ALLOC; }
-    if (hipMemset(h->aticket, 0, (size_t)c.B * c.Hkv * sizeof(uint32_t)) != hipSuccess) {
-        free_ws(h); delete h; return FDLLM_ERR_HIP;
-    }
     st = ensure_split_ws(h);
     if (st) { free_ws(h); delete h; return st; }
 

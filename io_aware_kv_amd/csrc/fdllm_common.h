@@ -42,14 +42,11 @@ struct ProjArgs {
     float* qbuf;            // [B, Hkv, q_max * G, dh] fp32, row j * G + hl  (unused in prefill)
     void* sideK;            // [B, Hkv, q_max, dh]: rows whose position an earlier row owns
     void* sideV;
-    float* gpart;           // split-d partial sums
-    uint32_t* gticket;      // one counter per output tile, zero between launches
     int B, N, d, H, Hkv, dh, G;
     int x_rows;
     int rows_per_seq;       // nq, or N in prefill mode
     int q_max;
     int prefill;            // 1: k/v heads only, no q, no side buffer
-    int splitk;
     int tile_choice;        // 0: default tile configuration for the row count
     CacheMap map;           // cache layout (flat when map.table is NULL)
     const int32_t* nq_seq;  // [B] query rows of each sequence (rows j >= nq_seq[b] are padding) or NULL
@@ -67,7 +64,6 @@ struct AttnArgs {
     float* LSE;             // [B, nq, H]
     float* apart;           // [B * Hkv, splits, Rpad, dh]  unnormalised partial outputs
     float* aml;             // [B * Hkv, splits, Rpad, 2]    (max in log2 units, sum)
-    uint32_t* aticket;      // [B * Hkv], zero between launches
     int B, N, H, Hkv, dh, G, nq, q_max;
     int R;                  // nq * G query rows per (sequence, kv head)
     int Rpad;               // R rounded up for the partial buffers
