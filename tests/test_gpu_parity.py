@@ -65,7 +65,7 @@ def test_chain_mask_dependencies_on_gpu():
             assert not torch.equal(pert["O"][b, moved[b]], base["O"][b, moved[b]])
 
 
-@pytest.mark.parametrize("layer", [0, 31])
+@pytest.mark.parametrize("layer", [0, 15, 31])
 def test_large_batch_stack_layers(layer):
     log("case: workload 5 layer %d" % layer)
     wl = make_workload(5, layer=layer)
