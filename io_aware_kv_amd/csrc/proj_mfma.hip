@@ -61,6 +61,11 @@ struct ProjCfg {
     static constexpr int RBW = BM / 16 / NRW;             // row blocks per consumer wave
     static constexpr int PAIRS = NCB / 2;                 // rotary block pairs per tile
     static constexpr int PPW = PAIRS / NPW;               // pairs per consumer wave
+    static constexpr int V4 = PAIRS * 8;                  // 16 B rotary-table loads per tile row
+    // rotary-table loads per consumer lane when they are prefetched into
+    // registers before the loop (0: loaded after it, where registers are short)
+    static constexpr int RPF0 = (BM * V4 + NCW * 64 - 1) / (NCW * 64);
+    static constexpr int RPF = (NKW == 1 && RPF0 <= 22) ? RPF0 : 0;
     static_assert(BK == 64 || BK == 128, "stage depth");
     static_assert((NS - 2) * DMAP <= 63 || NS <= 2, "in-flight DMA blocks per producer");
     static_assert(BM % (16 * NRW) == 0 && PAIRS % NPW == 0 && NS >= 2, "tile shape");
@@ -145,6 +150,11 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
         for (int q = 0; q < 2 * C::PPW; ++q) acc[r][q] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int wk = wave / C::NHW;                 // consumer coordinates
     const int wr = (wave % C::NHW) / NPW, wp = wave % NPW;
+    const bool rotate = head < a.H + a.Hkv;
+    // the tile's rotary-table rows (first-half columns of its pairs), loaded
+    // by the consumer waves before the loop so the epilogue does not wait on
+    // them (16 B of (cos, sin) pairs each)
+    f32x4 ropepf[C::RPF > 0 ? C::RPF : 1];
 
     if (wave >= C::NCW) {
         // ================= producer waves =================
@@ -180,6 +190,16 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
         }
     } else {
         // ================= consumer waves =================
+        if constexpr (C::RPF > 0) {
+            if (rotate) {
+#pragma unroll
+                for (int i = 0; i < C::RPF; ++i) {
+                    const int e = min(tid + i * C::NCW * 64, BM * C::V4 - 1);
+                    const int row = e / C::V4, v = e - row * C::V4;
+                    ropepf[i] = *(const f32x4*)&a.rope[(size_t)sPos[row] * (kDH / 2) + p0 * 16 + 2 * v];
+                }
+            }
+        }
         if (!a.prefill && head >= a.H) {
             // first-occurrence rule: a row owns the cache write of its
             // position unless an earlier row of its sequence has the same one
@@ -261,15 +281,27 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
     // table rows of the tile's positions (first-half columns of its pairs)
     // are first staged in the free ring with all loads in flight at once.
     const bool consumer = wave < C::NHW;             // the waves that hold the finished tile
-    const bool rotate = head < a.H + a.Hkv;
     if (rotate) {
         constexpr int PC = C::PAIRS * 16;                  // table columns of the tile
         float2* sCS = (float2*)smem;                       // [BM][PC]
-        constexpr int V4 = PC / 2;                         // 16 B loads per row
-        for (int e = tid; e < BM * V4; e += C::NT) {
-            const int row = e / V4, v = e - row * V4;
-            *(f32x4*)&sCS[row * PC + 2 * v] =
-                *(const f32x4*)&a.rope[(size_t)sPos[row] * (kDH / 2) + p0 * 16 + 2 * v];
+        constexpr int V4 = C::V4;
+        if constexpr (C::RPF > 0) {
+            if (consumer) {
+#pragma unroll
+                for (int i = 0; i < C::RPF; ++i) {
+                    const int e = tid + i * C::NCW * 64;
+                    if (e < BM * V4) {
+                        const int row = e / V4, v = e - row * V4;
+                        *(f32x4*)&sCS[row * PC + 2 * v] = ropepf[i];
+                    }
+                }
+            }
+        } else {
+            for (int e = tid; e < BM * V4; e += C::NT) {
+                const int row = e / V4, v = e - row * V4;
+                *(f32x4*)&sCS[row * PC + 2 * v] =
+                    *(const f32x4*)&a.rope[(size_t)sPos[row] * (kDH / 2) + p0 * 16 + 2 * v];
+            }
         }
         __syncthreads();
         if (consumer) {
