@@ -45,7 +45,7 @@ namespace {
 
 constexpr int kDH = 128;
 constexpr int kRowB = kDH * 2;        // bytes of one K or V row
-constexpr int kRing = 128 * 1024;     // LDS ring of K/V stages per workgroup
+constexpr int kRing = 128 * 1024;     // LDS ring of K/V stages per workgroup (default)
 constexpr int kMaxChunks = 5;         // query rows per sequence, in chunks of 64 (R <= 288)
 constexpr float kNegBig = -1.0e30f;   // running max of a row that has seen no key
 
@@ -56,19 +56,19 @@ typedef __attribute__((address_space(1))) void glb_void;
 
 // RG row groups of 16 query rows per consumer wave, NWR x NWK consumer waves
 // (rows x keys of a tile), NPROD producer waves.
-template <int RG, int NWR, int NWK, int NPROD>
+template <int RG, int NWR, int NWK, int NPROD, int RING = kRing>
 struct AttnCfg {
     static constexpr int NC = NWR * NWK;            // consumer waves
     static constexpr int NT = (NC + NPROD) * 64;
     static constexpr int KW = 32;                   // keys per consumer wave per tile
     static constexpr int TK = KW * NWK;             // keys per tile
     static constexpr int STAGE = TK * 2 * kRowB;    // K rows then V rows
-    static constexpr int NS = kRing / STAGE;
+    static constexpr int NS = RING / STAGE;
     static constexpr int DMA = STAGE / 1024;        // 1 KB DMA instructions per stage
     static constexpr int DMAP = DMA / NPROD;        // ... issued by each producer wave
     static constexpr int MERGE = (NWK / 2) * NWR * RG * 64 * (32 + 2) * 4;
     static constexpr int SCRATCH = NS * STAGE > MERGE ? NS * STAGE : MERGE;
-    static_assert(NS >= 2 && NS * STAGE == kRing, "stage ring");
+    static_assert(NS >= 2 && NS * STAGE == RING, "stage ring");
     static_assert(DMA % (2 * NPROD) == 0, "K and V halves split evenly over the producers");
 };
 
@@ -178,11 +178,11 @@ __device__ __forceinline__ void issue_dup(unsigned char* st, int base, int ndup,
     }
 }
 
-template <int RG, int NWR, int NWK, int NPROD>
+template <int RG, int NWR, int NWK, int NPROD, int RING>
 __global__ void __launch_bounds__((NWR * NWK + NPROD) * 64)
 attn_mfma_kernel(AttnArgs a)
 {
-    using C = AttnCfg<RG, NWR, NWK, NPROD>;
+    using C = AttnCfg<RG, NWR, NWK, NPROD, RING>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     const int kps = a.keys_per_split;
     const int nq = a.nq;
@@ -789,10 +789,10 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a)
     if (d4 == 0) a.LSE[orow] = L > 0.f ? (mx + log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
-template <int RG, int NWR, int NWK, int NPROD>
+template <int RG, int NWR, int NWK, int NPROD, int RING = kRing>
 hipError_t launch_cfg(const AttnArgs& a, hipStream_t s)
 {
-    using C = AttnCfg<RG, NWR, NWK, NPROD>;
+    using C = AttnCfg<RG, NWR, NWK, NPROD, RING>;
     if (a.nq > 64 * kMaxChunks || a.keys_per_split % C::TK != 0) return hipErrorInvalidValue;
     const int VW = (a.nq + 31) / 32;
     const int tiles = (a.keys_per_split + C::TK - 1) / C::TK;
@@ -802,7 +802,7 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s)
     const size_t shm = C::SCRATCH + book;
     const int total = a.B * a.Hkv * a.splits;
     const int grid = ((total + 7) / 8) * 8;
-    auto kern = attn_mfma_kernel<RG, NWR, NWK, NPROD>;
+    auto kern = attn_mfma_kernel<RG, NWR, NWK, NPROD, RING>;
     // raise the dynamic LDS limit; a refusal shows up as a launch error below
     (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
     (void)hipGetLastError();
@@ -834,7 +834,12 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s)
     if (r16 <= 1) return launch_cfg<1, 1, 2, 1>(a, s);
     if (r16 <= 2) return launch_cfg<1, 2, 2, 2>(a, s);
     if (r16 <= 3) return launch_cfg<1, 3, 2, 2>(a, s);
-    if (r16 <= 4) return launch_cfg<1, 4, 2, 2>(a, s);
+    if (r16 <= 4) {
+        // more workgroups than CUs: 32-key tiles in a 64 KB ring, so two
+        // workgroups share a CU and the launch runs in one round
+        if ((long)a.B * a.Hkv * a.splits > 256) return launch_cfg<1, 4, 1, 2, 64 * 1024>(a, s);
+        return launch_cfg<1, 4, 2, 2>(a, s);
+    }
     if (r16 <= 6) return launch_cfg<2, 3, 2, 2>(a, s);
     if (r16 <= 10) return launch_cfg<2, 5, 1, 2>(a, s);
     if (r16 <= 14) return launch_cfg<2, 7, 1, 1>(a, s);

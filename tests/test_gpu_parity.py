@@ -87,6 +87,10 @@ SMALL = [
      dict(n_extra_rows=10, dup_frac=0.05, masked_vis=True)),
     ("large-mask-aligned", dict(B=1, N=500, d_model=256, H=2, Hkv=2, dh=128), 208,
      dict(n_extra_rows=16, dup_frac=0.05, masked_vis=True)),
+    # more (sequence, kv head) workgroups than CUs with up to 64 rows per kv
+    # head: the 32-key, 64 KB-ring layout that puts two workgroups on a CU
+    ("many-workgroups", dict(B=40, N=200, d_model=128, H=16, Hkv=8, dh=128), 13,
+     dict(n_extra_rows=3, dup_frac=0.2, masked_vis=True)),
     ("fp32-generic", dict(B=2, N=50, d_model=64, H=4, Hkv=2, dh=32, dtype=torch.float32), 7,
      dict(n_extra_rows=2, dup_frac=0.3, masked_vis=True)),
     ("fp32-dh64", dict(B=1, N=90, d_model=96, H=2, Hkv=2, dh=64, dtype=torch.float32), 5, dict()),
