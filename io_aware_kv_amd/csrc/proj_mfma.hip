@@ -412,11 +412,10 @@ hipError_t launch_tile(const ProjArgs& a, hipStream_t s)
 }  // namespace
 
 // Tile configurations (rows BM x 16-column blocks NCB): narrow tiles with a
-// 3-stage ring (two workgroups per CU) for a few rows, 64 x 64 tiles up to
-// 128 rows, and 128-column (one head) tiles beyond, as tall as needed to fit
-// every tile into a single round of the 256 CUs; the tallest (208 rows) splits
-// each stage's MFMA steps between two wave groups (choice 9; choice 7 is the
-// same tile without the split).  Measured on MI355X over the layer workloads.
+// 3-stage ring (two workgroups per CU), 64 x 64 tiles, and 128-column (one
+// head) tiles as tall as needed to fit every tile into a single round of the
+// 256 CUs; the tallest (208 rows) splits each stage's MFMA steps between two
+// wave groups (choice 9; choice 7 is the same tile without the split).
 struct ProjChoice { int bm, ncb; };
 static const ProjChoice kProjChoices[] = {
     {0, 0},
@@ -426,15 +425,19 @@ static const ProjChoice kProjChoices[] = {
 };
 constexpr int kNumChoices = (int)(sizeof(kProjChoices) / sizeof(kProjChoices[0]));
 
+// The loop of a tile is bound by the bytes its CU takes in from the L2 (X
+// and W rows), so the choice trades tile area against idle CUs.  Measured on
+// MI355X with d_model 4096, 1..352 rows, 48 and 96 heads: the narrow tiles
+// lead only for up to 32 rows of few heads (by up to 1.3 us), 64 x 64 tiles
+// everywhere else up to 128 rows (up to 4 us ahead of the narrow ones at 96
+// heads), and beyond that the 96-row head tiles whenever they fit one round
+// (1-4 us ahead of 128-row tiles at 160-256 rows), else the shortest head
+// tile that does.
 static int default_choice(int M, int heads)
 {
-    if (M <= 16) return 1;
-    // a few rows past 32 (the draft pass's 1 + 32 rows) still run faster as
-    // two 32-row tiles than as one 48-row tile (measured at M = 33)
-    if (M <= 36) return 2;
-    if (M <= 48) return 3;
+    if (M <= 32 && heads < 64) return M <= 16 ? 1 : 2;
     if (M <= 128) return 4;
-    for (int c : {5, 6, 9})
+    for (int c : {8, 5, 6, 9})
         if ((long)((M + kProjChoices[c].bm - 1) / kProjChoices[c].bm) * heads <= 256) return c;
     return 5;
 }
