@@ -426,20 +426,28 @@ static const ProjChoice kProjChoices[] = {
 constexpr int kNumChoices = (int)(sizeof(kProjChoices) / sizeof(kProjChoices[0]));
 
 // The loop of a tile is bound by the bytes its CU takes in from the L2 (X
-// and W rows), so the choice trades tile area against idle CUs.  Measured on
-// MI355X with d_model 4096, 1..352 rows, 48 and 96 heads: the narrow tiles
-// lead only for up to 32 rows of few heads (by up to 1.3 us), 64 x 64 tiles
-// everywhere else up to 128 rows (up to 4 us ahead of the narrow ones at 96
-// heads), and beyond that the 96-row head tiles whenever they fit one round
-// (1-4 us ahead of 128-row tiles at 160-256 rows), else the shortest head
-// tile that does.
+// and W rows), so the choice trades tile area against idle CUs and extra
+// rounds.  Measured on MI355X with d_model 4096, 1..1408 rows, 48 and 96
+// heads: the narrow tiles lead only for up to 32 rows of few heads (by up to
+// 1.3 us), 64 x 64 tiles everywhere else up to 128 rows (up to 4 us ahead of
+// the narrow ones at 96 heads).  Beyond 128 rows the order of the measured
+// times follows the staged rows per CU: rounds of 256 workgroups x (BM + BN)
+// (1408 rows of 96 heads: 176-row tiles in 3 rounds, 160 us, against 205 us
+// for 128-row tiles in 4.1 rounds).  The 208-row tile runs with its k split
+// (faster than without at every row count measured).
 static int default_choice(int M, int heads)
 {
     if (M <= 32 && heads < 64) return M <= 16 ? 1 : 2;
     if (M <= 128) return 4;
-    for (int c : {8, 5, 6, 9})
-        if ((long)((M + kProjChoices[c].bm - 1) / kProjChoices[c].bm) * heads <= 256) return c;
-    return 5;
+    int best = 5;
+    long best_cost = -1;
+    for (int c : {4, 8, 5, 6, 9}) {
+        const ProjChoice& p = kProjChoices[c];
+        const long tiles = (long)((M + p.bm - 1) / p.bm) * heads * (8 / p.ncb);
+        const long cost = ((tiles + 255) / 256) * (p.bm + 16 * p.ncb);
+        if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = c; }
+    }
+    return best;
 }
 
 ProjTile proj_mfma_tile(int M, int heads, int choice)
