@@ -229,30 +229,31 @@ def time_decision(wl, stream, iters):
             "confidence_hbm_frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
-def time_paged(fk, wl, stream, iters, block_size=16):
+def time_paged(fk, wl, stream, iters, n_sets, warmup, block_size=16):
     """Time the fused step over a paged cache (blocks of 16 positions in a
-    seeded random order, full lengths and row counts) on two pool sets."""
+    seeded random order, full lengths and row counts), with the flat step's
+    protocol: n_sets buffer sets in rotation (each its own X, W and pools),
+    `warmup` untimed steps, then `iters` timed steps back to back."""
     import torch
     from io_aware_kv_amd.workloads import paged_layout
     ls = wl.shape
     dev = torch.device("cuda")
     table, Kpool, Vpool, L, nb = paged_layout(wl, block_size, ragged=False)
     sets = []
-    for _ in range(2):
-        sets.append(dict(K=Kpool.to(dev), V=Vpool.to(dev),
+    for _ in range(n_sets):
+        sets.append(dict(X=wl.X.to(dev), W=wl.W.to(dev), K=Kpool.to(dev), V=Vpool.to(dev),
                          O=torch.empty((ls.B, wl.nq, ls.H, ls.dh), dtype=ls.dtype, device=dev),
                          LSE=torch.empty((ls.B, wl.nq, ls.H), dtype=torch.float32, device=dev)))
-    X, W = wl.X.to(dev), wl.W.to(dev)
     Q, P = wl.Q_idx.to(dev), wl.pos_ids.to(dev)
     vis = wl.vis.to(dev) if wl.vis is not None else None
     tab, Ld, nbd = table.to(dev), L.to(dev), nb.to(dev)
 
     def run(i):
-        st = sets[i % 2]
-        fk.step_paged(X, Q, P, vis, W, st["K"], st["V"], st["O"], st["LSE"], block_table=tab,
+        st = sets[i % n_sets]
+        fk.step_paged(st["X"], Q, P, vis, st["W"], st["K"], st["V"], st["O"], st["LSE"], block_table=tab,
                       block_size=block_size, num_blocks=Kpool.shape[0], seq_len=Ld, nq_seq=nbd, stream=stream)
 
-    for i in range(3):
+    for i in range(warmup):
         run(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -261,6 +262,7 @@ def time_paged(fk, wl, stream, iters, block_size=16):
         run(i)
     e1.record(stream)
     torch.cuda.synchronize()
+    del sets
     return {"block_size": block_size, "step_us": round(e0.elapsed_time(e1) / iters * 1e3, 3)}
 
 
@@ -387,7 +389,7 @@ def main():
             (decision["rows"], decision["vocab"], decision["confidence_us"], decision["confidence_GBps"],
              decision["accept_us"]))
         selection["decision"] = decision
-        paged = time_paged(fk, wl, stream, min(args.steps, 50))
+        paged = time_paged(fk, wl, stream, args.steps, n_sets, args.warmup)
         log("bench: paged cache (blocks of %d) step %.2f us" % (paged["block_size"], paged["step_us"]))
         selection["paged_step"] = paged
 
