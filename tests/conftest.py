@@ -14,8 +14,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped cleanly where no GPU is visible (they are meant for
-    # the GPU box; -m "not gpu" deselects them anyway).
+    # GPU tests are skipped cleanly where no GPU is visible (they need an
+    # MI355X; -m "not gpu" deselects them anyway).
     try:
         import torch
         has_gpu = torch.cuda.is_available()
