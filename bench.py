@@ -284,7 +284,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(--gpus %d requested; run with --gpus 1)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
