@@ -112,6 +112,20 @@ def run_copy(args):
                       "GBps": 2 * n * 4 / dt / 1e9}))
 
 
+def host_info():
+    """CPU model and thread count of the host the bench ran on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count()}
+
+
 def cpu_oracle_baseline(wl, K0, V0, budget_s):
     """Time the fp64 oracle (as it stands) on the host on the same inputs."""
     import oracle
@@ -131,7 +145,7 @@ def cpu_oracle_baseline(wl, K0, V0, budget_s):
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start > budget_s or len(times) >= 64:
             break
-    return r, sum(times) / len(times), len(times), oracle.threads()
+    return r, sorted(times)[len(times) // 2], len(times), oracle.threads()
 
 
 def time_selection(fk, wl, sets, stream, iters):
@@ -365,6 +379,27 @@ def main():
     attn_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
     proj_avg = sum(proj_ms) / len(proj_ms)
     attn_avg = sum(attn_ms) / len(attn_ms)
+    step_ms = sorted(e[0].elapsed_time(e[2]) for e in evs)
+
+    def pct(v):
+        n = len(v)
+        return {"p10": round(v[n // 10] * 1e3, 3), "p50": round(v[n // 2] * 1e3, 3),
+                "p90": round(v[min(n - 1, (n * 9) // 10)] * 1e3, 3)}
+
+    # the device's achievable streaming rate beside the 8 TB/s spec: a plain
+    # 1 GiB device copy on the same stream (bytes read + written per second)
+    cx = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cy = torch.empty_like(cx)
+    for _ in range(3):
+        cy.copy_(cx)
+    ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ce0.record(stream)
+    for _ in range(10):
+        cy.copy_(cx)
+    ce1.record(stream)
+    torch.cuda.synchronize()
+    copy_GBps = 2 * cx.numel() * 4 / (ce0.elapsed_time(ce1) / 10 * 1e-3) / 1e9
+    del cx, cy
     log("bench: %.2f us/step (proj %.2f us, attn %.2f us), wall %.3f s" %
         (ms_per_step * 1e3, proj_avg * 1e3, attn_avg * 1e3, wall))
 
@@ -450,8 +485,14 @@ def main():
             "attn_GBps": round(ab["attn"] / (attn_avg * 1e-3) / 1e9, 1),
             "proj_mfma_frac": round(ab["qkv_flops"] / (proj_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "attn_hbm_frac": round(ab["attn"] / (attn_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            # distribution over the evented pass (an event around each launch)
+            "proj_us_pct": pct(proj_ms),
+            "attn_us_pct": pct(attn_ms),
+            "step_us_pct": pct(step_ms),
         },
         "algorithmic_bytes_per_step": ab["total"],
+        "device_copy_GBps": round(copy_GBps, 1),
+        "host": host_info(),
         "next_rows": selection,
         "roofline": roofline,
         "cpu_baseline": None,
@@ -463,7 +504,7 @@ def main():
         result["cpu_baseline"] = {"value": round(ab["total"] / cpu_s / 1e9, 4), "unit": "GB/s",
                                   "cores": threads, "kind": "oracle",
                                   "sample": "the full step of this workload (all %d sequences), "
-                                            "%d run(s), %.2f s each" % (ls.B, reps, cpu_s)}
+                                            "median of %d run(s), %.2f s" % (ls.B, reps, cpu_s)}
         # parity of the timed path against the oracle on set 0
         import numpy as np
         o = sets[0]["O"].double().cpu().numpy()
