@@ -152,6 +152,8 @@ TOPK_CASES = [
     ("all-equal", 2, 3000, 50, "equal"),
     ("signs-and-zeros", 2, 777, 64, "signed"),
     ("k-one", 4, 2048, 1, "ties"),
+    ("k-256", 2, 4096, 256, "ties"),           # the rank-count sort's largest slot count
+    ("k-257", 1, 4096, 257, "ties"),           # one past it: the bitonic network
 ]
 
 
