@@ -91,6 +91,10 @@ SMALL = [
     # head: the 32-key, 64 KB-ring layout that puts two workgroups on a CU
     ("many-workgroups", dict(B=40, N=200, d_model=128, H=16, Hkv=8, dh=128), 13,
      dict(n_extra_rows=3, dup_frac=0.2, masked_vis=True)),
+    # more than 288 query rows per kv head (48 rows x 8 heads): the MFMA
+    # projection with the scalar attention kernel
+    ("gqa8-rows-past-mfma-attention", dict(B=2, N=260, d_model=256, H=16, Hkv=2, dh=128), 48,
+     dict(n_extra_rows=6, dup_frac=0.1, masked_vis=True)),
     ("fp32-generic", dict(B=2, N=50, d_model=64, H=4, Hkv=2, dh=32, dtype=torch.float32), 7,
      dict(n_extra_rows=2, dup_frac=0.3, masked_vis=True)),
     ("fp32-dh64", dict(B=1, N=90, d_model=96, H=2, Hkv=2, dh=64, dtype=torch.float32), 5, dict()),
@@ -103,6 +107,8 @@ def test_small_cases(label, shape, nq, kw):
     ls = LayerShape(**shape)
     wl = make_random_case(ls, nq, seed=zlib.crc32(label.encode()) % 10000, w_std=0.05, **kw)
     g = run_gpu(wl)
+    if label.startswith("gqa8-rows-past"):
+        assert g["plan"]["kernel_family"] == 1     # the projection stays on MFMA
     r = run_oracle(wl)
     compare(wl, g, r, label)
 
