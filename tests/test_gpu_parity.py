@@ -98,6 +98,9 @@ SMALL = [
     ("fp32-generic", dict(B=2, N=50, d_model=64, H=4, Hkv=2, dh=32, dtype=torch.float32), 7,
      dict(n_extra_rows=2, dup_frac=0.3, masked_vis=True)),
     ("fp32-dh64", dict(B=1, N=90, d_model=96, H=2, Hkv=2, dh=64, dtype=torch.float32), 5, dict()),
+    # a 64-wide head in bf16: the scalar kernels (the MFMA ones take 128)
+    ("bf16-dh64", dict(B=2, N=120, d_model=128, H=4, Hkv=2, dh=64), 9,
+     dict(n_extra_rows=3, dup_frac=0.2, masked_vis=True)),
 ]
 
 
@@ -109,6 +112,8 @@ def test_small_cases(label, shape, nq, kw):
     g = run_gpu(wl)
     if label.startswith("gqa8-rows-past"):
         assert g["plan"]["kernel_family"] == 1     # the projection stays on MFMA
+    if label == "bf16-dh64":
+        assert g["plan"]["kernel_family"] == 2
     r = run_oracle(wl)
     compare(wl, g, r, label)
 
