@@ -413,15 +413,16 @@ hipError_t launch_tile(const ProjArgs& a, hipStream_t s)
 
 // Tile configurations (rows BM x 16-column blocks NCB): narrow tiles with a
 // 3-stage ring (two workgroups per CU), 64 x 64 tiles, and 128-column (one
-// head) tiles as tall as needed to fit every tile into a single round of the
-// 256 CUs; the tallest (208 rows) splits each stage's MFMA steps between two
-// wave groups (choice 9; choice 7 is the same tile without the split).
+// head) tiles of 96 to 256 rows; the 208-row tile splits each stage's MFMA
+// steps between two wave groups (choice 9; choice 7 is the same tile without
+// the split), the 256-row tile runs eight consumer waves in a 2 x 4 layout.
 struct ProjChoice { int bm, ncb; };
 static const ProjChoice kProjChoices[] = {
     {0, 0},
     {16, 2}, {32, 2}, {48, 2}, {64, 4},   // 1-4
     {128, 8}, {176, 8}, {208, 8}, {96, 8},  // 5-8
     {208, 8},                             // 9
+    {256, 8},                             // 10
 };
 constexpr int kNumChoices = (int)(sizeof(kProjChoices) / sizeof(kProjChoices[0]));
 
@@ -433,15 +434,17 @@ constexpr int kNumChoices = (int)(sizeof(kProjChoices) / sizeof(kProjChoices[0])
 // the narrow ones at 96 heads).  Beyond 128 rows the order of the measured
 // times follows the staged rows per CU: rounds of 256 workgroups x (BM + BN)
 // (1408 rows of 96 heads: 176-row tiles in 3 rounds, 160 us, against 205 us
-// for 128-row tiles in 4.1 rounds).  The 208-row tile runs with its k split
-// (faster than without at every row count measured).
+// for 128-row tiles in 4.1 rounds, and 172 us for 256-row tiles in 2.25;
+// 1152 rows: 256-row tiles in 2 rounds, 119 us, against 154 us for 176-row
+// tiles in 2.6).  The 208-row tile runs with its k split (faster than without
+// at every row count measured).
 static int default_choice(int M, int heads)
 {
     if (M <= 32 && heads < 64) return M <= 16 ? 1 : 2;
     if (M <= 128) return 4;
     int best = 5;
     long best_cost = -1;
-    for (int c : {4, 8, 5, 6, 9}) {
+    for (int c : {4, 8, 5, 6, 9, 10}) {
         const ProjChoice& p = kProjChoices[c];
         const long tiles = (long)((M + p.bm - 1) / p.bm) * heads * (8 / p.ncb);
         const long cost = ((tiles + 255) / 256) * (p.bm + 16 * p.ncb);
@@ -472,6 +475,7 @@ hipError_t launch_proj_mfma(const ProjArgs& a, hipStream_t s)
         case 7: return launch_tile<208, 8, 1, 1, 4, 8, 64, 2>(a, s);
         case 8: return launch_tile<96, 8, 1, 1, 4, 8, 64, 2>(a, s);
         case 9: return launch_tile<208, 8, 2, 1, 2, 8, 64, 2>(a, s);
+        case 10: return launch_tile<256, 8, 1, 2, 4, 8, 64, 2>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

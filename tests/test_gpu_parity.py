@@ -130,7 +130,7 @@ def test_forced_splits(splits, nq):
     compare(wl, g, r, "splits%d-nq%d" % (splits, nq))
 
 
-@pytest.mark.parametrize("choice", list(range(1, 10)))
+@pytest.mark.parametrize("choice", list(range(1, 11)))
 def test_forced_projection_tiles(choice, monkeypatch):
     """Every projection tile configuration (FDLLM_PROJ_TILE) on a case with
     ragged row tiles, GQA, duplicates and a mask."""
