@@ -13,7 +13,11 @@ measure LLaDA-1.5 on public benchmarks; no weights or data are used here, the
 seeded tensors below stand in for them.
 
 All tensors are created on the CPU with a seeded ``torch.Generator`` in fp32
-and cast once (round to nearest even) to the layer's storage dtype.
+and cast once (round to nearest even) to the layer's storage dtype: hidden
+states X ~ N(0, 1) and weights W ~ N(0, w_std^2) with every bit of the storage
+type's significand in use.  ``grid=True`` instead snaps them to a coarse dyadic
+grid (see X_GRID) for the checks that need an fp32 projection exact in any
+summation order.
 """
 from __future__ import annotations
 
@@ -78,12 +82,14 @@ NAMES = {
 BASE_SEED = 20260
 
 
-# Hidden states and weights are normal draws rounded to a dyadic grid: X to
-# multiples of 1/8 (std 1), W to multiples of 1/512 (std w_std).  Every
-# product x*w is then a multiple of 2^-12 and every partial sum of a row's
-# projection (d_model <= 4096 terms, magnitude far below 2^11) fits in fp32's
-# 24-bit significand, so the projection is exact in fp32 in any summation
-# order.  The stored k/v rounding then depends on the rotary step alone.
+# The optional dyadic grid (grid=True): X rounded to multiples of 1/8 (std 1),
+# W to multiples of 1/512 (std w_std).  Every product x*w is then a multiple of
+# 2^-12 and every partial sum of a row's projection (d_model <= 4096 terms,
+# magnitude far below 2^11) fits in fp32's 24-bit significand, so the
+# projection is exact in fp32 in any summation order and the stored k/v
+# rounding depends on the rotary step alone.  Such values carry at most six
+# significant bits, so these inputs serve bit-level checks of the stored rows
+# only; the default inputs use the full bf16 significand.
 X_GRID = 2.0 ** -3
 W_GRID = 2.0 ** -9
 
@@ -103,24 +109,26 @@ def _perm(g, n):
     return torch.randperm(n, generator=g).tolist()
 
 
-def hidden_and_weights(shape: LayerShape, x_rows: int, g: torch.Generator, w_std: float = 0.02):
-    X_pre = _randn(g, (shape.B, shape.N, shape.d_model), 1.0, shape.dtype, X_GRID)
-    W = _randn(g, (shape.cols, shape.d_model), w_std, shape.dtype, W_GRID)
+def hidden_and_weights(shape: LayerShape, x_rows: int, g: torch.Generator, w_std: float = 0.02,
+                       grid: bool = False):
+    X_pre = _randn(g, (shape.B, shape.N, shape.d_model), 1.0, shape.dtype, X_GRID if grid else None)
+    W = _randn(g, (shape.cols, shape.d_model), w_std, shape.dtype, W_GRID if grid else None)
     return X_pre, W
 
 
-def step_hidden(shape: LayerShape, X_pre, Q_idx, x_rows, g):
+def step_hidden(shape: LayerShape, X_pre, Q_idx, x_rows, g, grid: bool = False):
     """Hidden states of the step: the prefill states with the query rows (and
     any rows past N) redrawn, so that the step's cache writes are observable."""
     B, N, d = X_pre.shape
+    xg = X_GRID if grid else None
     X = torch.empty((B, x_rows, d), dtype=shape.dtype)
     X[:, :N] = X_pre
     if x_rows > N:
-        X[:, N:] = _randn(g, (B, x_rows - N, d), 1.0, shape.dtype, X_GRID)
+        X[:, N:] = _randn(g, (B, x_rows - N, d), 1.0, shape.dtype, xg)
     for b in range(B):
         rows = sorted(set(int(r) for r in Q_idx[b].tolist() if r < N))
         if rows:
-            X[b, rows] = _randn(g, (len(rows), d), 1.0, shape.dtype, X_GRID)
+            X[b, rows] = _randn(g, (len(rows), d), 1.0, shape.dtype, xg)
     return X
 
 
@@ -161,10 +169,12 @@ def view_chain_mask(groups: List[List[str]]) -> torch.Tensor:
     return vis
 
 
-def make_workload(cid: int, layer: int = 0, w_std: float = 0.02, n_confident: int = 32) -> Workload:
+def make_workload(cid: int, layer: int = 0, w_std: float = 0.02, n_confident: int = 32,
+                  grid: bool = False) -> Workload:
     """The layer configurations, seeded with 20260 + id (+1000 per layer).
     n_confident sets how many of the 64 window positions the verification
-    pass (7) takes as confident; the rest are exploratory."""
+    pass (7) takes as confident; the rest are exploratory.  grid=True snaps
+    X and W to the dyadic grid (same seeds, same index sets)."""
     shape = SHAPES[cid]
     seed = BASE_SEED + cid + 1000 * layer
     g = torch.Generator().manual_seed(seed)
@@ -255,9 +265,10 @@ def make_workload(cid: int, layer: int = 0, w_std: float = 0.02, n_confident: in
         meta["groups"] = groups
     else:
         raise ValueError("unknown configuration %r" % cid)
-    X_pre, W = hidden_and_weights(shape, x_rows, g, w_std)
-    X = step_hidden(shape, X_pre, Q, x_rows, g)
+    X_pre, W = hidden_and_weights(shape, x_rows, g, w_std, grid)
+    X = step_hidden(shape, X_pre, Q, x_rows, g, grid)
     meta["w_std"] = w_std
+    meta["grid"] = grid
     name = NAMES[cid] if cid != 7 else NAMES[cid].replace("|Q|=176", "|Q|=%d" % nq)
     return Workload(name, shape, nq, x_rows, seed, X_pre, X, W, Q.contiguous(),
                     P.contiguous(), vis, meta)
@@ -265,7 +276,7 @@ def make_workload(cid: int, layer: int = 0, w_std: float = 0.02, n_confident: in
 
 def make_random_case(shape: LayerShape, nq: int, seed: int, *, n_extra_rows: int = 0,
                      dup_frac: float = 0.0, masked_vis: bool = False, w_std: float = 0.02,
-                     positions: Optional[List[List[int]]] = None) -> Workload:
+                     positions: Optional[List[List[int]]] = None, grid: bool = False) -> Workload:
     """Small generic case for parity tests: random distinct positions per
     sequence, optionally some rows duplicated at an earlier row's position
     (reading from X rows past N, like a second view), and an optional random
@@ -301,10 +312,10 @@ def make_random_case(shape: LayerShape, nq: int, seed: int, *, n_extra_rows: int
     vis = None
     if masked_vis and nq > 0:
         vis = (torch.rand((B, nq, nq), generator=g) < 0.7).to(torch.uint8)
-    X_pre, W = hidden_and_weights(shape, x_rows, g, w_std)
-    X = step_hidden(shape, X_pre, Q, x_rows, g)
+    X_pre, W = hidden_and_weights(shape, x_rows, g, w_std, grid)
+    X = step_hidden(shape, X_pre, Q, x_rows, g, grid)
     return Workload("random", shape, nq, x_rows, seed, X_pre, X, W, Q.contiguous(),
-                    P.contiguous(), vis, {"w_std": w_std})
+                    P.contiguous(), vis, {"w_std": w_std, "grid": grid})
 
 
 CACHE_SEED_OFFSET = 7_000_003

@@ -3,9 +3,8 @@ lengths and query counts (fdllm_fused_step_paged), against the oracle's
 definition (oracle.step_paged) and against the flat step.
 
 Bar: as for the flat step (written k/v and O within 2e-2 / 1e-4 relative of
-the oracle's magnitude, LSE within 1e-3 absolute beyond the rounding-tie
-slack of the flat comparison's reading); padding rows exactly 0 / -inf; pool
-rows the step does not write bit-exact.  With full lengths and row counts the
+the oracle's magnitude, LSE within 1e-3 absolute); padding rows exactly
+0 / -inf; pool rows the step does not write bit-exact.  With full lengths and row counts the
 paged step must reproduce the flat step bit for bit (the kernels visit the
 same keys in the same order; only the addresses differ).
 """

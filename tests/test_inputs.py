@@ -1,8 +1,9 @@
-"""The seeded input recipe: hidden states and weights sit on their dyadic
-grids after the cast to the storage dtype, and the projection's partial sums
-stay inside fp32's exact range, so that the stored rows' rounding is decided
-by the rotary step alone; the tie test of the parity helpers behaves as its
-derivation says."""
+"""The seeded input recipe: by default hidden states and weights are normal
+draws with the stated spreads that use the storage type's whole significand;
+with grid=True they sit on their dyadic grids after the cast to the storage
+dtype, and the projection's partial sums stay inside fp32's exact range, so
+that the stored rows' rounding is decided by the rotary step alone; the tie
+test of the parity helpers behaves as its derivation says."""
 import sys
 import os
 
@@ -20,10 +21,29 @@ def _on_grid(t, grid):
     return bool(torch.equal(a, torch.round(a)))
 
 
+@pytest.mark.parametrize("cid", [2, 3, 4])
+def test_default_inputs_full_significand_with_stated_spreads(cid):
+    """X ~ N(0, 1) and W ~ N(0, 0.02^2), cast once to bf16, not on any grid:
+    about half the elements have the last significand bit set, and the
+    sample spreads match the stated ones."""
+    wl = make_workload(cid)
+    assert not wl.meta["grid"]
+    for t, std in ((wl.X, 1.0), (wl.W, 0.02)):
+        low = (t.view(torch.int16) & 1).double().mean().item()
+        assert 0.45 < low < 0.55, low
+        assert abs(t.double().std().item() / std - 1.0) < 0.01
+        assert not _on_grid(t, X_GRID if std == 1.0 else W_GRID)
+
+
 @pytest.mark.parametrize("cid", [1, 2, 3, 4, 5, 6, 7])
 def test_workload_inputs_on_grid_and_exact_in_fp32(cid):
-    wl = make_workload(cid)
+    wl = make_workload(cid, grid=True)
+    assert wl.meta["grid"]
     assert _on_grid(wl.X, X_GRID) and _on_grid(wl.W, W_GRID)
+    # same seeds, same index sets as the default inputs
+    wd = make_workload(cid) if cid in (1, 2) else None
+    if wd is not None:
+        assert torch.equal(wd.Q_idx, wl.Q_idx) and torch.equal(wd.pos_ids, wl.pos_ids)
     # every partial sum of a query row's projection is a multiple of
     # X_GRID * W_GRID = 2^-12 bounded by sum |x||w|; exact in fp32 while that
     # bound stays below 2^(24 - 12)
