@@ -12,12 +12,17 @@ round robin so that no step finds its data in the 256 MB Infinity Cache.
 Prints one JSON line.  `value` is the achieved HBM bandwidth of the whole
 step counted in algorithmic bytes (weights once, the gathered X rows, the new
 k/v rows, one full read of K and V, O and LSE) divided by the step time;
-`roofline` is the dominant kernel's algorithmic bytes over its average
-launch time (HIP events on the launch stream) against the 8 TB/s HBM peak;
+`roofline` is the dominant kernel's algorithmic bytes (or flops, past the
+ridge point) over its average launch time (HIP events around that launch kind
+alone, back to back on the launch stream) against the 8 TB/s HBM peak (or
+2.5 PFLOP/s bf16); `configs` carries the same step and phase figures for the
+other layer workloads of the target set;
 `cpu_baseline` is the fp64 CPU oracle timed on the host on the same inputs.
 
   python bench.py [--steps K] [--warmup W] [--config 3] [--sets S] [--no-cpu]
+                  [--other-configs 1,2,4]
   python bench.py --mode copy      # plain device copy, for counter calibration
+  python bench.py --mode stream    # the device's streaming read and copy rates
 """
 import argparse
 import hashlib
@@ -280,6 +285,137 @@ def time_paged(fk, wl, stream, iters, n_sets, warmup, block_size=16):
     return {"block_size": block_size, "step_us": round(e0.elapsed_time(e1) / iters * 1e3, 3)}
 
 
+def build_sets(wl, n_sets, dev, attn_splits=0, gemm_splitk=0):
+    """The layer's handle and n_sets independent buffer sets (hidden states,
+    weights, caches from the seeded initial cache, outputs, indices)."""
+    import torch
+    from io_aware_kv_amd.binding import FusedKVCache
+    from io_aware_kv_amd.workloads import initial_cache
+    ls = wl.shape
+    K0, V0 = initial_cache(wl)
+    fk = FusedKVCache(ls.B, ls.N, ls.d_model, ls.H, ls.Hkv, ls.dh, wl.nq, ls.dtype, ls.rope_base)
+    if attn_splits or gemm_splitk:
+        fk.set_tuning(attn_splits=attn_splits, gemm_splitk=gemm_splitk)
+    sets = []
+    for _ in range(n_sets):
+        Kc = K0.to(dev).contiguous()
+        Vc = V0.to(dev).contiguous()
+        sets.append(dict(X=wl.X.to(dev), W=wl.W.to(dev), Kc=Kc, Vc=Vc,
+                         O=torch.empty((ls.B, wl.nq, ls.H, ls.dh), dtype=ls.dtype, device=dev),
+                         LSE=torch.empty((ls.B, wl.nq, ls.H), dtype=torch.float32, device=dev),
+                         Q=wl.Q_idx.to(dev), P=wl.pos_ids.to(dev),
+                         vis=wl.vis.to(dev) if wl.vis is not None else None))
+    torch.cuda.synchronize()
+    return fk, sets, K0, V0
+
+
+def n_sets_for(ab):
+    """Buffer sets in rotation: enough that no step finds its data in the
+    256 MB Infinity Cache (at least 768 MB across the sets, at least 3; at
+    most 12: a layer far smaller than the cache stays warm whatever the
+    count)."""
+    return min(12, max(3, -(-768 * 2 ** 20 // ab["total"])))
+
+
+def time_launches(fn, sets, stream, steps, warmup):
+    """Average time of fn(set) launched `steps` times back to back (sets in
+    rotation), after `warmup` untimed calls: one event pair around the run."""
+    import torch
+    for i in range(warmup):
+        fn(sets[i % len(sets)])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        fn(sets[i % len(sets)])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def phase_fraction(nbytes, flops, us):
+    """Roofline fraction of a phase: against HBM bytes, or against bf16 MFMA
+    flops when those take the longer at peak."""
+    mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBPS * 1e9)
+    if mfma:
+        ach = flops / (us * 1e-6) / 1e12
+        return {"bound": "mfma", "achieved": round(ach, 1), "unit": "TFLOP/s",
+                "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4)}
+    ach = nbytes / (us * 1e-6) / 1e9
+    return {"bound": "hbm", "achieved": round(ach, 1), "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4)}
+
+
+def measure_config(cid, steps, warmup, dev, read_GBps=None):
+    """Step, projection and attention times of one layer workload, each launch
+    kind timed alone back to back over rotating buffer sets, with the
+    phases' roofline fractions."""
+    import torch
+    from io_aware_kv_amd.workloads import make_workload
+    wl = make_workload(cid)
+    ab = algorithmic_bytes(wl)
+    n_sets = n_sets_for(ab)
+    fk, sets, _, _ = build_sets(wl, n_sets, dev)
+    stream = torch.cuda.current_stream()
+
+    def proj(st):
+        fk.project(st["X"], st["Q"], st["P"], st["W"], st["Kc"], st["Vc"], stream=stream)
+
+    def attn(st):
+        fk.attend(st["P"], st["vis"], st["Kc"], st["Vc"], st["O"], st["LSE"], stream=stream)
+
+    def step(st):
+        proj(st)
+        attn(st)
+
+    step_ms = time_launches(step, sets, stream, steps, warmup)
+    proj_ms = time_launches(proj, sets, stream, steps, warmup)
+    attn_ms = time_launches(attn, sets, stream, steps, warmup)
+    plan = fk.plan(wl.nq)
+    fk.close()
+    del sets
+    attn_GBps = ab["attn"] / (attn_ms * 1e-3) / 1e9
+    out = {"workload": wl.name, "plan": plan, "buffer_sets": n_sets,
+           "step_us": round(step_ms * 1e3, 3), "proj_us": round(proj_ms * 1e3, 3), "attn_us": round(attn_ms * 1e3, 3),
+           "proj_bytes": ab["proj"], "proj_flops": ab["qkv_flops"],
+           "proj_roofline": phase_fraction(ab["proj"], ab["qkv_flops"], proj_ms * 1e3),
+           "attn_bytes": ab["attn"], "attn_flops": ab["attn_flops"],
+           "attn_GBps": round(attn_GBps, 1), "attn_hbm_frac": round(attn_GBps / HBM_PEAK_GBPS, 4)}
+    if read_GBps:
+        out["attn_frac_of_read_ceiling"] = round(attn_GBps / read_GBps, 4)
+    return out
+
+
+def device_rates(dev, stream):
+    """The device's streaming rates beside the 8 TB/s spec, on the launch
+    stream: a plain 1 GiB device copy (bytes read + written per second) and
+    the library's read probe over 1 GiB (bytes read per second, the best of
+    five grid sizes)."""
+    import torch
+    from io_aware_kv_amd import binding
+    cx = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cy = torch.empty_like(cx)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        cy.copy_(cx)
+        binding.probe_read(cx, sink, stream=stream)
+    torch.cuda.synchronize()
+    copy_ms = time_launches(lambda _: cy.copy_(cx), [None], stream, 10, 0)
+    # the read probe's best grid (one to sixteen workgroups per CU)
+    read_ms = min(time_launches(lambda _: binding.probe_read(cx, sink, workgroups=wgs, stream=stream), [None],
+                                stream, 10, 2) for wgs in (256, 512, 1024, 2048, 4096))
+    nbytes = cx.numel() * 4
+    del cx, cy
+    return 2 * nbytes / (copy_ms * 1e-3) / 1e9, nbytes / (read_ms * 1e-3) / 1e9
+
+
+def run_stream(args):
+    import torch
+    torch.cuda.set_device(0)
+    copy_GBps, read_GBps = device_rates(torch.device("cuda"), torch.cuda.current_stream())
+    print(json.dumps({"mode": "stream", "bytes": 1 << 30, "read_GBps": round(read_GBps, 1),
+                      "copy_GBps": round(copy_GBps, 1), "hbm_peak_GBps": HBM_PEAK_GBPS}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -290,10 +426,12 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-select", action="store_true",
                     help="skip timing the steps after the path (selection, decisions) and the paged variant")
+    ap.add_argument("--other-configs", default="1,2,4",
+                    help="other layer workloads measured into the line's `configs` (comma list; '' for none)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--attn-splits", type=int, default=0)
     ap.add_argument("--gemm-splitk", type=int, default=0)
-    ap.add_argument("--mode", default="step", choices=["step", "copy"])
+    ap.add_argument("--mode", default="step", choices=["step", "copy", "stream"])
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     args = ap.parse_args()
 
@@ -305,9 +443,10 @@ def main():
     import torch
     if args.mode == "copy":
         return run_copy(args)
+    if args.mode == "stream":
+        return run_stream(args)
 
-    from io_aware_kv_amd.binding import FusedKVCache
-    from io_aware_kv_amd.workloads import initial_cache, make_workload
+    from io_aware_kv_amd.workloads import make_workload
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda")
@@ -316,39 +455,26 @@ def main():
     ls = wl.shape
     ab = algorithmic_bytes(wl)
     per_set = ab["total"] + ls.B * wl.x_rows * ls.d_model * (2 if ls.dtype == torch.bfloat16 else 4)
-    n_sets = args.sets or max(3, -(-768 * 2 ** 20 // ab["total"]))
-
-    K0, V0 = initial_cache(wl)
-    sets = []
-    fk = None
-    for s in range(n_sets):
-        X = wl.X.to(dev)
-        W = wl.W.to(dev)
-        Kc = torch.empty((ls.B, ls.Hkv, ls.N, ls.dh), dtype=ls.dtype, device=dev)
-        Vc = torch.empty_like(Kc)
-        if fk is None:
-            fk = FusedKVCache(ls.B, ls.N, ls.d_model, ls.H, ls.Hkv, ls.dh, wl.nq, ls.dtype, ls.rope_base)
-            if args.attn_splits or args.gemm_splitk:
-                fk.set_tuning(attn_splits=args.attn_splits, gemm_splitk=args.gemm_splitk)
-        Kc.copy_(K0)
-        Vc.copy_(V0)
-        O = torch.empty((ls.B, wl.nq, ls.H, ls.dh), dtype=ls.dtype, device=dev)
-        LSE = torch.empty((ls.B, wl.nq, ls.H), dtype=torch.float32, device=dev)
-        sets.append(dict(X=X, W=W, Kc=Kc, Vc=Vc, O=O, LSE=LSE, Q=wl.Q_idx.to(dev), P=wl.pos_ids.to(dev),
-                         vis=wl.vis.to(dev) if wl.vis is not None else None))
-    torch.cuda.synchronize()
+    n_sets = args.sets or n_sets_for(ab)
+    fk, sets, K0, V0 = build_sets(wl, n_sets, dev, args.attn_splits, args.gemm_splitk)
     plan = fk.plan(wl.nq)
     log("bench: %d buffer sets of %.1f MB, plan %s" % (n_sets, per_set / 1e6, plan))
 
     stream = torch.cuda.current_stream()
 
+    def proj(st):
+        fk.project(st["X"], st["Q"], st["P"], st["W"], st["Kc"], st["Vc"], stream=stream)
+
+    def attn(st):
+        fk.attend(st["P"], st["vis"], st["Kc"], st["Vc"], st["O"], st["LSE"], stream=stream)
+
     def step(st, evs=None):
         if evs is not None:
             evs[0].record(stream)
-        fk.project(st["X"], st["Q"], st["P"], st["W"], st["Kc"], st["Vc"], stream=stream)
+        proj(st)
         if evs is not None:
             evs[1].record(stream)
-        fk.attend(st["P"], st["vis"], st["Kc"], st["Vc"], st["O"], st["LSE"], stream=stream)
+        attn(st)
         if evs is not None:
             evs[2].record(stream)
 
@@ -368,17 +494,18 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = start.elapsed_time(end) / args.steps
-    # phase times from a second pass with an event around each launch (the
-    # events add a small gap between the launches, so they stay out of the
-    # timed steps above)
+    # each launch kind alone, back to back (the per-kernel average a kernel
+    # trace reports): the roofline's launch time
+    proj_avg = time_launches(proj, sets, stream, args.steps, 3)
+    attn_avg = time_launches(attn, sets, stream, args.steps, 3)
+    # the distribution over a pass with an event around each launch (the
+    # events add a small gap between launches; not used for the averages)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for i in range(args.steps):
         step(sets[i % n_sets], evs[i])
     torch.cuda.synchronize()
     proj_ms = sorted(e[0].elapsed_time(e[1]) for e in evs)
     attn_ms = sorted(e[1].elapsed_time(e[2]) for e in evs)
-    proj_avg = sum(proj_ms) / len(proj_ms)
-    attn_avg = sum(attn_ms) / len(attn_ms)
     step_ms = sorted(e[0].elapsed_time(e[2]) for e in evs)
 
     def pct(v):
@@ -386,33 +513,12 @@ def main():
         return {"p10": round(v[n // 10] * 1e3, 3), "p50": round(v[n // 2] * 1e3, 3),
                 "p90": round(v[min(n - 1, (n * 9) // 10)] * 1e3, 3)}
 
-    # the device's achievable streaming rate beside the 8 TB/s spec: a plain
-    # 1 GiB device copy on the same stream (bytes read + written per second)
-    cx = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    cy = torch.empty_like(cx)
-    for _ in range(3):
-        cy.copy_(cx)
-    ce0, ce1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ce0.record(stream)
-    for _ in range(10):
-        cy.copy_(cx)
-    ce1.record(stream)
-    torch.cuda.synchronize()
-    copy_GBps = 2 * cx.numel() * 4 / (ce0.elapsed_time(ce1) / 10 * 1e-3) / 1e9
-    del cx, cy
-    log("bench: %.2f us/step (proj %.2f us, attn %.2f us), wall %.3f s" %
-        (ms_per_step * 1e3, proj_avg * 1e3, attn_avg * 1e3, wall))
+    copy_GBps, read_GBps = device_rates(dev, stream)
+    log("bench: %.2f us/step (proj %.2f us, attn %.2f us alone), wall %.3f s; device copy %.0f GB/s, read %.0f GB/s" %
+        (ms_per_step * 1e3, proj_avg * 1e3, attn_avg * 1e3, wall, copy_GBps, read_GBps))
 
     # warm-cache reference: the same set every step (Infinity Cache may hold it)
-    warm_iters = min(args.steps, 50)
-    torch.cuda.synchronize()
-    ws, we = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ws.record(stream)
-    for _ in range(warm_iters):
-        step(sets[0])
-    we.record(stream)
-    torch.cuda.synchronize()
-    warm_ms = ws.elapsed_time(we) / warm_iters
+    warm_ms = time_launches(lambda st: step(st), [sets[0]], stream, min(args.steps, 50), 0)
 
     # the step after the path: tracked-set scores and top-k (not part of value)
     selection = None
@@ -432,7 +538,6 @@ def main():
     dom = "attn" if attn_avg >= proj_avg else "proj"
     dom_ms = attn_avg if dom == "attn" else proj_avg
     dom_bytes = ab[dom]
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
     wkey = "workload%d" % args.config
     # the attention phase is the split kernel plus, with several cache splits,
     # its combine kernel (same stream, back to back)
@@ -445,20 +550,17 @@ def main():
     # takes the longer at peak (a projection over many query rows is a
     # contraction well past the ridge point)
     dom_flops = ab["attn_flops"] if dom == "attn" else ab["qkv_flops"]
-    mfma_bound = dom_flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > dom_bytes / (HBM_PEAK_GBPS * 1e9)
-    if mfma_bound:
-        achieved_f = dom_flops / (dom_ms * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved_f, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                    "unit": "TFLOP/s", "frac": round(achieved_f / MFMA_BF16_PEAK_TFLOPS, 4)}
-    else:
-        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                    "frac": round(achieved / HBM_PEAK_GBPS, 4)}
+    pf = phase_fraction(dom_bytes, dom_flops, dom_ms * 1e3)
+    roofline = {"bound": pf["bound"], "achieved": pf["achieved"],
+                "peak": MFMA_BF16_PEAK_TFLOPS if pf["bound"] == "mfma" else HBM_PEAK_GBPS,
+                "unit": pf["unit"], "frac": pf["frac"]}
     roofline.update({"traffic": traffic,
                      "kernel": "attn_mfma_kernel" if dom == "attn" else "proj_mfma_kernel",
                      "algorithmic_bytes_per_launch": dom_bytes, "algorithmic_flops_per_launch": dom_flops,
                      "avg_launch_us": round(dom_ms * 1e3, 3)})
 
     value = ab["total"] / (ms_per_step * 1e-3) / 1e9
+    attn_GBps = ab["attn"] / (attn_avg * 1e-3) / 1e9
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -479,12 +581,14 @@ def main():
         "queries_per_s": round(ls.B * wl.nq / (ms_per_step * 1e-3), 1),
         "warm_cache_latency_us": round(warm_ms * 1e3, 3),
         "phases": {
+            # each launch kind alone, back to back
             "proj_us": round(proj_avg * 1e3, 3),
             "attn_us": round(attn_avg * 1e3, 3),
             "proj_GBps": round(ab["proj"] / (proj_avg * 1e-3) / 1e9, 1),
-            "attn_GBps": round(ab["attn"] / (attn_avg * 1e-3) / 1e9, 1),
+            "attn_GBps": round(attn_GBps, 1),
             "proj_mfma_frac": round(ab["qkv_flops"] / (proj_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-            "attn_hbm_frac": round(ab["attn"] / (attn_avg * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "attn_hbm_frac": round(attn_GBps / HBM_PEAK_GBPS, 4),
+            "attn_frac_of_read_ceiling": round(attn_GBps / read_GBps, 4),
             # distribution over the evented pass (an event around each launch)
             "proj_us_pct": pct(proj_ms),
             "attn_us_pct": pct(attn_ms),
@@ -492,11 +596,26 @@ def main():
         },
         "algorithmic_bytes_per_step": ab["total"],
         "device_copy_GBps": round(copy_GBps, 1),
+        "device_read_GBps": round(read_GBps, 1),
         "host": host_info(),
         "next_rows": selection,
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    fk.close()
+    sets_main = sets
+
+    # the other layer workloads of the target set, measured the same way
+    others = {}
+    for c in [int(x) for x in args.other_configs.split(",") if x.strip()]:
+        if c == args.config:
+            continue
+        log("bench: workload %d" % c)
+        others["workload%d" % c] = measure_config(c, min(args.steps, 100), 10, dev, read_GBps)
+        o = others["workload%d" % c]
+        log("bench: workload %d: step %.2f us, proj %.2f us, attn %.2f us (%.0f GB/s, %.3f of 8 TB/s)" %
+            (c, o["step_us"], o["proj_us"], o["attn_us"], o["attn_GBps"], o["attn_hbm_frac"]))
+    result["configs"] = others
 
     if not args.no_cpu:
         log("bench: timing the CPU oracle (budget %.0f s)" % args.cpu_budget)
@@ -507,8 +626,8 @@ def main():
                                             "median of %d run(s), %.2f s" % (ls.B, reps, cpu_s)}
         # parity of the timed path against the oracle on set 0
         import numpy as np
-        o = sets[0]["O"].double().cpu().numpy()
-        lse = sets[0]["LSE"].double().cpu().numpy()
+        o = sets_main[0]["O"].double().cpu().numpy()
+        lse = sets_main[0]["LSE"].double().cpu().numpy()
         fin = np.isfinite(r["LSE"])
         result["parity"] = {
             "O_rel": float(np.abs(o - r["O"]).max() / np.abs(r["O"]).max()),

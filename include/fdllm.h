@@ -98,26 +98,46 @@ typedef struct fdllm_ctx* fdllm_handle_t;
  * FDLLM_ERR_ARG or FDLLM_ERR_UNSUPPORTED. */
 int fdllm_validate_config(const fdllm_config_t* cfg);
 
-/* Create a handle: validates cfg, allocates the handle's workspace on the
- * current device (rotary table, q staging, duplicate-row side buffer, split
- * partials and counters) and, if X_full is not NULL, builds the cache from
- * the full sequence (see fdllm_prefill with x_rows = N).  W_qkv, Kc, Vc may
- * be NULL when X_full is NULL.  *out receives the handle, or NULL on error.
+/* Create a handle for one layer's persistent cache.  The cache is the flat,
+ * preallocated bidirectional KV store of the pages' system (jaehun.me review,
+ * "Performance Validation: Key Results": a flat, preallocated cache without
+ * padding; "How It Works: A Concrete Example", Step 1: Draft: every position
+ * of it can be rewritten at any step).  The caller owns Kc/Vc [B, Hkv, N, dh];
+ * this call validates cfg, allocates the handle's workspace on the current
+ * device (rotary table, q staging, duplicate-row side buffer, split partials
+ * and counters) and, if X_full is not NULL, builds the cache from the full
+ * sequence (see fdllm_prefill with x_rows = N).  W_qkv, Kc, Vc may be NULL
+ * when X_full is NULL.  *out receives the handle, or NULL on error.
  * Statuses: ARG, UNSUPPORTED, ALIGN, ALLOC, HIP. */
 int fdllm_cache_init(fdllm_handle_t* out, const fdllm_config_t* cfg, const void* X_full,
                      const void* W_qkv, void* Kc, void* Vc, void* stream);
 
-/* Cache build from a full sequence ("cache prefilled from full-sequence
- * projection"): for every b and position p < N, row p of X[b] is projected,
- * k is rotated at position p, and k, v are rounded and stored at
- * Kc/Vc[b, :, p, :].  X is [B, x_rows, d_model] with x_rows >= N.
- * Statuses: ARG, SHAPE, ALIGN, HIP. */
+/* Cache build from a full sequence, the state the step starts from (jaehun.me
+ * review, "Performance Validation: Key Results": the flat preallocated cache;
+ * "How It Works: A Concrete Example", Step 1: Draft: the cache holds k and v
+ * of every position, which the step then rewrites at its query positions):
+ * for every b and position p < N, row p of X[b] is projected, k is rotated at
+ * position p, and k, v are rounded and stored at Kc/Vc[b, :, p, :].  X is
+ * [B, x_rows, d_model] with x_rows >= N, device pointers owned by the caller.
+ * Asynchronous on stream.  Statuses: ARG, SHAPE, ALIGN, HIP. */
 int fdllm_prefill(fdllm_handle_t h, const void* X, int32_t x_rows, const void* W_qkv,
                   void* Kc, void* Vc, void* stream);
 
-/* One fused step (gather X[Q] -> q,k,v -> rotary -> in-place k/v write ->
- * attention over the whole cache under vis_mask), see the conventions above.
- * 0 <= nq <= q_max; nq == 0 launches nothing.
+/* One fused step (jaehun.me review, "How It Works: A Concrete Example",
+ * Step 1: Draft -- only the hidden states of the query rows are read, q, k, v
+ * are built on chip, k and v go straight into the cache, and the rows attend
+ * over the whole cache -- and Step 1: Verification -- the draft view and the
+ * [MASK] view share positions and are kept apart by the mask; alanhou.org
+ * summary, "Core Mechanism" item 1: cache lookup, similarity and masked
+ * attention fused so intermediates do not round-trip through HBM).
+ * Computes, for every sequence b: gather X[b, Q_idx[b, j]] -> q, k, v ->
+ * rotary at pos_ids[b, j] -> in-place write of k, v to Kc/Vc[b, :, pos, :]
+ * (first row at a position) -> attention of every query row over the whole
+ * cache under vis_mask -> O [B, nq, H, dh] (dtype) and LSE [B, nq, H] (fp32,
+ * natural log).  Arguments and layouts as in the conventions above; every
+ * pointer is a caller-owned device buffer; the handle's workspace holds the
+ * step's q rows and duplicate-position k/v rows until the step ends.
+ * 0 <= nq <= q_max; nq == 0 launches nothing.  Asynchronous on stream.
  * Statuses: ARG, SHAPE, ALIGN, INDEX (FDLLM_VALIDATE=1 only), HIP. */
 int fdllm_fused_step(fdllm_handle_t h, const void* X, int32_t x_rows, const int32_t* Q_idx,
                      const int32_t* pos_ids, int32_t nq, const uint8_t* vis_mask,

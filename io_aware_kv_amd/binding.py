@@ -17,6 +17,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfdllm.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "fdllm.h")
+HEADERS = [os.path.join(os.path.dirname(_PKG), "include", h) for h in ("fdllm.h", "fdllm_probe.h")]
 
 FDLLM_F32, FDLLM_BF16 = 0, 1
 STATUS = {0: "FDLLM_OK", -1: "FDLLM_ERR_ARG", -2: "FDLLM_ERR_SHAPE", -3: "FDLLM_ERR_ALIGN",
@@ -44,9 +45,12 @@ _lib = None
 
 
 def declared_symbols():
-    """Function names declared in include/fdllm.h."""
-    txt = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(fdllm_\w+)\s*\(", txt, re.M)))
+    """Function names declared in the library's headers (include/fdllm*.h)."""
+    names = set()
+    for path in HEADERS:
+        with open(path) as f:
+            names |= set(re.findall(r"^\s*(?:int|const char\*)\s+(fdllm_\w+)\s*\(", f.read(), re.M))
+    return sorted(names)
 
 
 def load():
@@ -72,12 +76,13 @@ def load():
     lib.fdllm_set_tuning.argtypes = [P, ctypes.POINTER(Tuning)]
     lib.fdllm_get_plan.argtypes = [P, i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.fdllm_cache_destroy.argtypes = [P]
+    lib.fdllm_probe_read.argtypes = [P, ctypes.c_int64, i32, P, P]
     lib.fdllm_status_str.argtypes = [ctypes.c_int]
     lib.fdllm_status_str.restype = ctypes.c_char_p
     for name in ("fdllm_validate_config", "fdllm_cache_init", "fdllm_prefill", "fdllm_fused_step",
                  "fdllm_step_project", "fdllm_step_attend", "fdllm_tracked_scores", "fdllm_select_tracked",
                  "fdllm_confidence", "fdllm_accept", "fdllm_fused_step_paged",
-                 "fdllm_set_tuning", "fdllm_get_plan", "fdllm_cache_destroy"):
+                 "fdllm_set_tuning", "fdllm_get_plan", "fdllm_cache_destroy", "fdllm_probe_read"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -139,6 +144,14 @@ def accept(x_hat: torch.Tensor, x_tilde: torch.Tensor, c_tilde: torch.Tensor, ga
         raise ValueError("n_accept must be int32 [B]")
     _check(load().fdllm_accept(_ptr(x_hat), _ptr(x_tilde), _ptr(c_tilde), B, S, float(gamma), _ptr(n_accept),
                                _stream(stream)), "fdllm_accept")
+
+
+def probe_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int = 0, stream=None):
+    """One streaming read of buf (fdllm_probe.h); sink is a 16-byte device buffer."""
+    if sink.numel() * sink.element_size() < 16:
+        raise ValueError("sink must hold 16 bytes")
+    _check(load().fdllm_probe_read(_ptr(buf), buf.numel() * buf.element_size(), workgroups, _ptr(sink),
+                                   _stream(stream)), "fdllm_probe_read")
 
 
 def make_config(B, N, d_model, H, Hkv, dh, q_max, dtype=torch.bfloat16, rope_base=10000.0) -> Config:

@@ -79,6 +79,16 @@ def test_init_without_gpu_reports_hip_error(lib):
     assert rc in (-6, -5) and not out.value
 
 
+def test_read_probe_argument_errors_are_host_side(lib):
+    P = ctypes.c_void_p
+    assert lib.fdllm_probe_read(None, 1024, 0, P(16), None) == -1
+    assert lib.fdllm_probe_read(P(16), 1024, 0, None, None) == -1
+    assert lib.fdllm_probe_read(P(16), 8, 0, P(16), None) == -1       # fewer than 16 bytes
+    assert lib.fdllm_probe_read(P(16), 1000, 0, P(16), None) == -1    # not whole 16-byte chunks
+    assert lib.fdllm_probe_read(P(16), 1024, -1, P(16), None) == -1
+    assert lib.fdllm_probe_read(P(24), 1024, 0, P(16), None) == -3    # misaligned buffer
+
+
 def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         binding._ptr(torch.zeros(4))
