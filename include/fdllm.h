@@ -48,9 +48,10 @@
  *     rounded to the dtype.  Accumulation is fp32; O is rounded once at the
  *     end; LSE stays fp32.
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls are
- *     asynchronous on that stream and never synchronise, except that
- *     FDLLM_VALIDATE=1 in the environment makes fdllm_fused_step copy the
- *     index arrays to the host and range-check them first.
+ *     asynchronous on that stream and never synchronise, except that a
+ *     handle created while FDLLM_VALIDATE=1 is set in the environment makes
+ *     its steps copy the index arrays to the host and range-check them
+ *     first.
  *   - Return value: FDLLM_OK or a negative status; on any error nothing has
  *     been launched.  Indices out of range are undefined behaviour unless
  *     FDLLM_VALIDATE=1.  A handle serves one stream at a time; concurrent
@@ -90,6 +91,7 @@ typedef struct {
     int32_t attn_splits;    /* cache splits per (sequence, kv head) in the attention */
     int32_t gemm_splitk;    /* reserved: the projection does not split d_model (plan reports 1) */
     int32_t kernel_family;  /* 0 auto, 1 tiled MFMA (bf16 only), 2 generic scalar */
+    int32_t proj_tile;      /* 0 auto, 1..10: a tile configuration of the MFMA projection */
 } fdllm_tuning_t;
 
 typedef struct fdllm_ctx* fdllm_handle_t;
@@ -242,7 +244,7 @@ int fdllm_accept(const int32_t* x_hat, const int32_t* x_tilde, const float* c_ti
                  float gamma, int32_t* n_accept, void* stream);
 
 /* Set (tuning != NULL) or reset (NULL) the launch-shape overrides of h.
- * Statuses: ARG. */
+ * Statuses: ARG (a negative field, kernel_family > 2, proj_tile > 10). */
 int fdllm_set_tuning(fdllm_handle_t h, const fdllm_tuning_t* tuning);
 
 /* Report the launch shapes fdllm_fused_step would use for nq: attention

@@ -38,7 +38,7 @@ class Config(ctypes.Structure):
 
 class Tuning(ctypes.Structure):
     _fields_ = [("attn_splits", ctypes.c_int32), ("gemm_splitk", ctypes.c_int32),
-                ("kernel_family", ctypes.c_int32)]
+                ("kernel_family", ctypes.c_int32), ("proj_tile", ctypes.c_int32)]
 
 
 _lib = None
@@ -283,8 +283,8 @@ class FusedKVCache:
         rc = load().fdllm_select_tracked(self._h, _ptr(scores), _ptr(cand), k, _ptr(out), _stream(stream))
         _check(rc, "fdllm_select_tracked")
 
-    def set_tuning(self, attn_splits=0, gemm_splitk=0, kernel_family=0):
-        t = Tuning(attn_splits, gemm_splitk, kernel_family)
+    def set_tuning(self, attn_splits=0, gemm_splitk=0, kernel_family=0, proj_tile=0):
+        t = Tuning(attn_splits, gemm_splitk, kernel_family, proj_tile)
         _check(load().fdllm_set_tuning(self._h, ctypes.byref(t)), "fdllm_set_tuning")
 
     def plan(self, nq):

@@ -802,9 +802,10 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s)
     const size_t shm = C::SCRATCH + book;
     const int total = a.B * a.Hkv * a.splits;
     const int grid = ((total + 7) / 8) * 8;
-    auto kern = attn_mfma_kernel<RG, NWR, NWK, NPROD, RING>;
-    // raise the dynamic LDS limit; a refusal shows up as a launch error below
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    constexpr auto kern = attn_mfma_kernel<RG, NWR, NWK, NPROD, RING>;
+    // the dynamic LDS limit is raised once per device; a refusal shows up as
+    // a launch error below
+    (void)allow_full_lds<kern>();
     (void)hipGetLastError();
     hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), shm, s, a);
     hipError_t e = hipGetLastError();

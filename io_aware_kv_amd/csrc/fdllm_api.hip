@@ -27,37 +27,31 @@ struct fdllm_ctx {
     float* aml = nullptr;
     size_t apart_rows = 0;        // (B*Hkv) * splits * Rpad rows available
     float* mpart = nullptr;       // [B * Hkv, N] per kv head sums of the tracked-set scores
-    fdllm_tuning_t tune{0, 0, 0};
+    fdllm_tuning_t tune{0, 0, 0, 0};
+    bool validate = false;        // FDLLM_VALIDATE=1 when the handle was created: range-check indices
 };
 
 namespace {
 
-enum { FAMILY_MFMA = 1, FAMILY_GENERIC = 2 };
-
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int env_int(const char* name, int dflt)
+bool env_flag(const char* name)
 {
     const char* v = getenv(name);
-    return (v && *v) ? atoi(v) : dflt;
+    return v && *v && atoi(v) != 0;
 }
 
-struct Plan {
-    int proj_family, attn_family;
-    int splitk, proj_tiles, bm;
-    int splits, keys_per_split, R, Rpad;
-};
+}  // namespace
 
-Plan make_plan(const fdllm_ctx* h, int nq)
+Plan fdllm::make_plan(const fdllm_config_t& c, int G, const fdllm_tuning_t& tune, int nq)
 {
-    const fdllm_config_t& c = h->cfg;
     Plan p{};
-    int fam = h->tune.kernel_family;
+    int fam = tune.kernel_family;
     const bool mfma_ok = c.dtype == FDLLM_BF16 && c.dh == 128 && c.d_model % 128 == 0;
     if (fam == 0) fam = mfma_ok ? FAMILY_MFMA : FAMILY_GENERIC;
     if (fam == FAMILY_MFMA && !mfma_ok) fam = FAMILY_GENERIC;
     p.proj_family = fam;
-    p.R = nq * h->G;
+    p.R = nq * G;
     p.Rpad = ((p.R + 15) / 16) * 16;
     p.attn_family = (fam == FAMILY_MFMA && (p.R + 15) / 16 <= 18) ? FAMILY_MFMA : FAMILY_GENERIC;
 
@@ -66,7 +60,7 @@ Plan make_plan(const fdllm_ctx* h, int nq)
     const int M = c.B * nq;
     p.splitk = 1;
     if (p.proj_family == FAMILY_MFMA && M > 0) {
-        const ProjTile pt = proj_mfma_tile(M, c.H + 2 * c.Hkv, env_int("FDLLM_PROJ_TILE", 0));
+        const ProjTile pt = proj_mfma_tile(M, c.H + 2 * c.Hkv, tune.proj_tile);
         p.bm = pt.bm;
         p.proj_tiles = ((M + pt.bm - 1) / pt.bm) * (c.H + 2 * c.Hkv) * (128 / pt.bn);
     }
@@ -79,7 +73,7 @@ Plan make_plan(const fdllm_ctx* h, int nq)
         const int tk = attn_mfma_tile_keys(p.R);
         const int bgs = c.B * c.Hkv;
         const int max_splits = (c.N + tk - 1) / tk;
-        int sp = h->tune.attn_splits > 0 ? h->tune.attn_splits : env_int("FDLLM_SPLITS", 0);
+        int sp = tune.attn_splits;
         if (sp <= 0) sp = (256 + bgs - 1) / bgs;
         sp = std::max(1, std::min(sp, max_splits));
         int kps = (c.N + sp - 1) / sp;
@@ -92,10 +86,14 @@ Plan make_plan(const fdllm_ctx* h, int nq)
     return p;
 }
 
+namespace {
+
+Plan make_plan(const fdllm_ctx* h, int nq) { return fdllm::make_plan(h->cfg, h->G, h->tune, nq); }
+
 int hip_status(hipError_t e)
 {
     if (e == hipSuccess) return FDLLM_OK;
-    if (getenv("FDLLM_LOG")) fprintf(stderr, "fdllm: HIP error %s\n", hipGetErrorString(e));
+    if (env_flag("FDLLM_LOG")) fprintf(stderr, "fdllm: HIP error %s\n", hipGetErrorString(e));
     return FDLLM_ERR_HIP;
 }
 
@@ -151,7 +149,7 @@ ProjArgs proj_args(const fdllm_ctx* h, const void* X, int x_rows, const int32_t*
     a.B = c.B; a.N = c.N; a.d = c.d_model; a.H = c.H; a.Hkv = c.Hkv; a.dh = c.dh; a.G = h->G;
     a.x_rows = x_rows; a.rows_per_seq = rows_per_seq; a.q_max = c.q_max;
     a.prefill = prefill;
-    a.tile_choice = prefill ? 0 : env_int("FDLLM_PROJ_TILE", 0);
+    a.tile_choice = prefill ? 0 : h->tune.proj_tile;
     return a;
 }
 
@@ -176,7 +174,7 @@ int project_impl(fdllm_ctx* h, const void* X, int32_t x_rows, const int32_t* Q_i
     int st = set_device(h);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    if (!validated && env_int("FDLLM_VALIDATE", 0)) {
+    if (!validated && h->validate) {
         std::vector<int32_t> qi((size_t)c.B * nq), pi((size_t)c.B * nq);
         if (hipMemcpyAsync(qi.data(), Q_idx, qi.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
             hipMemcpyAsync(pi.data(), pos_ids, pi.size() * 4, hipMemcpyDeviceToHost, s) != hipSuccess ||
@@ -290,6 +288,7 @@ int fdllm_cache_init(fdllm_handle_t* out, const fdllm_config_t* cfg, const void*
     if (!h) return FDLLM_ERR_ALLOC;
     h->cfg = *cfg;
     h->G = cfg->H / cfg->Hkv;
+    h->validate = env_flag("FDLLM_VALIDATE");
     h->elt = cfg->dtype == FDLLM_BF16 ? 2 : 4;
     if (hipGetDevice(&h->device) != hipSuccess) { delete h; return FDLLM_ERR_HIP; }
 
@@ -328,9 +327,10 @@ int fdllm_cache_init(fdllm_handle_t* out, const fdllm_config_t* cfg, const void*
 int fdllm_set_tuning(fdllm_handle_t h, const fdllm_tuning_t* t)
 {
     if (!h) return FDLLM_ERR_ARG;
-    if (t && (t->attn_splits < 0 || t->gemm_splitk < 0 || t->kernel_family < 0 || t->kernel_family > 2))
+    if (t && (t->attn_splits < 0 || t->gemm_splitk < 0 || t->kernel_family < 0 || t->kernel_family > 2 ||
+              t->proj_tile < 0 || t->proj_tile > 10))
         return FDLLM_ERR_ARG;
-    h->tune = t ? *t : fdllm_tuning_t{0, 0, 0};
+    h->tune = t ? *t : fdllm_tuning_t{0, 0, 0, 0};
     int st = set_device(h);
     if (st) return st;
     return ensure_split_ws(h);
@@ -384,7 +384,7 @@ int fdllm_fused_step_paged(fdllm_handle_t h, const void* X, int32_t x_rows, cons
     int st = set_device(h);
     if (st) return st;
     hipStream_t s = (hipStream_t)stream;
-    if (env_int("FDLLM_VALIDATE", 0)) {
+    if (h->validate) {
         // host copies of the lengths, indices and table: every row a sequence
         // uses must point inside its valid positions and allocated blocks
         std::vector<int32_t> qi((size_t)c.B * nq), pi((size_t)c.B * nq), nb(c.B, nq), L(c.B, c.N);

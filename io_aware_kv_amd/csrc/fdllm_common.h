@@ -5,6 +5,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
+#include "fdllm.h"
+
 namespace fdllm {
 
 typedef __bf16 bf16;
@@ -111,6 +115,32 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s);
 struct ProjTile { int bm, bn, choice; };
 ProjTile proj_mfma_tile(int M, int heads, int choice);   // choice 0: the default for M rows
 int attn_mfma_tile_keys(int R);
+
+// Launch plan of a step with nq query rows per sequence (host side).
+enum { FAMILY_MFMA = 1, FAMILY_GENERIC = 2 };
+struct Plan {
+    int proj_family, attn_family;
+    int splitk, proj_tiles, bm;
+    int splits, keys_per_split, R, Rpad;
+};
+
+Plan make_plan(const fdllm_config_t& c, int G, const fdllm_tuning_t& tune, int nq);
+
+// Raise a kernel's dynamic LDS limit to the CU's 160 KB, once per device
+// (the launches then pass their exact size).
+template <auto Kern>
+hipError_t allow_full_lds()
+{
+    static std::atomic<unsigned long long> done{0};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const unsigned long long bit = 1ull << (dev & 63);
+    if (done.load(std::memory_order_relaxed) & bit) return hipSuccess;
+    e = hipFuncSetAttribute((const void*)Kern, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (e == hipSuccess) done.fetch_or(bit);
+    return e;
+}
 
 // Conversions between storage types and fp32.
 __device__ __forceinline__ float to_f32(float x) { return x; }

@@ -402,8 +402,8 @@ hipError_t launch_tile(const ProjArgs& a, hipStream_t s)
     const int total = m_tiles * n_tiles;
     const int grid = ((total + 7) / 8) * 8;
     const size_t shm = (size_t)C::NS * C::STAGE;
-    auto kern = proj_mfma_kernel<BM, NCB, NKW, NRW, NPW, NSMAX, BK, NPROD>;
-    (void)hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    constexpr auto kern = proj_mfma_kernel<BM, NCB, NKW, NRW, NPW, NSMAX, BK, NPROD>;
+    (void)allow_full_lds<kern>();
     (void)hipGetLastError();
     hipLaunchKernelGGL(kern, dim3(grid), dim3(C::NT), shm, s, a, m_tiles, n_tiles);
     return hipGetLastError();

@@ -699,14 +699,12 @@ hipError_t launch_key_mass(const MassArgs& a, hipStream_t s)
         if (ns < kMassMinStages) ns = (int)std::min<size_t>(8, (160 * 1024 - 256 - book) / kMassStage);
         if (ns < kMassMinStages) return hipErrorInvalidValue;
         const size_t shm = (size_t)ns * kMassStage + book;
-        (void)hipFuncSetAttribute((const void*)key_mass_ring_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)shm);
+        (void)allow_full_lds<key_mass_ring_kernel>();
         (void)hipGetLastError();
         hipLaunchKernelGGL(key_mass_ring_kernel, dim3(wgs), dim3((kMassWaves + 1) * 64), shm, s, a, ns);
     } else {
         // more: the direct form keeps every pair's work in its own waves
-        (void)hipFuncSetAttribute((const void*)key_mass_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)book);
+        (void)allow_full_lds<key_mass_kernel>();
         (void)hipGetLastError();
         hipLaunchKernelGGL(key_mass_kernel, dim3(wgs), dim3(kMassWaves * 64), book, s, a);
     }
@@ -745,7 +743,7 @@ hipError_t launch_select_top(const float* scores, const uint8_t* cand, int B, in
     while (n2 < m) n2 <<= 1;
     const size_t staged = (size_t)((N + 3) & ~3) * 4 + (size_t)((N + 31) / 32) * 4;
     const size_t shm = std::max((size_t)n2 * sizeof(uint64_t), staged);
-    (void)hipFuncSetAttribute((const void*)select_top_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    (void)allow_full_lds<select_top_kernel>();
     (void)hipGetLastError();
     hipLaunchKernelGGL(select_top_kernel, dim3(B), dim3(kTopThreads), shm, s, scores, cand, N, n2, k, out);
     return hipGetLastError();

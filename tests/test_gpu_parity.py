@@ -151,14 +151,13 @@ def test_forced_splits(splits, nq):
 
 
 @pytest.mark.parametrize("choice", list(range(1, 11)))
-def test_forced_projection_tiles(choice, monkeypatch):
-    """Every projection tile configuration (FDLLM_PROJ_TILE) on a case with
+def test_forced_projection_tiles(choice):
+    """Every projection tile configuration (tuning proj_tile) on a case with
     ragged row tiles, GQA, duplicates and a mask."""
     log("case: projection tile %d" % choice)
-    monkeypatch.setenv("FDLLM_PROJ_TILE", str(choice))
     ls = LayerShape(B=3, N=400, d_model=512, H=4, Hkv=2, dh=128)
     wl = make_random_case(ls, 70, seed=31, n_extra_rows=8, dup_frac=0.1, masked_vis=True, w_std=0.05)
-    g = run_gpu(wl)
+    g = run_gpu(wl, tuning={"proj_tile": choice})
     compare(wl, g, run_oracle(wl), "proj-tile%d" % choice)
 
 
@@ -273,14 +272,17 @@ def test_status_codes_on_gpu():
     with pytest.raises(FdllmError) as e:
         fk.step(X, Q5, Q5, None, W, Kc, Vc, O, LSE)
     assert e.value.status == -2
+    fk.close()
     bad = torch.tensor([[0, 1, 2, 64]], dtype=torch.int32, device=dev)
     O4 = torch.empty((1, 4, 2, 128), dtype=torch.bfloat16, device=dev)
     L4 = torch.empty((1, 4, 2), dtype=torch.float32, device=dev)
+    # range checks belong to handles created while FDLLM_VALIDATE=1 is set
     os.environ["FDLLM_VALIDATE"] = "1"
     try:
-        with pytest.raises(FdllmError) as e:
-            fk.step(X, bad - 1, bad, None, W, Kc, Vc, O4, L4)
-        assert e.value.status == -4
+        fkv = FusedKVCache(1, 64, 128, 2, 2, 128, 4)
     finally:
         del os.environ["FDLLM_VALIDATE"]
-    fk.close()
+    with pytest.raises(FdllmError) as e:
+        fkv.step(X, bad - 1, bad, None, W, Kc, Vc, O4, L4)
+    assert e.value.status == -4
+    fkv.close()
