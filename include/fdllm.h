@@ -76,7 +76,8 @@ enum {
     FDLLM_ERR_INDEX = -4,    /* index out of range (only with FDLLM_VALIDATE=1) */
     FDLLM_ERR_ALLOC = -5,    /* device workspace allocation failed */
     FDLLM_ERR_HIP = -6,      /* a HIP runtime call or launch failed */
-    FDLLM_ERR_UNSUPPORTED = -7 /* shape outside what the kernels implement */
+    FDLLM_ERR_UNSUPPORTED = -7, /* shape outside what the kernels implement */
+    FDLLM_ERR_SCRATCH = -8   /* workspace larger than the allocation-free scratch */
 };
 
 typedef struct {
@@ -252,6 +253,26 @@ int fdllm_set_tuning(fdllm_handle_t h, const fdllm_tuning_t* tuning);
  * 2 generic).  Any output pointer may be NULL.  Statuses: ARG, SHAPE. */
 int fdllm_get_plan(fdllm_handle_t h, int32_t nq, int32_t* attn_splits, int32_t* gemm_splitk,
                    int32_t* kernel_family);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * step as fdllm_fused_step with the default launch plan, without a handle.
+ * cfg describes the layer (q_max bounds nq); the kernels' workspace (rotary
+ * rows of the step's positions, q staging, duplicate-row side buffers, split
+ * partials) lives in a static device array of FDLLM_NOALLOC_SCRATCH_BYTES
+ * that each GPU the library runs on holds until the process ends; the call
+ * allocates nothing.  Every call on one GPU shares that array and leaves its
+ * contents behind, so calls that overlap on one GPU (several streams or
+ * threads) race; serialise them.  Indices are not range-checked
+ * (FDLLM_VALIDATE does not apply).  Other arguments as for fdllm_fused_step.
+ * Statuses: ARG, UNSUPPORTED (invalid configuration), SHAPE, ALIGN, SCRATCH
+ * (the step's workspace exceeds the array: about N*dh*4 + B*Hkv*nq*dh*(4G +
+ * 2*elt) bytes, plus B*Hkv*splits*R*(dh+2)*4 when the cache is split, with
+ * G = H/Hkv and R = nq*G), HIP. */
+#define FDLLM_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int fdllm_fused_step_noalloc(const fdllm_config_t* cfg, const void* X, int32_t x_rows, const int32_t* Q_idx,
+                             const int32_t* pos_ids, int32_t nq, const uint8_t* vis_mask, const void* W_qkv,
+                             void* Kc, void* Vc, void* O, float* LSE, void* stream);
 
 /* Free the handle and its workspace (synchronises the device first).
  * NULL is accepted.  Statuses: HIP. */

@@ -21,7 +21,8 @@ HEADERS = [os.path.join(os.path.dirname(_PKG), "include", h) for h in ("fdllm.h"
 
 FDLLM_F32, FDLLM_BF16 = 0, 1
 STATUS = {0: "FDLLM_OK", -1: "FDLLM_ERR_ARG", -2: "FDLLM_ERR_SHAPE", -3: "FDLLM_ERR_ALIGN",
-          -4: "FDLLM_ERR_INDEX", -5: "FDLLM_ERR_ALLOC", -6: "FDLLM_ERR_HIP", -7: "FDLLM_ERR_UNSUPPORTED"}
+          -4: "FDLLM_ERR_INDEX", -5: "FDLLM_ERR_ALLOC", -6: "FDLLM_ERR_HIP", -7: "FDLLM_ERR_UNSUPPORTED",
+          -8: "FDLLM_ERR_SCRATCH"}
 
 
 class FdllmError(RuntimeError):
@@ -77,12 +78,14 @@ def load():
     lib.fdllm_get_plan.argtypes = [P, i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.fdllm_cache_destroy.argtypes = [P]
     lib.fdllm_probe_read.argtypes = [P, ctypes.c_int64, i32, P, P]
+    lib.fdllm_fused_step_noalloc.argtypes = [ctypes.POINTER(Config), P, i32, P, P, i32, P, P, P, P, P, P, P]
     lib.fdllm_status_str.argtypes = [ctypes.c_int]
     lib.fdllm_status_str.restype = ctypes.c_char_p
     for name in ("fdllm_validate_config", "fdllm_cache_init", "fdllm_prefill", "fdllm_fused_step",
                  "fdllm_step_project", "fdllm_step_attend", "fdllm_tracked_scores", "fdllm_select_tracked",
                  "fdllm_confidence", "fdllm_accept", "fdllm_fused_step_paged",
-                 "fdllm_set_tuning", "fdllm_get_plan", "fdllm_cache_destroy", "fdllm_probe_read"):
+                 "fdllm_set_tuning", "fdllm_get_plan", "fdllm_cache_destroy", "fdllm_probe_read",
+                 "fdllm_fused_step_noalloc"):
         getattr(lib, name).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -152,6 +155,32 @@ def probe_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int = 0, strea
         raise ValueError("sink must hold 16 bytes")
     _check(load().fdllm_probe_read(_ptr(buf), buf.numel() * buf.element_size(), workgroups, _ptr(sink),
                                    _stream(stream)), "fdllm_probe_read")
+
+
+def fused_step_noalloc(X, Q_idx, pos_ids, vis, W, Kc, Vc, O, LSE, H, Hkv, rope_base=10000.0, q_max=None,
+                       stream=None):
+    """The fused step without a handle (fdllm_fused_step_noalloc): the layer
+    shape comes from the tensors (X [B, x_rows, d], Kc [B, Hkv, N, dh]) and
+    H, Hkv; the workspace is the library's static per-device scratch."""
+    B, x_rows, d = X.shape
+    N, dh = Kc.shape[2], Kc.shape[3]
+    nq = Q_idx.shape[1]
+    cfg = make_config(B, N, d, H, Hkv, dh, q_max or max(1, nq), X.dtype, rope_base)
+    for name, t, shape in (("Q_idx", Q_idx, (B, nq)), ("pos_ids", pos_ids, (B, nq))):
+        if t.dtype != torch.int32 or tuple(t.shape) != shape:
+            raise ValueError("%s must be int32 [B, nq]" % name)
+    if vis is not None and (vis.dtype != torch.uint8 or tuple(vis.shape) != (B, nq, nq)):
+        raise ValueError("vis must be uint8 [B, nq, nq]")
+    if tuple(W.shape) != ((H + 2 * Hkv) * dh, d) or tuple(Vc.shape) != tuple(Kc.shape) or Kc.shape[:2] != (B, Hkv):
+        raise ValueError("W must be [(H + 2 Hkv) dh, d], Kc/Vc [B, Hkv, N, dh]")
+    if tuple(O.shape) != (B, nq, H, dh) or tuple(LSE.shape) != (B, nq, H) or LSE.dtype != torch.float32:
+        raise ValueError("O must be [B, nq, H, dh], LSE fp32 [B, nq, H]")
+    for t in (W, Kc, Vc, O):
+        if t.dtype != X.dtype:
+            raise ValueError("X, W, Kc, Vc and O share the layer dtype")
+    _check(load().fdllm_fused_step_noalloc(ctypes.byref(cfg), _ptr(X), x_rows, _ptr(Q_idx), _ptr(pos_ids), nq,
+                                           _ptr(vis), _ptr(W), _ptr(Kc), _ptr(Vc), _ptr(O), _ptr(LSE),
+                                           _stream(stream)), "fdllm_fused_step_noalloc")
 
 
 def make_config(B, N, d_model, H, Hkv, dh, q_max, dtype=torch.bfloat16, rope_base=10000.0) -> Config:

@@ -240,6 +240,7 @@ const char* fdllm_status_str(int status)
         case FDLLM_ERR_ALLOC: return "FDLLM_ERR_ALLOC: device workspace allocation failed";
         case FDLLM_ERR_HIP: return "FDLLM_ERR_HIP: HIP runtime or launch error";
         case FDLLM_ERR_UNSUPPORTED: return "FDLLM_ERR_UNSUPPORTED: shape not implemented";
+        case FDLLM_ERR_SCRATCH: return "FDLLM_ERR_SCRATCH: workspace larger than the allocation-free scratch";
         default: return "FDLLM: unknown status";
     }
 }

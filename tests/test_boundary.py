@@ -89,6 +89,26 @@ def test_read_probe_argument_errors_are_host_side(lib):
     assert lib.fdllm_probe_read(P(24), 1024, 0, P(16), None) == -3    # misaligned buffer
 
 
+def test_noalloc_step_host_side_errors(lib):
+    """The allocation-free step validates its arguments and sizes its
+    workspace against the static scratch before any HIP call."""
+    P = ctypes.c_void_p
+    a = [P(16)] * 2
+    def call(cfg, nq, x_rows=64):
+        return lib.fdllm_fused_step_noalloc(ctypes.byref(cfg) if cfg is not None else None, P(16), x_rows, P(16),
+                                            P(16), nq, None, P(16), P(16), P(16), P(16), P(16), None)
+    assert call(None, 1) == -1
+    assert call(_cfg(H=3), 1) == -1
+    assert call(_cfg(), 9) == -2                 # nq > q_max
+    assert call(_cfg(), 1, x_rows=0) == -2
+    assert call(_cfg(), 0) == 0                  # nothing to do
+    # a workspace larger than the 64 MiB scratch: q staging alone is
+    # B*Hkv*nq*G*dh*4 = 64*32*64*128*4 bytes = 64 MiB, plus the rest
+    big = _cfg(B=64, N=4096, d_model=256, H=32, Hkv=32, dh=128, q_max=64)
+    assert call(big, 64) == -8
+    assert lib.fdllm_status_str(-8).decode().startswith("FDLLM_ERR_SCRATCH")
+
+
 def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         binding._ptr(torch.zeros(4))
