@@ -12,11 +12,11 @@
 //  * one workgroup per (sequence, kv head, cache split): all nq * H/Hkv query
 //    rows that share a kv head are packed as the MFMA N dimension, so every
 //    K/V byte is read from HBM once per step;
-//  * one producer wave streams K/V tiles straight into a ring of LDS stages
-//    with global_load_lds (16 B per lane, no registers), keeping up to three
-//    tiles (~96 KB) in flight per CU; it waits on its own vmcnt and releases
-//    each stage with a barrier.  The consumer waves never issue global loads
-//    in the loop, they only read LDS and run MFMAs;
+//  * one or two producer waves stream K/V tiles straight into a ring of LDS
+//    stages with global_load_lds (16 B per lane, no registers), each keeping
+//    at most 48 of its loads (48 KB) in flight; a producer waits on its own
+//    vmcnt and releases each stage with a barrier.  The consumer waves never
+//    issue global loads in the loop, they only read LDS and run MFMAs;
 //  * LDS rows are 256 B with their 16 B chunks XOR-swizzled by the row index,
 //    which makes both fragment read patterns below bank-conflict free;
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 leaves each lane with one query
@@ -28,9 +28,10 @@
 //    registers, so P never goes through LDS;
 //  * consumer waves split the query rows and the keys of a tile; key-split
 //    waves merge their softmax states through LDS at the end;
-//  * with several cache splits, each writes its (max, sum, output) partial
-//    state and a small second kernel merges them into O and LSE (a kernel
-//    boundary is far cheaper than a device-scope fence per workgroup).
+//  * with several cache splits, each writes its (max, sum, normalised bf16
+//    output) partial state and a small second kernel merges them into O and
+//    LSE (a kernel boundary is far cheaper than a device-scope fence per
+//    workgroup).
 //
 // Key set of query row i (same definition as the CPU oracle): every cache
 // position not written by this step, plus each new row j that i may see.  A
@@ -66,6 +67,11 @@ struct AttnCfg {
     static constexpr int NS = RING / STAGE;
     static constexpr int DMA = STAGE / 1024;        // 1 KB DMA instructions per stage
     static constexpr int DMAP = DMA / NPROD;        // ... issued by each producer wave
+    // stages in flight per producer: at most 48 of its loads, so an issue
+    // never stalls on the 63-load counter (a stalled issue would hold back
+    // the release of the oldest stage)
+    static constexpr int AHEAD0 = 48 / DMAP > 1 ? 48 / DMAP : 1;
+    static constexpr int AHEAD = AHEAD0 < NS - 1 ? AHEAD0 : NS - 1;
     static constexpr int MERGE = (NWK / 2) * NWR * RG * 64 * (32 + 2) * 4;
     static constexpr int SCRATCH = NS * STAGE > MERGE ? NS * STAGE : MERGE;
     static_assert(NS >= 2 && NS * STAGE == RING, "stage ring");
@@ -255,15 +261,16 @@ attn_mfma_kernel(AttnArgs a)
             for (int c = 0; c < kMaxChunks; ++c)
                 if (64 * c < nq) posr[c] = pos_b[min(64 * c + lane, nq - 1)];
         }
-        // (without a mask the loads read a valid dummy byte; no branch or
-        // select around them, so nothing waits for them before the barrier)
-        const int8_t* vsrc = (const int8_t*)(vis_b ? vis_b : (const uint8_t*)pos_b);
-        const int vstep = vis_b ? 1 : 0;
+        // a few mask rows: their bytes, one per lane (under a mask these are
+        // read before the stream starts: issued after it they would queue
+        // behind the first stages' DMA)
+        if (vis_b && nunits <= 8 * C::NC) {
 #pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            const int u = min(wave + C::NC * t, max(nunits - 1, 0));
-            const int i = u / nch, col = min((u - i * nch) * 64 + lane, nq - 1);
-            vbyte[t] = vsrc[(size_t)(i * nq + col) * vstep];
+            for (int t = 0; t < 8; ++t) {
+                const int u = min(wave + C::NC * t, nunits - 1);
+                const int i = u / nch, col = min((u - i * nch) * 64 + lane, nq - 1);
+                vbyte[t] = vis_b[(size_t)i * nq + col];
+            }
         }
         if (vis_b) {
             for (int k = tid; k < kps; k += C::NC * 64) sSlot[k] = -1;
@@ -292,20 +299,20 @@ attn_mfma_kernel(AttnArgs a)
         // ================= producer waves: K/V tiles -> LDS ring =================
         const int p = wave - C::NC;
         int issued = 0;
-        for (; issued < min(C::NS - 1, n_main); ++issued)
+        for (; issued < min(C::AHEAD, n_main); ++issued)
             issue_main<C::TK, C::DMA, NPROD>(smem + (issued % C::NS) * C::STAGE, k0 + issued * C::TK, klast, Kg, Vg, p,
                                              lane, sTab, a.map.bits, a.Hkv, g);
         int ntot = n_main;
         int ndup = 0;
         for (int t = 0;; ++t) {
-            producer_sync<C::DMAP, C::NS - 2>(issued - t - 1);
+            producer_sync<C::DMAP, C::AHEAD - 1>(issued - t - 1);
             if (t == 0 && split == 0) {
                 // the consumers published the duplicate rows before this barrier
                 ndup = __builtin_amdgcn_readfirstlane(sMisc[0]);
                 ntot = n_main + (ndup + C::TK - 1) / C::TK;
             }
             if (t + 1 >= ntot) break;
-            for (; issued < ntot && issued < t + C::NS; ++issued) {
+            for (; issued < ntot && issued < t + 1 + C::AHEAD; ++issued) {
                 unsigned char* st = smem + (issued % C::NS) * C::STAGE;
                 if (issued < n_main)
                     issue_main<C::TK, C::DMA, NPROD>(st, k0 + issued * C::TK, klast, Kg, Vg, p, lane, sTab,
@@ -352,7 +359,8 @@ attn_mfma_kernel(AttnArgs a)
             if (lane == 0) sMisc[0] = ndup;
         }
         // visibility rows as bit words: chunk c of row i fills words 2c, 2c+1
-        if (nunits <= 8 * C::NC) {
+        // (only under a mask: without one no key is gated by visibility)
+        if (vis_b && nunits <= 8 * C::NC) {
             // (the bytes were loaded before the stream started)
 #pragma unroll
             for (int t = 0; t < 8; ++t) {
@@ -366,7 +374,7 @@ attn_mfma_kernel(AttnArgs a)
                     }
                 }
             }
-        } else {
+        } else if (vis_b) {
             // a large mask: each thread packs whole 32-column words, with the
             // loads of four words in flight at once (addresses are clamped
             // into the matrix and the bytes past the row end dropped)
@@ -474,11 +482,14 @@ attn_mfma_kernel(AttnArgs a)
                     for (int c = 0; c < 4; ++c) kf[kb][c] = *(const bf16x8*)(st + kofs[c] + kb * 16 * kRowB);
                 // (the hi and lo passes alternate between the two key blocks'
                 // accumulators, so back-to-back MFMAs do not depend on each other)
-                f32x4 sc[RG][KB];
+                f32x4 sc[RG][KB], sl[RG][KB];
 #pragma unroll
                 for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) sc[rg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int kb = 0; kb < KB; ++kb) {
+                        sc[rg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        sl[rg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -490,8 +501,12 @@ attn_mfma_kernel(AttnArgs a)
                     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                         for (int rg = 0; rg < RG; ++rg)
-                            sc[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][c], ql[rg][c], sc[rg][kb], 0, 0, 0);
+                            sl[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][c], ql[rg][c], sl[rg][kb], 0, 0, 0);
                 }
+#pragma unroll
+                for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+                    for (int kb = 0; kb < KB; ++kb) sc[rg][kb] += sl[rg][kb];
                 // all K fragment reads are issued before the first MFMA waits on one
                 __builtin_amdgcn_sched_group_barrier(0x100, 4 * KB, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 8 * KB * RG, 0);
@@ -618,6 +633,7 @@ attn_mfma_kernel(AttnArgs a)
                         o[rg][db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[db], pf[rg], o[rg][db], 0, 0, 0);
             }
         }
+
         // per-lane sums -> row sums (row lr is spread over the 4 lane groups)
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) l_run[rg] = sum4(l_run[rg]);
@@ -697,17 +713,26 @@ attn_mfma_kernel(AttnArgs a)
         return;
     }
 
-    // publish this split's partial state (max in log2 units, sum, unnormalised
-    // output); the combine kernel merges the splits after this launch ends
+    // publish this split's partial state (max in log2 units, sum, and the
+    // split's normalised output O_s / l_s in bf16: half the bytes of the
+    // unnormalised fp32 sum, and a weighted mean of values the output is
+    // rounded to anyway); the combine kernel merges the splits after this
+    // launch ends
     if (writer) {
 #pragma unroll
         for (int rg = 0; rg < RG; ++rg) {
             const int row = (wr * RG + rg) * 16 + lr;
             if (row >= a.R) continue;
             const size_t prow = ((size_t)bg * a.splits + split) * a.Rpad + row;
-            float* pp = a.apart + prow * kDH;
+            bf16* pp = a.apart + prow * kDH;
+            const float inv = l_run[rg] > 0.f ? 1.f / l_run[rg] : 0.f;
 #pragma unroll
-            for (int db = 0; db < 8; ++db) *(f32x4*)(pp + db * 16 + lg * 4) = o[rg][db];
+            for (int db = 0; db < 8; ++db) {
+                bf16x4v v;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = (bf16)(o[rg][db][i] * inv);
+                *(bf16x4v*)(pp + db * 16 + lg * 4) = v;
+            }
             if (lg == 0) {
                 a.aml[prow * 2 + 0] = m_run[rg];
                 a.aml[prow * 2 + 1] = l_run[rg];
@@ -716,8 +741,9 @@ attn_mfma_kernel(AttnArgs a)
     }
 }
 
-// Merge of the cache splits: O = sum_s 2^(m_s - M) acc_s / L and
-// LSE = (M + log2 L) ln 2 with M = max_s m_s, L = sum_s 2^(m_s - M) l_s.
+// Merge of the cache splits: O = sum_s 2^(m_s - M) l_s O_s / L and
+// LSE = (M + log2 L) ln 2 with M = max_s m_s, L = sum_s 2^(m_s - M) l_s, where
+// O_s is split s's normalised output.
 // A workgroup takes 8 query rows of one (sequence, kv head): the (m, l) of
 // every split go through LDS first, then each thread sums 4 output dims of
 // its row over the splits with the loads of 8 splits in flight at a time.
@@ -751,27 +777,28 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a)
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     float L = 0.f;
     int sp = 0;
+    auto to_f32x4 = [](bf16x4v v) { return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]}; };
     for (; sp + 8 <= S; sp += 8) {
-        f32x4 v[8];
+        bf16x4v v[8];
         float l[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const size_t pr = pbase + (size_t)(sp + u) * a.Rpad + rowc;
-            v[u] = *(const f32x4*)(a.apart + pr * kDH + d4 * 4);
+            v[u] = *(const bf16x4v*)(a.apart + pr * kDH + d4 * 4);
             l[u] = a.aml[pr * 2 + 1];
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const float w = sW[r * S + sp + u];
-            acc += v[u] * w;
-            L += l[u] * w;
+            const float wl = sW[r * S + sp + u] * l[u];
+            acc += to_f32x4(v[u]) * wl;
+            L += wl;
         }
     }
     for (; sp < S; ++sp) {
         const size_t pr = pbase + (size_t)sp * a.Rpad + rowc;
-        const float w = sW[r * S + sp];
-        acc += *(const f32x4*)(a.apart + pr * kDH + d4 * 4) * w;
-        L += a.aml[pr * 2 + 1] * w;
+        const float wl = sW[r * S + sp] * a.aml[pr * 2 + 1];
+        acc += to_f32x4(*(const bf16x4v*)(a.apart + pr * kDH + d4 * 4)) * wl;
+        L += wl;
     }
     if (row >= a.R) return;
     const int b = bg / a.Hkv, g = bg - b * a.Hkv;

@@ -23,7 +23,7 @@ struct fdllm_ctx {
     float* qbuf = nullptr;
     void* sideK = nullptr;
     void* sideV = nullptr;
-    float* apart = nullptr;
+    bf16* apart = nullptr;
     float* aml = nullptr;
     size_t apart_rows = 0;        // (B*Hkv) * splits * Rpad rows available
     float* mpart = nullptr;       // [B * Hkv, N] per kv head sums of the tracked-set scores
@@ -103,7 +103,8 @@ void free_ws(fdllm_ctx* h)
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
     h->rope = nullptr; h->qbuf = nullptr; h->sideK = h->sideV = nullptr;
-    h->apart = h->aml = nullptr;
+    h->apart = nullptr;
+    h->aml = nullptr;
     h->mpart = nullptr;
 }
 
@@ -120,8 +121,9 @@ int ensure_split_ws(fdllm_ctx* h)
     if (arows > h->apart_rows) {
         if (h->apart) (void)hipFree(h->apart);
         if (h->aml) (void)hipFree(h->aml);
-        h->apart = h->aml = nullptr;
-        if (hipMalloc(&h->apart, arows * c.dh * sizeof(float)) != hipSuccess ||
+        h->apart = nullptr;
+    h->aml = nullptr;
+        if (hipMalloc(&h->apart, arows * c.dh * sizeof(bf16)) != hipSuccess ||
             hipMalloc(&h->aml, arows * 2 * sizeof(float)) != hipSuccess) {
             h->apart_rows = 0;
             return FDLLM_ERR_ALLOC;

@@ -66,7 +66,7 @@ struct AttnArgs {
     const uint8_t* vis;     // [B, nq, nq] or NULL
     void* O;                // [B, nq, H, dh]
     float* LSE;             // [B, nq, H]
-    float* apart;           // [B * Hkv, splits, Rpad, dh]  unnormalised partial outputs
+    bf16* apart;            // [B * Hkv, splits, Rpad, dh]  each split's normalised output (O_s / l_s)
     float* aml;             // [B * Hkv, splits, Rpad, 2]    (max in log2 units, sum)
     int B, N, H, Hkv, dh, G, nq, q_max;
     int R;                  // nq * G query rows per (sequence, kv head)

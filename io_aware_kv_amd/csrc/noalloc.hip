@@ -73,7 +73,7 @@ Layout layout(const fdllm_config_t& c, int nq, const Plan& p)
     l.sideK = at; at += up256((size_t)c.B * c.Hkv * nq * c.dh * elt);
     l.sideV = at; at += up256((size_t)c.B * c.Hkv * nq * c.dh * elt);
     const size_t arows = (p.attn_family == FAMILY_MFMA && p.splits > 1) ? (size_t)c.B * c.Hkv * p.splits * p.Rpad : 0;
-    l.apart = at; at += up256(arows * c.dh * sizeof(float));
+    l.apart = at; at += up256(arows * c.dh * sizeof(bf16));
     l.aml = at;   at += up256(arows * 2 * sizeof(float));
     l.total = at;
     return l;
@@ -135,7 +135,7 @@ extern "C" int fdllm_fused_step_noalloc(const fdllm_config_t* cfg, const void* X
     AttnArgs aa{};
     aa.qbuf = pa.qbuf; aa.Kc = Kc; aa.Vc = Vc; aa.sideK = pa.sideK; aa.sideV = pa.sideV;
     aa.pos_ids = pos_ids; aa.vis = vis_mask; aa.O = O; aa.LSE = LSE;
-    aa.apart = (float*)(base + lay.apart); aa.aml = (float*)(base + lay.aml);
+    aa.apart = (bf16*)(base + lay.apart); aa.aml = (float*)(base + lay.aml);
     aa.B = c.B; aa.N = c.N; aa.H = c.H; aa.Hkv = c.Hkv; aa.dh = c.dh; aa.G = G; aa.nq = nq; aa.q_max = nq;
     aa.R = p.R; aa.Rpad = p.Rpad; aa.splits = p.splits; aa.keys_per_split = p.keys_per_split;
     aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.dh));
