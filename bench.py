@@ -345,6 +345,28 @@ def phase_fraction(nbytes, flops, us):
     return {"bound": "hbm", "achieved": round(ach, 1), "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBPS, 4)}
 
 
+def read_floor_us(nbytes, dev, stream, reps=20):
+    """Time of one streaming read of nbytes with the library's read probe
+    (best of four grid sizes), over enough rotating buffers that no read
+    finds its bytes in the 256 MB Infinity Cache: what this GPU needs to
+    read a phase's bytes once, latency and ramp included."""
+    import torch
+    from io_aware_kv_amd import binding
+    n16 = max(1, nbytes // 16)
+    nbuf = max(3, -(-768 * 2 ** 20 // (n16 * 16)))
+    bufs = [torch.empty(n16 * 4, dtype=torch.int32, device=dev) for _ in range(nbuf)]
+    for b in bufs:
+        b.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    best = None
+    for wgs in (256, 512, 1024, 2048):
+        ms = time_launches(lambda buf: binding.probe_read(buf, sink, workgroups=wgs, stream=stream), bufs, stream,
+                           max(reps, nbuf), 3)
+        best = ms if best is None else min(best, ms)
+    del bufs
+    return best * 1e3
+
+
 def measure_config(cid, steps, warmup, dev, read_GBps=None):
     """Step, projection and attention times of one layer workload, each launch
     kind timed alone back to back over rotating buffer sets, with the
@@ -382,6 +404,9 @@ def measure_config(cid, steps, warmup, dev, read_GBps=None):
            "attn_GBps": round(attn_GBps, 1), "attn_hbm_frac": round(attn_GBps / HBM_PEAK_GBPS, 4)}
     if read_GBps:
         out["attn_frac_of_read_ceiling"] = round(attn_GBps / read_GBps, 4)
+    floor = read_floor_us(ab["attn"], dev, stream)
+    out["attn_read_floor_us"] = round(floor, 3)
+    out["attn_frac_of_read_floor"] = round(floor / (attn_ms * 1e3), 4)
     return out
 
 
@@ -589,6 +614,8 @@ def main():
             "proj_mfma_frac": round(ab["qkv_flops"] / (proj_avg * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
             "attn_hbm_frac": round(attn_GBps / HBM_PEAK_GBPS, 4),
             "attn_frac_of_read_ceiling": round(attn_GBps / read_GBps, 4),
+            # one streaming read of the phase's bytes with the read probe
+            "attn_read_floor_us": round(read_floor_us(ab["attn"], dev, stream), 3),
             # distribution over the evented pass (an event around each launch)
             "proj_us_pct": pct(proj_ms),
             "attn_us_pct": pct(attn_ms),
