@@ -347,13 +347,16 @@ def phase_fraction(nbytes, flops, us):
 
 def read_floor_us(nbytes, dev, stream, reps=20):
     """Time of one streaming read of nbytes with the library's read probe
-    (best of four grid sizes), over enough rotating buffers that no read
-    finds its bytes in the 256 MB Infinity Cache: what this GPU needs to
-    read a phase's bytes once, latency and ramp included."""
+    (best of four grid sizes), over rotating buffers (enough that a phase of
+    more than 12 MB never finds its bytes in the 256 MB Infinity Cache):
+    what this GPU needs to read a phase's bytes once, latency and ramp
+    included."""
     import torch
     from io_aware_kv_amd import binding
     n16 = max(1, nbytes // 16)
-    nbuf = max(3, -(-768 * 2 ** 20 // (n16 * 16)))
+    # (at most 64 buffers: a phase of a few MB stays in the caches whatever
+    # the rotation, and its read is latency-bound anyway)
+    nbuf = min(64, max(3, -(-768 * 2 ** 20 // (n16 * 16))))
     bufs = [torch.empty(n16 * 4, dtype=torch.int32, device=dev) for _ in range(nbuf)]
     for b in bufs:
         b.fill_(1)

@@ -26,6 +26,8 @@ KERNEL_SOURCES = {
     "attn_mfma": os.path.join(ROOT, "io_aware_kv_amd", "csrc", "attn_mfma.hip"),
     "attn_combine": os.path.join(ROOT, "io_aware_kv_amd", "csrc", "attn_mfma.hip"),
     "proj_mfma": os.path.join(ROOT, "io_aware_kv_amd", "csrc", "proj_mfma.hip"),
+    "attn_generic": os.path.join(ROOT, "io_aware_kv_amd", "csrc", "generic_kernels.hip"),
+    "proj_generic": os.path.join(ROOT, "io_aware_kv_amd", "csrc", "generic_kernels.hip"),
 }
 
 
