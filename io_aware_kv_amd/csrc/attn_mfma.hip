@@ -286,11 +286,15 @@ attn_mfma_kernel(AttnArgs a)
     consumer_sync();
 
     float m_run[RG], l_run[RG];
+    // the score accumulators start at -ref, so a row's scores come out
+    // relative to its reference max (ref = 0 until the row has one)
+    f32x4 negref[RG];
     f32x4 o[RG][8];
 #pragma unroll
     for (int rg = 0; rg < RG; ++rg) {
         m_run[rg] = kNegBig;
         l_run[rg] = 0.f;
+        negref[rg] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int db = 0; db < 8; ++db) o[rg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -480,33 +484,49 @@ attn_mfma_kernel(AttnArgs a)
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int c = 0; c < 4; ++c) kf[kb][c] = *(const bf16x8*)(st + kofs[c] + kb * 16 * kRowB);
-                // (the hi and lo passes alternate between the two key blocks'
-                // accumulators, so back-to-back MFMAs do not depend on each other)
-                f32x4 sc[RG][KB], sl[RG][KB];
+                // The accumulators start at the row's -ref.  With four or more
+                // accumulators one chain each takes the hi then the lo products;
+                // with fewer, the lo products go to a second set of chains (so
+                // back-to-back MFMAs do not depend on each other) added at the end.
+                f32x4 sc[RG][KB];
+                if constexpr (RG * KB >= 4) {
 #pragma unroll
-                for (int rg = 0; rg < RG; ++rg)
+                    for (int c = 0; c < 4; ++c)
 #pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) {
-                        sc[rg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-                        sl[rg][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                            for (int rg = 0; rg < RG; ++rg)
+                                sc[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    kf[kb][c], qh[rg][c], c == 0 ? negref[rg] : sc[rg][kb], 0, 0, 0);
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                            for (int rg = 0; rg < RG; ++rg)
+                                sc[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][c], ql[rg][c], sc[rg][kb], 0, 0, 0);
+                } else {
+                    f32x4 sl[RG][KB];
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                            for (int rg = 0; rg < RG; ++rg)
+                                sc[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    kf[kb][c], qh[rg][c], c == 0 ? negref[rg] : sc[rg][kb], 0, 0, 0);
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                            for (int rg = 0; rg < RG; ++rg)
+                                sl[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    kf[kb][c], ql[rg][c], c == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : sl[rg][kb], 0, 0, 0);
                     }
 #pragma unroll
-                for (int c = 0; c < 4; ++c) {
+                    for (int rg = 0; rg < RG; ++rg)
 #pragma unroll
-                    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                        for (int rg = 0; rg < RG; ++rg)
-                            sc[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][c], qh[rg][c], sc[rg][kb], 0, 0, 0);
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-                        for (int rg = 0; rg < RG; ++rg)
-                            sl[rg][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[kb][c], ql[rg][c], sl[rg][kb], 0, 0, 0);
+                        for (int kb = 0; kb < KB; ++kb) sc[rg][kb] += sl[rg][kb];
                 }
-#pragma unroll
-                for (int rg = 0; rg < RG; ++rg)
-#pragma unroll
-                    for (int kb = 0; kb < KB; ++kb) sc[rg][kb] += sl[rg][kb];
                 // all K fragment reads are issued before the first MFMA waits on one
                 __builtin_amdgcn_sched_group_barrier(0x100, 4 * KB, 0);
                 __builtin_amdgcn_sched_group_barrier(0x008, 8 * KB * RG, 0);
@@ -585,6 +605,8 @@ attn_mfma_kernel(AttnArgs a)
                 // max exceeds it by more than 2^8, so p <= 256 and the
                 // accumulators are rescaled a few times per split.  The
                 // decision is per row; the block is skipped when no row grows.
+                // The scores are already relative to the reference (ref), so
+                // the exponent needs no subtraction unless the reference moves.
                 float pv[RG][KB][4];
 #pragma unroll
                 for (int rg = 0; rg < RG; ++rg) {
@@ -593,23 +615,31 @@ attn_mfma_kernel(AttnArgs a)
                     for (int kb = 1; kb < KB; ++kb)
                         mx = fmaxf(mx, fmaxf(fmaxf(sc[rg][kb][0], sc[rg][kb][1]), fmaxf(sc[rg][kb][2], sc[rg][kb][3])));
                     mx = max4(mx);
-                    const bool grow = mx > m_run[rg] + 8.f;
+                    const float ref = -negref[rg][0];
+                    const bool grow = mx + ref > m_run[rg] + 8.f;
                     if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                        const float shift = grow ? mx : 0.f;
                         if (grow) {
-                            const float alpha = __builtin_amdgcn_exp2f(m_run[rg] - mx);
+                            const float mnew = mx + ref;
+                            const float alpha = __builtin_amdgcn_exp2f(m_run[rg] - mnew);
                             l_run[rg] *= alpha;
 #pragma unroll
                             for (int db = 0; db < 8; ++db) o[rg][db] *= alpha;
-                            m_run[rg] = mx;
+                            m_run[rg] = mnew;
+                            negref[rg] = f32x4{-mnew, -mnew, -mnew, -mnew};
                         }
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) sc[rg][kb][i] -= shift;
                     }
                     float lsum = 0.f;
 #pragma unroll
                     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
-                            pv[rg][kb][i] = __builtin_amdgcn_exp2f(sc[rg][kb][i] - m_run[rg]);   // exp2(-inf) = 0
-                            lsum += pv[rg][kb][i];
+                            pv[rg][kb][i] = __builtin_amdgcn_exp2f(sc[rg][kb][i]);   // exp2(-inf) = 0
+                            lsum = kb == 0 && i == 0 ? pv[rg][0][0] : lsum + pv[rg][kb][i];
                         }
                     l_run[rg] += lsum;
                 }
