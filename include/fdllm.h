@@ -92,7 +92,7 @@ typedef struct {
     int32_t attn_splits;    /* cache splits per (sequence, kv head) in the attention */
     int32_t gemm_splitk;    /* reserved: the projection does not split d_model (plan reports 1) */
     int32_t kernel_family;  /* 0 auto, 1 tiled MFMA (bf16 only), 2 generic scalar */
-    int32_t proj_tile;      /* 0 auto, 1..10: a tile configuration of the MFMA projection */
+    int32_t proj_tile;      /* 0 auto, 1..11: a tile configuration of the MFMA projection */
 } fdllm_tuning_t;
 
 typedef struct fdllm_ctx* fdllm_handle_t;
@@ -245,7 +245,7 @@ int fdllm_accept(const int32_t* x_hat, const int32_t* x_tilde, const float* c_ti
                  float gamma, int32_t* n_accept, void* stream);
 
 /* Set (tuning != NULL) or reset (NULL) the launch-shape overrides of h.
- * Statuses: ARG (a negative field, kernel_family > 2, proj_tile > 10). */
+ * Statuses: ARG (a negative field, kernel_family > 2, proj_tile > 11). */
 int fdllm_set_tuning(fdllm_handle_t h, const fdllm_tuning_t* tuning);
 
 /* Report the launch shapes fdllm_fused_step would use for nq: attention

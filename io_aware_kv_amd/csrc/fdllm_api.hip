@@ -331,7 +331,7 @@ int fdllm_set_tuning(fdllm_handle_t h, const fdllm_tuning_t* t)
 {
     if (!h) return FDLLM_ERR_ARG;
     if (t && (t->attn_splits < 0 || t->gemm_splitk < 0 || t->kernel_family < 0 || t->kernel_family > 2 ||
-              t->proj_tile < 0 || t->proj_tile > 10))
+              t->proj_tile < 0 || t->proj_tile > 11))
         return FDLLM_ERR_ARG;
     h->tune = t ? *t : fdllm_tuning_t{0, 0, 0, 0};
     int st = set_device(h);

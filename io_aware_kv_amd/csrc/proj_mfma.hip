@@ -413,9 +413,10 @@ hipError_t launch_tile(const ProjArgs& a, hipStream_t s)
 
 // Tile configurations (rows BM x 16-column blocks NCB): narrow tiles with a
 // 3-stage ring (two workgroups per CU), 64 x 64 tiles, and 128-column (one
-// head) tiles of 96 to 256 rows; the 208-row tile splits each stage's MFMA
-// steps between two wave groups (choice 9; choice 7 is the same tile without
-// the split), the 256-row tile runs eight consumer waves in a 2 x 4 layout.
+// head) tiles of 96 to 256 rows; the 208-row and 176-row tiles split each
+// stage's MFMA steps between two wave groups (choices 9 and 11; choices 7 and
+// 6 are the same tiles without the split), the 256-row tile runs eight
+// consumer waves in a 2 x 4 layout.
 struct ProjChoice { int bm, ncb; };
 static const ProjChoice kProjChoices[] = {
     {0, 0},
@@ -423,6 +424,7 @@ static const ProjChoice kProjChoices[] = {
     {128, 8}, {176, 8}, {208, 8}, {96, 8},  // 5-8
     {208, 8},                             // 9
     {256, 8},                             // 10
+    {176, 8},                             // 11
 };
 constexpr int kNumChoices = (int)(sizeof(kProjChoices) / sizeof(kProjChoices[0]));
 
@@ -436,15 +438,20 @@ constexpr int kNumChoices = (int)(sizeof(kProjChoices) / sizeof(kProjChoices[0])
 // (1408 rows of 96 heads: 176-row tiles in 3 rounds, 160 us, against 205 us
 // for 128-row tiles in 4.1 rounds, and 172 us for 256-row tiles in 2.25;
 // 1152 rows: 256-row tiles in 2 rounds, 119 us, against 154 us for 176-row
-// tiles in 2.6).  The 208-row tile runs with its k split (faster than without
-// at every row count measured).
+// tiles in 2.6).  The 208-row and 176-row tiles run with their k split
+// (faster than without at every row count measured: 176 rows, 352 rows of 96
+// heads 54.6 against 55.4 us, 1408 rows 162 against 166 us).  With the
+// split a SIMD holds two consumer waves, yet the tile is no more than a few
+// per cent faster: the loop is bound by the rate at which the stages land in
+// LDS (the same loop without its MFMAs takes 53 of the 55 us), not by the
+// fragment reads or the MFMAs.
 static int default_choice(int M, int heads)
 {
     if (M <= 32 && heads < 64) return M <= 16 ? 1 : 2;
     if (M <= 128) return 4;
     int best = 5;
     long best_cost = -1;
-    for (int c : {4, 8, 5, 6, 9, 10}) {
+    for (int c : {4, 8, 5, 11, 9, 10}) {
         const ProjChoice& p = kProjChoices[c];
         const long tiles = (long)((M + p.bm - 1) / p.bm) * heads * (8 / p.ncb);
         const long cost = ((tiles + 255) / 256) * (p.bm + 16 * p.ncb);
@@ -476,6 +483,7 @@ hipError_t launch_proj_mfma(const ProjArgs& a, hipStream_t s)
         case 8: return launch_tile<96, 8, 1, 1, 4, 8, 64, 2>(a, s);
         case 9: return launch_tile<208, 8, 2, 1, 2, 8, 64, 2>(a, s);
         case 10: return launch_tile<256, 8, 1, 2, 4, 8, 64, 2>(a, s);
+        case 11: return launch_tile<176, 8, 2, 1, 4, 8, 64, 2>(a, s);
         default: return hipErrorInvalidValue;
     }
 }

@@ -150,7 +150,7 @@ def test_forced_splits(splits, nq):
     compare(wl, g, r, "splits%d-nq%d" % (splits, nq))
 
 
-@pytest.mark.parametrize("choice", list(range(1, 11)))
+@pytest.mark.parametrize("choice", list(range(1, 12)))
 def test_forced_projection_tiles(choice):
     """Every projection tile configuration (tuning proj_tile) on a case with
     ragged row tiles, GQA, duplicates and a mask."""
