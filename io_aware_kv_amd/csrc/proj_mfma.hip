@@ -202,13 +202,22 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
         }
         if (!a.prefill && head >= a.H) {
             // first-occurrence rule: a row owns the cache write of its
-            // position unless an earlier row of its sequence has the same one
-            for (int r = tid; r < BM; r += C::NCW * 64) {
-                const int m = m0 + r;
-                if (m >= M || sDst[r] < 0) continue;
-                const int b = m / a.rows_per_seq, j = m - b * a.rows_per_seq;
-                const int32_t* pb = a.pos_ids + (size_t)b * a.rows_per_seq;
-                const int p = sPos[r];
+            // position unless an earlier row of its sequence has the same one.
+            // Each wave copies the positions of the tile's sequences (from the
+            // first row of the first one) into its own slice of the last ring
+            // stage, which no DMA writes before the first barrier, and
+            // compares from there: one round trip to memory instead of one
+            // per eight earlier rows.
+            const int mlo = (m0 / a.rows_per_seq) * a.rows_per_seq;
+            const int cnt = min(m0 + BM, M) - mlo;
+            const int pw = (cnt + 3) & ~3;
+            const bool staged = (size_t)pw * C::NCW * 4 <= (size_t)C::STAGE;
+            int* sP = (int*)(smem + (size_t)(C::NS - 1) * C::STAGE) + wave * pw;
+            if (staged)
+                for (int e = lane; e < cnt; e += 64) sP[e] = a.pos_ids[mlo + e];
+            // (the two sources in separate loops, so each compiles to its own
+            // kind of load rather than a generic one)
+            auto owns = [](const int* pb, int j, int p) {
                 bool own = true;
                 int jj = 0;
                 for (; jj + 8 <= j; jj += 8) {
@@ -219,6 +228,14 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
                     for (int u = 0; u < 8; ++u) own = own && v[u] != p;
                 }
                 for (; jj < j; ++jj) own = own && pb[jj] != p;
+                return own;
+            };
+            for (int r = tid; r < BM; r += C::NCW * 64) {
+                const int m = m0 + r;
+                if (m >= M || sDst[r] < 0) continue;
+                const int b = m / a.rows_per_seq, j = m - b * a.rows_per_seq;
+                const bool own = staged ? owns(sP + (b * a.rows_per_seq - mlo), j, sPos[r])
+                                        : owns(a.pos_ids + (size_t)b * a.rows_per_seq, j, sPos[r]);
                 if (!own) sDst[r] = 0;
             }
         }
