@@ -136,7 +136,7 @@ size_t attn_generic_lds(int dh, int nq)
            sizeof(int) * (3 * (size_t)nq + kGK + 1);
 }
 
-template <typename T>
+template <typename T, int DU>
 __global__ void __launch_bounds__(kGenThreads) attn_generic_kernel(AttnArgs a)
 {
     extern __shared__ float smem[];
@@ -198,9 +198,11 @@ __global__ void __launch_bounds__(kGenThreads) attn_generic_kernel(AttnArgs a)
     const T* SVb = (const T*)a.sideV + ((size_t)b * a.Hkv + g) * a.q_max * dh;
 
     float m = -1.0e30f, l = 0.f;
-    float acc[16];                               // dh <= 256: dims kq + 16 u
+    // dims kq + 16 u, u < DU (16 * DU >= dh); lanes past dh run on a clamped
+    // dim and are never stored, so the loops carry no per-dim branches
+    float acc[DU];
 #pragma unroll
-    for (int u = 0; u < 16; ++u) acc[u] = 0.f;
+    for (int u = 0; u < DU; ++u) acc[u] = 0.f;
     // a chunk's K and V rows move as 16-byte units (kEPU elements; a row is
     // dh / kEPU units), at most kUPT per thread; the next chunk is fetched
     // into registers while this one is worked on.  The unit coordinates
@@ -291,9 +293,21 @@ __global__ void __launch_bounds__(kGenThreads) attn_generic_kernel(AttnArgs a)
             }
             float d0 = 0.f;
             if (keep) {
+                // four independent partial sums, so the LDS reads of one
+                // group of four dims are in flight together
                 const float* qr = sq + rr * dh;
                 const float* kr = sk + k * (dh + 1);
-                for (int d = 0; d < dh; ++d) d0 = fmaf(qr[d], kr[d], d0);
+                float d1 = 0.f, d2 = 0.f, d3 = 0.f;
+                int d = 0;
+#pragma unroll 2
+                for (; d + 4 <= dh; d += 4) {
+                    d0 = fmaf(qr[d], kr[d], d0);
+                    d1 = fmaf(qr[d + 1], kr[d + 1], d1);
+                    d2 = fmaf(qr[d + 2], kr[d + 2], d2);
+                    d3 = fmaf(qr[d + 3], kr[d + 3], d3);
+                }
+                for (; d < dh; ++d) d0 = fmaf(qr[d], kr[d], d0);
+                d0 = (d0 + d1) + (d2 + d3);
             }
             s[h] = keep ? d0 * a.scale_log2 : -INFINITY;
         }
@@ -311,16 +325,13 @@ __global__ void __launch_bounds__(kGenThreads) attn_generic_kernel(AttnArgs a)
         sp[rr * kGK + kq + 16] = p1;
         __syncthreads();
 #pragma unroll
-        for (int u = 0; u < 16; ++u) acc[u] *= alpha;
-#pragma unroll 1
+        for (int u = 0; u < DU; ++u) acc[u] *= alpha;
+#pragma unroll 4
         for (int k = 0; k < kGK; ++k) {
             const float pk = sp[rr * kGK + k];
             const float* vr = sv + k * dh;
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int d = kq + 16 * u;
-                if (d < dh) acc[u] = fmaf(pk, vr[d], acc[u]);
-            }
+            for (int u = 0; u < DU; ++u) acc[u] = fmaf(pk, vr[min(kq + 16 * u, dh - 1)], acc[u]);
         }
         __syncthreads();
     }
@@ -330,12 +341,15 @@ __global__ void __launch_bounds__(kGenThreads) attn_generic_kernel(AttnArgs a)
     T* o = (T*)a.O + orow * dh;
     const float inv = (live && l > 0.f) ? 1.f / l : 0.f;
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
+    for (int u = 0; u < DU; ++u) {
         const int d = kq + 16 * u;
         if (d < dh) o[d] = from_f32<T>(acc[u] * inv);
     }
     if (kq == 0) a.LSE[orow] = (live && l > 0.f) ? (m + log2f(l)) * 0.69314718055994531f : -INFINITY;
 }
+
+template <auto K>
+struct KernelTag { static constexpr auto value = K; };
 
 }  // namespace
 
@@ -361,14 +375,22 @@ hipError_t launch_attn_generic(const AttnArgs& a, int dtype, hipStream_t s)
     if (a.dh > 256) return hipErrorInvalidValue;
     const size_t shm = attn_generic_lds(a.dh, a.nq);
     if (shm > 160 * 1024) return hipErrorInvalidValue;
+    const int du = a.dh <= 32 ? 2 : a.dh <= 64 ? 4 : a.dh <= 128 ? 8 : 16;
+    auto go = [&](auto kern) {
+        (void)allow_full_lds<decltype(kern)::value>();
+        (void)hipGetLastError();
+        hipLaunchKernelGGL(decltype(kern)::value, dim3(blocks), dim3(kGenThreads), shm, s, a);
+    };
     if (dtype == 0) {
-        (void)allow_full_lds<attn_generic_kernel<float>>();
-        (void)hipGetLastError();
-        hipLaunchKernelGGL(attn_generic_kernel<float>, dim3(blocks), dim3(kGenThreads), shm, s, a);
+        if (du == 2) go(KernelTag<attn_generic_kernel<float, 2>>{});
+        else if (du == 4) go(KernelTag<attn_generic_kernel<float, 4>>{});
+        else if (du == 8) go(KernelTag<attn_generic_kernel<float, 8>>{});
+        else go(KernelTag<attn_generic_kernel<float, 16>>{});
     } else {
-        (void)allow_full_lds<attn_generic_kernel<bf16>>();
-        (void)hipGetLastError();
-        hipLaunchKernelGGL(attn_generic_kernel<bf16>, dim3(blocks), dim3(kGenThreads), shm, s, a);
+        if (du == 2) go(KernelTag<attn_generic_kernel<bf16, 2>>{});
+        else if (du == 4) go(KernelTag<attn_generic_kernel<bf16, 4>>{});
+        else if (du == 8) go(KernelTag<attn_generic_kernel<bf16, 8>>{});
+        else go(KernelTag<attn_generic_kernel<bf16, 16>>{});
     }
     return hipGetLastError();
 }
