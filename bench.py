@@ -541,9 +541,20 @@ def main():
         return {"p10": round(v[n // 10] * 1e3, 3), "p50": round(v[n // 2] * 1e3, 3),
                 "p90": round(v[min(n - 1, (n * 9) // 10)] * 1e3, 3)}
 
+    # host cost of submitting a step: the enqueue loop alone (the launches
+    # queue up on the device; this is the Python binding's and the library's
+    # time per step, not the device's)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(sets[i % n_sets])
+    host_submit_us = (time.perf_counter() - t0) / args.steps * 1e6
+    torch.cuda.synchronize()
+
     copy_GBps, read_GBps = device_rates(dev, stream)
-    log("bench: %.2f us/step (proj %.2f us, attn %.2f us alone), wall %.3f s; device copy %.0f GB/s, read %.0f GB/s" %
-        (ms_per_step * 1e3, proj_avg * 1e3, attn_avg * 1e3, wall, copy_GBps, read_GBps))
+    log("bench: %.2f us/step (proj %.2f us, attn %.2f us alone), wall %.3f s, host submit %.1f us/step; "
+        "device copy %.0f GB/s, read %.0f GB/s" %
+        (ms_per_step * 1e3, proj_avg * 1e3, attn_avg * 1e3, wall, host_submit_us, copy_GBps, read_GBps))
 
     # warm-cache reference: the same set every step (Infinity Cache may hold it)
     warm_ms = time_launches(lambda st: step(st), [sets[0]], stream, min(args.steps, 50), 0)
@@ -608,6 +619,7 @@ def main():
         "latency_us": round(ms_per_step * 1e3, 3),
         "queries_per_s": round(ls.B * wl.nq / (ms_per_step * 1e-3), 1),
         "warm_cache_latency_us": round(warm_ms * 1e3, 3),
+        "host_submit_us_per_step": round(host_submit_us, 2),
         "phases": {
             # each launch kind alone, back to back
             "proj_us": round(proj_avg * 1e3, 3),

@@ -77,6 +77,7 @@ def test_bench_json_line_on_the_gpu():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
     assert d["device_read_GBps"] > 0 and d["device_copy_GBps"] > 0
+    assert d["host_submit_us_per_step"] > 0
     # the other workloads of the target set: step and phase figures of each
     assert set(d["configs"]) == {"workload1", "workload2", "workload4"}
     for c in d["configs"].values():
