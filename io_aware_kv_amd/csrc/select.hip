@@ -367,24 +367,52 @@ __global__ void __launch_bounds__(kMassWaves * 64) key_mass_kernel(MassArgs a)
                 const int owner = ownu[u] == 0x7fffffff ? -1 : ownu[u];
                 const bool gated = vis_b != nullptr && owner >= 0;
                 float colsum = 0.f;
+                if (vis_b == nullptr) {
+                    // no mask: every row block runs (rows past R have zero q
+                    // and L2 = +inf, so they add nothing); the accumulators
+                    // start at -L2, so the scores leave the MFMAs as
+                    // exponents, and the hi and lo chains of the four row
+                    // blocks interleave
+                    f32x4 sc[kMassRowBlocks];
 #pragma unroll
-                for (int rb = 0; rb < kMassRowBlocks; ++rb) {
-                    if (r0 + rb * 16 >= R) break;          // (uniform: no selected pair left)
-                    f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+                    for (int rb = 0; rb < kMassRowBlocks; ++rb)
+                        sc[rb] = f32x4{-l2[rb][0], -l2[rb][1], -l2[rb][2], -l2[rb][3]};
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
-                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[rb][c], kf[u][c], sc, 0, 0, 0);
-                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[rb][c], kf[u][c], sc, 0, 0, 0);
+#pragma unroll
+                        for (int rb = 0; rb < kMassRowBlocks; ++rb)
+                            sc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[rb][c], kf[u][c], sc[rb], 0, 0, 0);
+#pragma unroll
+                        for (int rb = 0; rb < kMassRowBlocks; ++rb)
+                            sc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[rb][c], kf[u][c], sc[rb], 0, 0, 0);
                     }
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        bool keep = key < k1;
-                        if (gated) {
-                            const int sr = max(srow[rb][i], 0);
-                            keep = keep && ((sVis[sr * VW + (owner >> 5)] >> (owner & 31)) & 1u);
+                    for (int rb = 0; rb < kMassRowBlocks; ++rb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) colsum += __builtin_amdgcn_exp2f(sc[rb][i]);   // 2^-inf = 0
+                    colsum = key < k1 ? colsum : 0.f;
+                } else {
+                    // under a mask, row block by row block: a key written this
+                    // step is dropped for the rows that do not see its owner
+#pragma unroll
+                    for (int rb = 0; rb < kMassRowBlocks; ++rb) {
+                        if (r0 + rb * 16 >= R) break;          // (uniform: no selected pair left)
+                        f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[rb][c], kf[u][c], sc, 0, 0, 0);
+                            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[rb][c], kf[u][c], sc, 0, 0, 0);
                         }
-                        const float pv = __builtin_amdgcn_exp2f(sc[i] - l2[rb][i]);   // 2^-inf = 0
-                        colsum += keep ? pv : 0.f;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            bool keep = key < k1;
+                            if (gated) {
+                                const int sr = max(srow[rb][i], 0);
+                                keep = keep && ((sVis[sr * VW + (owner >> 5)] >> (owner & 31)) & 1u);
+                            }
+                            const float pv = __builtin_amdgcn_exp2f(sc[i] - l2[rb][i]);   // 2^-inf = 0
+                            colsum += keep ? pv : 0.f;
+                        }
                     }
                 }
                 colsum = sum4x(colsum);
