@@ -444,6 +444,34 @@ def run_stream(args):
                       "copy_GBps": round(copy_GBps, 1), "hbm_peak_GBps": HBM_PEAK_GBPS}))
 
 
+def run_probes(args):
+    """Device rates the step's kernels are bound by: streaming reads, the bf16
+    MFMA issue rate (four and eight waves per CU), and LDS-DMA loads from an
+    L2-resident 2 MB buffer with one to eight issuing waves per CU."""
+    import torch
+    from io_aware_kv_amd import binding
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    copy_GBps, read_GBps = device_rates(dev, stream)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    wgs, iters = 256, 8192
+    mfma = {}
+    for waves in (4, 8):
+        ms = time_launches(lambda _: binding.probe_mfma(sink, wgs, waves, iters, stream=stream), [None], stream, 5, 2)
+        mfma["waves%d" % waves] = round(wgs * waves * iters * 8 * 16384 / (ms * 1e-3) / 1e12, 1)
+    buf = torch.ones(2 << 20, dtype=torch.uint8, device=dev)
+    dma = {}
+    for waves in (1, 2, 4, 8):
+        ms = time_launches(lambda _: binding.probe_lds_dma(buf, sink, wgs, waves, iters, stream=stream), [None],
+                           stream, 5, 2)
+        gbps = wgs * waves * iters * 1024 / (ms * 1e-3) / 1e9
+        dma["waves%d" % waves] = {"GBps": round(gbps, 1), "per_cu_GBps": round(gbps / 256, 1)}
+    print(json.dumps({"mode": "probes", "read_GBps": round(read_GBps, 1), "copy_GBps": round(copy_GBps, 1),
+                      "mfma_bf16_TFLOPs": mfma, "mfma_bf16_peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                      "lds_dma_l2_resident": dma, "hbm_peak_GBps": HBM_PEAK_GBPS}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -459,7 +487,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--attn-splits", type=int, default=0)
     ap.add_argument("--gemm-splitk", type=int, default=0)
-    ap.add_argument("--mode", default="step", choices=["step", "copy", "stream"])
+    ap.add_argument("--mode", default="step", choices=["step", "copy", "stream", "probes"])
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     args = ap.parse_args()
 
@@ -473,6 +501,8 @@ def main():
         return run_copy(args)
     if args.mode == "stream":
         return run_stream(args)
+    if args.mode == "probes":
+        return run_probes(args)
 
     from io_aware_kv_amd.workloads import make_workload
 

@@ -78,6 +78,8 @@ def load():
     lib.fdllm_get_plan.argtypes = [P, i32, ctypes.POINTER(i32), ctypes.POINTER(i32), ctypes.POINTER(i32)]
     lib.fdllm_cache_destroy.argtypes = [P]
     lib.fdllm_probe_read.argtypes = [P, ctypes.c_int64, i32, P, P]
+    lib.fdllm_probe_mfma.argtypes = [i32, i32, i32, P, P]
+    lib.fdllm_probe_lds_dma.argtypes = [P, ctypes.c_int64, i32, i32, i32, P, P]
     lib.fdllm_fused_step_noalloc.argtypes = [ctypes.POINTER(Config), P, i32, P, P, i32, P, P, P, P, P, P, P]
     lib.fdllm_status_str.argtypes = [ctypes.c_int]
     lib.fdllm_status_str.restype = ctypes.c_char_p
@@ -155,6 +157,20 @@ def probe_read(buf: torch.Tensor, sink: torch.Tensor, workgroups: int = 0, strea
         raise ValueError("sink must hold 16 bytes")
     _check(load().fdllm_probe_read(_ptr(buf), buf.numel() * buf.element_size(), workgroups, _ptr(sink),
                                    _stream(stream)), "fdllm_probe_read")
+
+
+def probe_mfma(sink: torch.Tensor, workgroups: int = 0, waves: int = 4, iters: int = 4096, stream=None):
+    """Issue-rate probe of the bf16 MFMA (fdllm_probe.h); executed flops are
+    workgroups * waves * iters * 8 * 16384 (workgroups 0 means 256)."""
+    _check(load().fdllm_probe_mfma(workgroups, waves, iters, _ptr(sink), _stream(stream)), "fdllm_probe_mfma")
+
+
+def probe_lds_dma(buf: torch.Tensor, sink: torch.Tensor, workgroups: int = 0, waves: int = 4, iters: int = 4096,
+                  stream=None):
+    """LDS-DMA rate probe over buf (fdllm_probe.h); bytes moved are
+    workgroups * waves * iters * 1024 (workgroups 0 means 256)."""
+    _check(load().fdllm_probe_lds_dma(_ptr(buf), buf.numel() * buf.element_size(), workgroups, waves, iters,
+                                      _ptr(sink), _stream(stream)), "fdllm_probe_lds_dma")
 
 
 def fused_step_noalloc(X, Q_idx, pos_ids, vis, W, Kc, Vc, O, LSE, H, Hkv, rope_base=10000.0, q_max=None,

@@ -1,6 +1,8 @@
-// probe.hip -- streaming-read ceiling of the device: a plain read kernel over
-// a caller buffer, so that the attention phase's bandwidth can be set beside
-// what this GPU sustains for pure reads (no arithmetic of the step here).
+// probe.hip -- device ceilings the step's kernels are measured against: a
+// plain streaming read over a caller buffer (the attention phase's bandwidth
+// beside what this GPU sustains for pure reads), the issue rate of the bf16
+// matrix instruction, and the rate of LDS-DMA loads per issuing wave (no
+// arithmetic of the step here).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -10,6 +12,10 @@
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
 
 // Each workgroup reads one contiguous slice of the buffer (as the attention
 // streams one contiguous cache slice per workgroup), 16 B per lane, eight
@@ -32,7 +38,74 @@ __global__ void __launch_bounds__(256) probe_read_kernel(const u32x4* __restrict
     if (acc[0] == 0x9e3779b9u && acc[1] == 0x7f4a7c15u && acc[2] == 0x6a09e667u) sink[0] = acc;
 }
 
+// Eight independent accumulator chains per wave, so back-to-back MFMAs never
+// wait on one another; operands from registers (no memory in the loop).
+__global__ void __launch_bounds__(512) probe_mfma_kernel(int iters, u32x4* sink)
+{
+    bf16x8 a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(float)((threadIdx.x + i) & 7);
+        b[i] = (__bf16)(float)(i & 3);
+    }
+    f32x4 acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+    if (s == -1.0f) sink[0] = u32x4{1u, 2u, 3u, 4u};   // sums of non-negative products
+}
+
+// Each wave issues 1 KB LDS-DMA loads (64 lanes x 16 B) from consecutive
+// 1 KB blocks of the buffer, into its workgroup's 64 KB of LDS, keeping at
+// most 16 in flight.
+__global__ void __launch_bounds__(512) probe_lds_dma_kernel(const unsigned char* __restrict__ buf, size_t blocks,
+                                                            int iters, u32x4* sink)
+{
+    __shared__ __attribute__((aligned(16))) unsigned char lds[64 * 1024];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    size_t blk = ((size_t)blockIdx.x * nw + wave) % blocks;
+    for (int i = 0; i < iters; ++i) {
+        __builtin_amdgcn_global_load_lds((glb_void*)(buf + blk * 1024 + lane * 16),
+                                         (lds_void*)(lds + ((i * nw + wave) & 63) * 1024), 16, 0, 0);
+        if (i >= 16) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+        blk += nw;
+        if (blk >= blocks) blk -= blocks;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    const u32x4 v = *(const u32x4*)(lds + (threadIdx.x & 4095) * 16);
+    if (v[0] == 0x9e3779b9u && v[1] == 0x7f4a7c15u && v[2] == 0x6a09e667u && v[3] == 0x3c6ef372u) sink[0] = v;
+}
+
 }  // namespace
+
+extern "C" int fdllm_probe_mfma(int32_t workgroups, int32_t waves, int32_t iters, void* sink, void* stream)
+{
+    if (!sink || workgroups < 0 || waves < 1 || waves > 8 || iters < 1) return FDLLM_ERR_ARG;
+    if (reinterpret_cast<uintptr_t>(sink) & 15u) return FDLLM_ERR_ALIGN;
+    const int grid = workgroups > 0 ? workgroups : 256;
+    hipLaunchKernelGGL(probe_mfma_kernel, dim3(grid), dim3(waves * 64), 0, (hipStream_t)stream, iters, (u32x4*)sink);
+    return hipGetLastError() == hipSuccess ? FDLLM_OK : FDLLM_ERR_HIP;
+}
+
+extern "C" int fdllm_probe_lds_dma(const void* buf, int64_t bytes, int32_t workgroups, int32_t waves, int32_t iters,
+                                   void* sink, void* stream)
+{
+    if (!buf || !sink || bytes < 1024 || (bytes % 1024) || workgroups < 0 || waves < 1 || waves > 8 || iters < 1)
+        return FDLLM_ERR_ARG;
+    if ((reinterpret_cast<uintptr_t>(buf) & 15u) || (reinterpret_cast<uintptr_t>(sink) & 15u))
+        return FDLLM_ERR_ALIGN;
+    const int grid = workgroups > 0 ? workgroups : 256;
+    hipLaunchKernelGGL(probe_lds_dma_kernel, dim3(grid), dim3(waves * 64), 0, (hipStream_t)stream,
+                       (const unsigned char*)buf, (size_t)bytes / 1024, iters, (u32x4*)sink);
+    return hipGetLastError() == hipSuccess ? FDLLM_OK : FDLLM_ERR_HIP;
+}
 
 extern "C" int fdllm_probe_read(const void* buf, int64_t bytes, int32_t workgroups, void* sink, void* stream)
 {

@@ -89,6 +89,22 @@ def test_read_probe_argument_errors_are_host_side(lib):
     assert lib.fdllm_probe_read(P(24), 1024, 0, P(16), None) == -3    # misaligned buffer
 
 
+def test_rate_probe_argument_errors_are_host_side(lib):
+    P = ctypes.c_void_p
+    assert lib.fdllm_probe_mfma(0, 4, 16, None, None) == -1
+    assert lib.fdllm_probe_mfma(-1, 4, 16, P(16), None) == -1
+    assert lib.fdllm_probe_mfma(0, 0, 16, P(16), None) == -1         # no wave
+    assert lib.fdllm_probe_mfma(0, 9, 16, P(16), None) == -1         # more than eight waves
+    assert lib.fdllm_probe_mfma(0, 4, 0, P(16), None) == -1
+    assert lib.fdllm_probe_mfma(0, 4, 16, P(24), None) == -3         # misaligned sink
+    assert lib.fdllm_probe_lds_dma(None, 1024, 0, 4, 16, P(16), None) == -1
+    assert lib.fdllm_probe_lds_dma(P(16), 1000, 0, 4, 16, P(16), None) == -1   # not whole 1 KB blocks
+    assert lib.fdllm_probe_lds_dma(P(16), 512, 0, 4, 16, P(16), None) == -1
+    assert lib.fdllm_probe_lds_dma(P(16), 1024, 0, 9, 16, P(16), None) == -1
+    assert lib.fdllm_probe_lds_dma(P(16), 1024, 0, 4, 0, P(16), None) == -1
+    assert lib.fdllm_probe_lds_dma(P(24), 1024, 0, 4, 16, P(16), None) == -3
+
+
 def test_noalloc_step_host_side_errors(lib):
     """The allocation-free step validates its arguments and sizes its
     workspace against the static scratch before any HIP call."""
