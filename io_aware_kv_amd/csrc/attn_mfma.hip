@@ -17,12 +17,16 @@
 //    at most 48 of its loads (48 KB) in flight; a producer waits on its own
 //    vmcnt and releases each stage with a barrier.  The consumer waves never
 //    issue global loads in the loop, they only read LDS and run MFMAs;
-//  * LDS rows are 256 B with their 16 B chunks XOR-swizzled by the row index,
-//    which makes both fragment read patterns below bank-conflict free;
+//  * LDS rows are 256 B with their 16 B chunks XOR-swizzled by the row index:
+//    the K fragment reads are conflict-free; the transposed V reads are not
+//    entirely (the bank-conflict counter reads about a third of the
+//    LDS-active cycles on the long-context layer; a swizzle aimed at them
+//    doubled it);
 //  * S^T = K Q^T on v_mfma_f32_16x16x32_bf16 leaves each lane with one query
 //    row, so the row max needs two cross-lane steps and the rescale of the
 //    output accumulators is lane-local; q enters as bf16 hi + lo parts so the
-//    scores keep q's fp32 accumulation precision;
+//    scores keep q's fp32 accumulation precision, and the accumulators start
+//    at the row's -reference max, so the exponentials need no subtraction;
 //  * O^T += V^T P^T takes V^T fragments from the row-major tile with
 //    ds_read_b64_tr_b16 (gfx950 transpose read) and P^T from the score
 //    registers, so P never goes through LDS;
