@@ -314,10 +314,33 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
                 }
             }
         } else {
-            for (int e = tid; e < BM * V4; e += C::NT) {
-                const int row = e / V4, v = e - row * V4;
-                *(f32x4*)&sCS[row * PC + 2 * v] =
-                    *(const f32x4*)&a.rope[(size_t)sPos[row] * (kDH / 2) + p0 * 16 + 2 * v];
+            // all of a thread's table loads in flight before the first store
+            // (one memory round trip, not one per load), where the registers
+            // allow it beside the accumulators
+            constexpr int PER = (BM * V4 + C::NT - 1) / C::NT;
+            constexpr bool BATCH = 4 * C::RBW * 2 * C::PPW + 4 * PER <= 160;
+            if constexpr (BATCH) {
+                f32x4 cs[PER];
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const int e = min(tid + i * C::NT, BM * V4 - 1);
+                    const int row = e / V4, v = e - row * V4;
+                    cs[i] = *(const f32x4*)&a.rope[(size_t)sPos[row] * (kDH / 2) + p0 * 16 + 2 * v];
+                }
+#pragma unroll
+                for (int i = 0; i < PER; ++i) {
+                    const int e = tid + i * C::NT;
+                    if (e < BM * V4) {
+                        const int row = e / V4, v = e - row * V4;
+                        *(f32x4*)&sCS[row * PC + 2 * v] = cs[i];
+                    }
+                }
+            } else {
+                for (int e = tid; e < BM * V4; e += C::NT) {
+                    const int row = e / V4, v = e - row * V4;
+                    *(f32x4*)&sCS[row * PC + 2 * v] =
+                        *(const f32x4*)&a.rope[(size_t)sPos[row] * (kDH / 2) + p0 * 16 + 2 * v];
+                }
             }
         }
         __syncthreads();
