@@ -333,6 +333,44 @@ def time_launches(fn, sets, stream, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def time_graph_steps(fk, sets, steps, warmup):
+    """The step (projection + attention) captured once per buffer set into a
+    HIP graph and replayed back to back over the sets: the device time per
+    step without the host's launch calls between the kernels.  The library
+    issues no memset and allocates nothing inside a step, so each graph holds
+    only the step's kernel nodes."""
+    import torch
+    cs = torch.cuda.Stream()
+    cs.wait_stream(torch.cuda.current_stream())
+
+    def step(st):
+        fk.project(st["X"], st["Q"], st["P"], st["W"], st["Kc"], st["Vc"], stream=cs)
+        fk.attend(st["P"], st["vis"], st["Kc"], st["Vc"], st["O"], st["LSE"], stream=cs)
+
+    with torch.cuda.stream(cs):
+        for st in sets:
+            step(st)
+    torch.cuda.synchronize()
+    graphs = []
+    for st in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cs):
+            step(st)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(cs):
+        for i in range(warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cs)
+        for i in range(steps):
+            graphs[i % len(graphs)].replay()
+        e1.record(cs)
+        torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def phase_fraction(nbytes, flops, us):
     """Roofline fraction of a phase: against HBM bytes, or against bf16 MFMA
     flops when those take the longer at peak."""
@@ -395,12 +433,14 @@ def measure_config(cid, steps, warmup, dev, read_GBps=None):
     step_ms = time_launches(step, sets, stream, steps, warmup)
     proj_ms = time_launches(proj, sets, stream, steps, warmup)
     attn_ms = time_launches(attn, sets, stream, steps, warmup)
+    graph_ms = time_graph_steps(fk, sets, steps, warmup)
     plan = fk.plan(wl.nq)
     fk.close()
     del sets
     attn_GBps = ab["attn"] / (attn_ms * 1e-3) / 1e9
     out = {"workload": wl.name, "plan": plan, "buffer_sets": n_sets,
-           "step_us": round(step_ms * 1e3, 3), "proj_us": round(proj_ms * 1e3, 3), "attn_us": round(attn_ms * 1e3, 3),
+           "step_us": round(step_ms * 1e3, 3), "graph_step_us": round(graph_ms * 1e3, 3),
+           "proj_us": round(proj_ms * 1e3, 3), "attn_us": round(attn_ms * 1e3, 3),
            "proj_bytes": ab["proj"], "proj_flops": ab["qkv_flops"],
            "proj_roofline": phase_fraction(ab["proj"], ab["qkv_flops"], proj_ms * 1e3),
            "attn_bytes": ab["attn"], "attn_flops": ab["attn_flops"],
@@ -588,6 +628,9 @@ def main():
 
     # warm-cache reference: the same set every step (Infinity Cache may hold it)
     warm_ms = time_launches(lambda st: step(st), [sets[0]], stream, min(args.steps, 50), 0)
+    # the same step replayed from HIP graphs (no host launch calls between kernels)
+    graph_ms = time_graph_steps(fk, sets, args.steps, 5)
+    log("bench: graph-replayed step %.2f us" % (graph_ms * 1e3))
 
     # the step after the path: tracked-set scores and top-k (not part of value)
     selection = None
@@ -649,6 +692,7 @@ def main():
         "latency_us": round(ms_per_step * 1e3, 3),
         "queries_per_s": round(ls.B * wl.nq / (ms_per_step * 1e-3), 1),
         "warm_cache_latency_us": round(warm_ms * 1e3, 3),
+        "graph_step_us": round(graph_ms * 1e3, 3),
         "host_submit_us_per_step": round(host_submit_us, 2),
         "phases": {
             # each launch kind alone, back to back
@@ -685,8 +729,8 @@ def main():
         log("bench: workload %d" % c)
         others["workload%d" % c] = measure_config(c, min(args.steps, 100), 10, dev, read_GBps)
         o = others["workload%d" % c]
-        log("bench: workload %d: step %.2f us, proj %.2f us, attn %.2f us (%.0f GB/s, %.3f of 8 TB/s)" %
-            (c, o["step_us"], o["proj_us"], o["attn_us"], o["attn_GBps"], o["attn_hbm_frac"]))
+        log("bench: workload %d: step %.2f us (graph %.2f us), proj %.2f us, attn %.2f us (%.0f GB/s, %.3f of 8 TB/s)" %
+            (c, o["step_us"], o["graph_step_us"], o["proj_us"], o["attn_us"], o["attn_GBps"], o["attn_hbm_frac"]))
     result["configs"] = others
 
     if not args.no_cpu:

@@ -78,9 +78,11 @@ def test_bench_json_line_on_the_gpu():
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
     assert d["device_read_GBps"] > 0 and d["device_copy_GBps"] > 0
     assert d["host_submit_us_per_step"] > 0
+    assert d["graph_step_us"] > 0
     # the other workloads of the target set: step and phase figures of each
     assert set(d["configs"]) == {"workload1", "workload2", "workload4"}
     for c in d["configs"].values():
-        for key in ("workload", "step_us", "proj_us", "attn_us", "attn_hbm_frac", "proj_roofline", "plan"):
+        for key in ("workload", "step_us", "graph_step_us", "proj_us", "attn_us", "attn_hbm_frac", "proj_roofline",
+                    "plan"):
             assert key in c, key
         assert c["step_us"] > 0 and 0 < c["attn_hbm_frac"] < 1
