@@ -121,6 +121,14 @@ SMALL = [
     # a 64-wide head in bf16: the scalar kernels (the MFMA ones take 128)
     ("bf16-dh64", dict(B=2, N=120, d_model=128, H=4, Hkv=2, dh=64), 9,
      dict(n_extra_rows=3, dup_frac=0.2, masked_vis=True)),
+    # head widths that are not a multiple of 16 or reach the scalar kernels'
+    # limit: lanes past dh run on a clamped dim and are never stored
+    ("fp32-dh24", dict(B=1, N=70, d_model=64, H=2, Hkv=1, dh=24, dtype=torch.float32), 6,
+     dict(n_extra_rows=2, dup_frac=0.2, masked_vis=True)),
+    ("bf16-dh8", dict(B=1, N=40, d_model=32, H=2, Hkv=2, dh=8), 4, dict()),
+    ("bf16-dh48", dict(B=2, N=100, d_model=96, H=4, Hkv=2, dh=48), 8,
+     dict(n_extra_rows=2, dup_frac=0.2, masked_vis=True)),
+    ("bf16-dh256", dict(B=1, N=80, d_model=256, H=2, Hkv=1, dh=256), 5, dict(n_extra_rows=1)),
 ]
 
 
