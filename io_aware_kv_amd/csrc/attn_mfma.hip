@@ -903,7 +903,12 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s)
         return launch_cfg<1, 4, 2, 2>(a, s);
     }
     if (r16 <= 6) return launch_cfg<2, 3, 2, 2>(a, s);
-    if (r16 <= 10) return launch_cfg<2, 5, 1, 2>(a, s);
+    // 9 to 11 row groups: one row group per wave, two or three waves on each
+    // SIMD (with two row groups a wave, the busiest SIMD carried four: 2-7 %
+    // slower on the default-window workloads)
+    if (r16 <= 9) return launch_cfg<1, 9, 1, 2>(a, s);
+    if (r16 <= 10) return launch_cfg<1, 10, 1, 2>(a, s);
+    if (r16 <= 11) return launch_cfg<1, 11, 1, 1>(a, s);
     if (r16 <= 14) return launch_cfg<2, 7, 1, 1>(a, s);
     if (r16 <= 18) return launch_cfg<3, 6, 1, 1>(a, s);
     return hipErrorInvalidValue;
