@@ -341,15 +341,28 @@ attn_mfma_kernel(AttnArgs a)
                 if (64 * c >= nq) break;
                 const int j = 64 * c + lane;
                 if (j >= nqb) posr[c] = -1;  // padding lanes and rows (their load repeated the last row)
-                bool own = true;
+                // lanes whose position an earlier row holds, as a wave-wide
+                // mask: each earlier position is broadcast and compared with
+                // every lane at once (no per-lane branches)
+                const int my = posr[c];
+                uint64_t dupm = 0;
 #pragma unroll
-                for (int cq = 0; cq <= c; ++cq) {
-                    const int lim = min(64, nq - 64 * cq);
-                    for (int t = 0; t < lim; ++t) {
-                        const int pq = __builtin_amdgcn_readlane(posr[cq], t);
-                        own = own && !(pq == posr[c] && 64 * cq + t < j);
+                for (int cq = 0; cq < c; ++cq)       // an earlier chunk: all 64 rows precede this one
+#pragma unroll 1
+                    for (int t = 0; t < 64; t += 4) {
+                        const int p0 = __builtin_amdgcn_readlane(posr[cq], t);
+                        const int p1 = __builtin_amdgcn_readlane(posr[cq], t + 1);
+                        const int p2 = __builtin_amdgcn_readlane(posr[cq], t + 2);
+                        const int p3 = __builtin_amdgcn_readlane(posr[cq], t + 3);
+                        dupm |= __builtin_amdgcn_ballot_w64(my == p0) | __builtin_amdgcn_ballot_w64(my == p1) |
+                                __builtin_amdgcn_ballot_w64(my == p2) | __builtin_amdgcn_ballot_w64(my == p3);
                     }
+                const int lim = min(64, nq - 64 * c);
+                for (int t = 0; t < lim; ++t) {        // this chunk: row t precedes lanes t+1..63
+                    const int pq = __builtin_amdgcn_readlane(my, t);
+                    dupm |= __builtin_amdgcn_ballot_w64(my == pq) & (~1ull << t);
                 }
+                const bool own = ((dupm >> lane) & 1ull) == 0;
                 const bool valid = j < nqb;
                 const uint64_t dm = __builtin_amdgcn_ballot_w64(valid && !own);
                 const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(dm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)dm, 0u));
