@@ -139,7 +139,8 @@ int fdllm_prefill(fdllm_handle_t h, const void* X, int32_t x_rows, const void* W
  * cache under vis_mask -> O [B, nq, H, dh] (dtype) and LSE [B, nq, H] (fp32,
  * natural log).  Arguments and layouts as in the conventions above; every
  * pointer is a caller-owned device buffer; the handle's workspace holds the
- * step's q rows and duplicate-position k/v rows until the step ends.
+ * step's q rows, duplicate-position k/v rows and ownership flags until the
+ * step ends.
  * 0 <= nq <= q_max; nq == 0 launches nothing.  Asynchronous on stream.
  * Statuses: ARG, SHAPE, ALIGN, INDEX (FDLLM_VALIDATE=1 only), HIP. */
 int fdllm_fused_step(fdllm_handle_t h, const void* X, int32_t x_rows, const int32_t* Q_idx,
@@ -149,7 +150,8 @@ int fdllm_fused_step(fdllm_handle_t h, const void* X, int32_t x_rows, const int3
 /* The two launches of fdllm_fused_step, callable separately (same arguments
  * and statuses; used to time the phases or to run work between them).
  * fdllm_step_project runs gather + projection + rotary + k/v write and leaves
- * the step's fp32 q rows and duplicate-position k/v rows in the handle's
+ * the step's fp32 q rows, duplicate-position k/v rows and the rows' ownership
+ * flags (which row stored each position in the cache) in the handle's
  * workspace; fdllm_step_attend consumes them (it must follow the project call
  * of the same step on the same stream, with the same nq and pos_ids). */
 int fdllm_step_project(fdllm_handle_t h, const void* X, int32_t x_rows, const int32_t* Q_idx,

@@ -42,6 +42,8 @@
 // position written by its first row j is reached through the cache (the
 // projection kernel stored it there) and gated by vis[i][j]; later rows at a
 // shared position live in the side buffer and are attended as extra tiles.
+// Which rows own their position is read from the flags the projection
+// recorded while deciding where to store each row.
 #include "fdllm_common.h"
 
 namespace fdllm {
@@ -247,7 +249,7 @@ attn_mfma_kernel(AttnArgs a)
     // ---- every global load of the consumers is issued before the producers
     //      start streaming, so none of them waits behind the K/V tiles
     f32x4 qraw[RG][8];
-    int posr[kMaxChunks];
+    int posr[kMaxChunks], ownr[kMaxChunks];
     int vbyte[8];
     if (!producer) {
         const float* qbase = a.qbuf + (size_t)bg * a.q_max * G * kDH;
@@ -261,9 +263,13 @@ attn_mfma_kernel(AttnArgs a)
                 qraw[rg][h] = *(const f32x4*)(qbase + (size_t)row * kDH + (h >> 1) * 32 + lg * 8 + (h & 1) * 4);
         }
         if (wave == 0) {
+            const int8_t* own_b = a.own + (size_t)b * nq;
 #pragma unroll
             for (int c = 0; c < kMaxChunks; ++c)
-                if (64 * c < nq) posr[c] = pos_b[min(64 * c + lane, nq - 1)];
+                if (64 * c < nq) {
+                    posr[c] = pos_b[min(64 * c + lane, nq - 1)];
+                    ownr[c] = own_b[min(64 * c + lane, nq - 1)];
+                }
         }
         // a few mask rows: their bytes, one per lane (under a mask these are
         // read before the stream starts: issued after it they would queue
@@ -334,35 +340,14 @@ attn_mfma_kernel(AttnArgs a)
         // per-sequence bookkeeping while the first tiles stream in
         if (wave == 0) {
             // row j owns the cache write of its position unless an earlier
-            // row has the same position; the others are listed in sDup
+            // row has the same position (the projection recorded which rows
+            // do); the others are listed in sDup
             int ndup = 0;
 #pragma unroll
             for (int c = 0; c < kMaxChunks; ++c) {
                 if (64 * c >= nq) break;
                 const int j = 64 * c + lane;
-                if (j >= nqb) posr[c] = -1;  // padding lanes and rows (their load repeated the last row)
-                // lanes whose position an earlier row holds, as a wave-wide
-                // mask: each earlier position is broadcast and compared with
-                // every lane at once (no per-lane branches)
-                const int my = posr[c];
-                uint64_t dupm = 0;
-#pragma unroll
-                for (int cq = 0; cq < c; ++cq)       // an earlier chunk: all 64 rows precede this one
-#pragma unroll 1
-                    for (int t = 0; t < 64; t += 4) {
-                        const int p0 = __builtin_amdgcn_readlane(posr[cq], t);
-                        const int p1 = __builtin_amdgcn_readlane(posr[cq], t + 1);
-                        const int p2 = __builtin_amdgcn_readlane(posr[cq], t + 2);
-                        const int p3 = __builtin_amdgcn_readlane(posr[cq], t + 3);
-                        dupm |= __builtin_amdgcn_ballot_w64(my == p0) | __builtin_amdgcn_ballot_w64(my == p1) |
-                                __builtin_amdgcn_ballot_w64(my == p2) | __builtin_amdgcn_ballot_w64(my == p3);
-                    }
-                const int lim = min(64, nq - 64 * c);
-                for (int t = 0; t < lim; ++t) {        // this chunk: row t precedes lanes t+1..63
-                    const int pq = __builtin_amdgcn_readlane(my, t);
-                    dupm |= __builtin_amdgcn_ballot_w64(my == pq) & (~1ull << t);
-                }
-                const bool own = ((dupm >> lane) & 1ull) == 0;
+                const bool own = ownr[c] > 0;
                 const bool valid = j < nqb;
                 const uint64_t dm = __builtin_amdgcn_ballot_w64(valid && !own);
                 const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(dm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)dm, 0u));
@@ -903,6 +888,7 @@ int attn_mfma_tile_keys(int R)
 hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s)
 {
     if (a.B * a.Hkv * a.splits == 0 || a.R == 0) return hipSuccess;
+    if (!a.own) return hipErrorInvalidValue;   // the projection's ownership flags are required
     // row groups of 16 per wave x row waves x key waves x producer waves; at
     // most two waves per SIMD once a wave holds two or more row groups
     const int r16 = (a.R + 15) / 16;

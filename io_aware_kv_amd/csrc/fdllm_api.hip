@@ -23,6 +23,7 @@ struct fdllm_ctx {
     float* qbuf = nullptr;
     void* sideK = nullptr;
     void* sideV = nullptr;
+    int8_t* own = nullptr;        // [B, q_max] ownership flags of the step's rows
     bf16* apart = nullptr;
     float* aml = nullptr;
     size_t apart_rows = 0;        // (B*Hkv) * splits * Rpad rows available
@@ -99,10 +100,10 @@ int hip_status(hipError_t e)
 
 void free_ws(fdllm_ctx* h)
 {
-    void* ptrs[] = {h->rope, h->qbuf, h->sideK, h->sideV, h->apart, h->aml, h->mpart};
+    void* ptrs[] = {h->rope, h->qbuf, h->sideK, h->sideV, h->own, h->apart, h->aml, h->mpart};
     for (void* p : ptrs)
         if (p) (void)hipFree(p);
-    h->rope = nullptr; h->qbuf = nullptr; h->sideK = h->sideV = nullptr;
+    h->rope = nullptr; h->qbuf = nullptr; h->sideK = h->sideV = nullptr; h->own = nullptr;
     h->apart = nullptr;
     h->aml = nullptr;
     h->mpart = nullptr;
@@ -147,7 +148,7 @@ ProjArgs proj_args(const fdllm_ctx* h, const void* X, int x_rows, const int32_t*
     const fdllm_config_t& c = h->cfg;
     ProjArgs a{};
     a.X = X; a.W = W; a.Q_idx = Q_idx; a.pos_ids = pos; a.rope = h->rope;
-    a.Kc = Kc; a.Vc = Vc; a.qbuf = h->qbuf; a.sideK = h->sideK; a.sideV = h->sideV;
+    a.Kc = Kc; a.Vc = Vc; a.qbuf = h->qbuf; a.sideK = h->sideK; a.sideV = h->sideV; a.own = h->own;
     a.B = c.B; a.N = c.N; a.d = c.d_model; a.H = c.H; a.Hkv = c.Hkv; a.dh = c.dh; a.G = h->G;
     a.x_rows = x_rows; a.rows_per_seq = rows_per_seq; a.q_max = c.q_max;
     a.prefill = prefill;
@@ -223,6 +224,7 @@ int attend_impl(fdllm_ctx* h, const int32_t* pos_ids, int32_t nq, const uint8_t*
     aa.map = map;
     aa.seq_len = seq_len;
     aa.nq_seq = nq_seq;
+    aa.own = h->own;
     hipError_t e = p.attn_family == FAMILY_MFMA ? launch_attn_mfma(aa, s) : launch_attn_generic(aa, c.dtype, s);
     return hip_status(e);
 }
@@ -303,6 +305,7 @@ int fdllm_cache_init(fdllm_handle_t* out, const fdllm_config_t* cfg, const void*
               hipMalloc(&h->qbuf, qrows * c.dh * sizeof(float)) == hipSuccess &&
               hipMalloc(&h->sideK, srows * c.dh * h->elt) == hipSuccess &&
               hipMalloc(&h->sideV, srows * c.dh * h->elt) == hipSuccess &&
+              hipMalloc(&h->own, (size_t)c.B * c.q_max) == hipSuccess &&
               hipMalloc(&h->mpart, (size_t)c.B * c.Hkv * c.N * sizeof(float)) == hipSuccess;
     if (!ok) { free_ws(h); delete h; return FDLLM_ERR_ALLOC; }
     st = ensure_split_ws(h);

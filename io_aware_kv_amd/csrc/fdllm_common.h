@@ -54,6 +54,8 @@ struct ProjArgs {
     int tile_choice;        // 0: default tile configuration for the row count
     CacheMap map;           // cache layout (flat when map.table is NULL)
     const int32_t* nq_seq;  // [B] query rows of each sequence (rows j >= nq_seq[b] are padding) or NULL
+    int8_t* own;            // [B, rows_per_seq] per row: 1 owns the cache write of its position, 0 an
+                            // earlier row does, < 0 padding (not in prefill mode); NULL: not recorded
 };
 
 struct AttnArgs {
@@ -77,6 +79,7 @@ struct AttnArgs {
     CacheMap map;           // cache layout (flat when map.table is NULL)
     const int32_t* seq_len; // [B] valid cache positions of each sequence (>= 1) or NULL (all N)
     const int32_t* nq_seq;  // [B] query rows of each sequence or NULL (all nq)
+    const int8_t* own;      // [B, nq] the step's ownership flags, as the projection recorded them
 };
 
 // Tracked-set scores after a step: attention mass of the selected query rows

@@ -55,7 +55,7 @@ __global__ void __launch_bounds__(64) rope_rows_kernel(const int32_t* pos, int N
 }
 
 struct Layout {
-    size_t rope, qbuf, sideK, sideV, apart, aml, total;
+    size_t rope, qbuf, sideK, sideV, own, apart, aml, total;
 };
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -72,6 +72,7 @@ Layout layout(const fdllm_config_t& c, int nq, const Plan& p)
     l.qbuf = at;  at += up256((size_t)c.B * c.Hkv * nq * G * c.dh * sizeof(float));
     l.sideK = at; at += up256((size_t)c.B * c.Hkv * nq * c.dh * elt);
     l.sideV = at; at += up256((size_t)c.B * c.Hkv * nq * c.dh * elt);
+    l.own = at;   at += up256((size_t)c.B * nq);
     const size_t arows = (p.attn_family == FAMILY_MFMA && p.splits > 1) ? (size_t)c.B * c.Hkv * p.splits * p.Rpad : 0;
     l.apart = at; at += up256(arows * c.dh * sizeof(bf16));
     l.aml = at;   at += up256(arows * 2 * sizeof(float));
@@ -129,6 +130,7 @@ extern "C" int fdllm_fused_step_noalloc(const fdllm_config_t* cfg, const void* X
     pa.prefill = 0; pa.tile_choice = 0;
     pa.map = CacheMap{nullptr, 0, 0};
     pa.nq_seq = nullptr;
+    pa.own = (int8_t*)(base + lay.own);
     hipError_t e = p.proj_family == FAMILY_MFMA ? launch_proj_mfma(pa, s) : launch_proj_generic(pa, c.dtype, s);
     if (e != hipSuccess) return FDLLM_ERR_HIP;
 
@@ -142,6 +144,7 @@ extern "C" int fdllm_fused_step_noalloc(const fdllm_config_t* cfg, const void* X
     aa.map = CacheMap{nullptr, 0, 0};
     aa.seq_len = nullptr;
     aa.nq_seq = nullptr;
+    aa.own = pa.own;
     e = p.attn_family == FAMILY_MFMA ? launch_attn_mfma(aa, s) : launch_attn_generic(aa, c.dtype, s);
     return e == hipSuccess ? FDLLM_OK : FDLLM_ERR_HIP;
 }

@@ -411,6 +411,12 @@ proj_mfma_kernel(ProjArgs a, int m_tiles, int n_tiles)
             }
     }
     __syncthreads();
+    // one column tile of the first k head records the rows' ownership for
+    // the attention launch (which would otherwise settle it again in every
+    // (sequence, kv head) workgroup)
+    if (a.own && !a.prefill && head == a.H && p0 == 0)
+        for (int r = tid; r < BM; r += C::NT)
+            if (m0 + r < M) a.own[m0 + r] = (int8_t)sDst[r];
     const bool isk = head < a.H + a.Hkv;
     const int g = head - a.H - (isk ? 0 : a.Hkv);
     constexpr int CPR = BN / 8;
