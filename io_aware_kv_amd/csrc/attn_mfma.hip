@@ -208,6 +208,14 @@ attn_mfma_kernel(AttnArgs a)
     int* sDup = (int*)(sVis + (size_t)nq * VW);     // [nq] rows that do not own their position
     int* sMisc = sDup + nq;                         // [0] number of such rows
     int* sTabLds = sMisc + 1;                       // [max_blocks] block table of the sequence (paged)
+    // under a mask, when they fit: per query row and 32-key word of the split,
+    // the written keys the row may not see (hidden); per owner row, its
+    // key's offset in the split; per 32 rows, the rows that own a key of it
+    const int TWS = kps >> 5;
+    uint32_t* sHid = (uint32_t*)(sTabLds + (a.map.table != nullptr ? a.map.max_blocks : 0));   // [nq][TWS]
+    int* sKt = (int*)(sHid + (size_t)nq * TWS);     // [32 VW]
+    uint32_t* sOwnIn = (uint32_t*)(sKt + 32 * VW);  // [VW]
+    const bool hid = a.hid_words != 0;
 
     const int total = a.B * a.Hkv * a.splits;
     const int logical = xcd_remap(blockIdx.x, total);
@@ -286,6 +294,10 @@ attn_mfma_kernel(AttnArgs a)
             for (int k = tid; k < kps; k += C::NC * 64) sSlot[k] = -1;
             for (int t = tid; t < 2 * n_main; t += C::NC * 64) sMask[t] = 0u;
         }
+        if (hid) {
+            for (int t = tid; t < nq * TWS; t += C::NC * 64) sHid[t] = 0u;
+            for (int t = tid; t < VW; t += C::NC * 64) sOwnIn[t] = 0u;
+        }
         if (paged) {
             const int32_t* tb = a.map.table + (size_t)b * a.map.max_blocks;
             for (int t = tid; t < a.map.max_blocks; t += C::NC * 64) sTabLds[t] = tb[t];
@@ -318,6 +330,9 @@ attn_mfma_kernel(AttnArgs a)
                                              lane, sTab, a.map.bits, a.Hkv, g);
         int ntot = n_main;
         int ndup = 0;
+        // the consumers' extra barrier between their bookkeeping and the
+        // hidden-key words (the stages stay in flight)
+        if (hid) asm volatile("s_barrier" ::: "memory");
         for (int t = 0;; ++t) {
             producer_sync<C::DMAP, C::AHEAD - 1>(issued - t - 1);
             if (t == 0 && split == 0) {
@@ -353,12 +368,18 @@ attn_mfma_kernel(AttnArgs a)
                 const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(dm >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)dm, 0u));
                 if (valid && !own) sDup[ndup + below] = j;
                 ndup += __builtin_popcountll(dm);
-                if (vis_b && valid && own) {
-                    const int pp = posr[c];
-                    if (pp >= k0 && pp < k1) {
-                        const int kt = pp - k0;
-                        sSlot[kt] = (int16_t)j;
-                        atomicOr(&sMask[2 * (kt / C::TK) + ((kt % C::TK) >> 5)], 1u << (kt & 31));
+                const bool inr = vis_b && valid && own && posr[c] >= k0 && posr[c] < k1;
+                if (inr) {
+                    const int kt = posr[c] - k0;
+                    sSlot[kt] = (int16_t)j;
+                    atomicOr(&sMask[2 * (kt / C::TK) + ((kt % C::TK) >> 5)], 1u << (kt & 31));
+                    if (hid) sKt[j] = kt;
+                }
+                if (hid) {
+                    const uint64_t om = __builtin_amdgcn_ballot_w64(inr);
+                    if (lane == 0) {
+                        sOwnIn[2 * c] = (uint32_t)om;
+                        if (2 * c + 1 < VW) sOwnIn[2 * c + 1] = (uint32_t)(om >> 32);
                     }
                 }
             }
@@ -454,6 +475,31 @@ attn_mfma_kernel(AttnArgs a)
                 }
         }
 
+        // hidden-key words: pair (64-row chunk, 32-owner word) per wave
+        // iteration, a lane per query row; each owner of a key in the split
+        // that the row may not see sets the key's bit in the row's word.
+        // Wave 0 comes to the barrier last (it did the owner bookkeeping), so
+        // the pairs are dealt from the last wave down.
+        if (hid) {
+            consumer_sync();   // owner bookkeeping and visibility words are in LDS
+            const int npairs = ((nq + 63) >> 6) * VW;
+            for (int pr = C::NC - 1 - wave; pr < npairs; pr += C::NC) {
+                const int rc = pr / VW, ow = pr - rc * VW;
+                uint32_t om = __builtin_amdgcn_readfirstlane(sOwnIn[ow]);
+                const int jrow = 64 * rc + lane;
+                const int ktv = sKt[32 * ow + (lane & 31)];   // lane k < 32: owner 32 ow + k
+                const uint32_t seen = jrow < nq ? sVis[jrow * VW + ow] : ~0u;
+                const uint32_t hm = om & ~seen;
+                if (__builtin_amdgcn_ballot_w64(hm != 0u) == 0) continue;   // every row sees these owners
+                while (om != 0u) {
+                    const int k = __builtin_ctz(om);
+                    om &= om - 1u;
+                    const int kt = __builtin_amdgcn_readlane(ktv, k);
+                    if ((hm >> k) & 1u) atomicOr(&sHid[jrow * TWS + (kt >> 5)], 1u << (kt & 31));
+                }
+            }
+        }
+
         // per-lane LDS offsets of the fragments within a stage
         int kofs[4], vofs[8];
 #pragma unroll
@@ -478,6 +524,15 @@ attn_mfma_kernel(AttnArgs a)
                     ntot = n_main + (ndup + C::TK - 1) / C::TK;
                 }
                 const unsigned char* st = smem + s * C::STAGE;
+                // this lane's hidden-key bits of the wave's 32 keys (rows past
+                // the live ones hide every written key), read ahead of the MFMAs
+                uint32_t hw[RG];
+                if (hid) {
+                    const int itc = min(it, n_main - 1);
+#pragma unroll
+                    for (int rg = 0; rg < RG; ++rg)
+                        hw[rg] = qrow[rg] >= 0 ? sHid[qrow[rg] * TWS + itc * NWK + wk] : sMask[2 * itc + wk];
+                }
 
                 // ---- S^T = K Q^T for this wave's 32 keys (rows past R run on zero q)
                 constexpr int KB = C::KW / 16;                 // 16-key blocks per wave
@@ -543,7 +598,7 @@ attn_mfma_kernel(AttnArgs a)
                 // this wave's 32 bits of the tile's written-key mask; with
                 // more than a few written keys the per-lane general path is
                 // cheaper than visiting them one at a time
-                uint32_t wm = vis_b && !dup ? __builtin_amdgcn_readfirstlane(sMask[2 * it + wk]) : 0u;
+                uint32_t wm = vis_b && !dup && !hid ? __builtin_amdgcn_readfirstlane(sMask[2 * it + wk]) : 0u;
                 if (dup || tbase + C::TK > kend || __builtin_popcount(wm) > 2) {
                     // branch-free: every lane reads its keys' owners and its
                     // rows' visibility words at clamped (valid) indices
@@ -583,6 +638,14 @@ attn_mfma_kernel(AttnArgs a)
                                     sc[rg][kb][i] = key < kend ? sc[rg][kb][i] : -INFINITY;
                             }
                     }
+                } else if (hid) {
+#pragma unroll
+                    for (int rg = 0; rg < RG; ++rg)
+#pragma unroll
+                        for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if ((hw[rg] >> (kb * 16 + lg * 4 + i)) & 1u) sc[rg][kb][i] = -INFINITY;
                 } else if (vis_b) {
                     while (wm != 0u) {
                         const int k = __builtin_ctz(wm);          // key wk*32 + k of the tile
@@ -849,16 +912,23 @@ __global__ void __launch_bounds__(256) attn_combine_kernel(AttnArgs a)
 }
 
 template <int RG, int NWR, int NWK, int NPROD, int RING = kRing>
-hipError_t launch_cfg(const AttnArgs& a, hipStream_t s)
+hipError_t launch_cfg(const AttnArgs& a0, hipStream_t s)
 {
     using C = AttnCfg<RG, NWR, NWK, NPROD, RING>;
+    AttnArgs a = a0;
     if (a.nq > 64 * kMaxChunks || a.keys_per_split % C::TK != 0) return hipErrorInvalidValue;
     const int VW = (a.nq + 31) / 32;
     const int tiles = (a.keys_per_split + C::TK - 1) / C::TK;
     const size_t book = 2 * (size_t)((a.keys_per_split + 1) & ~1) + 8 * (size_t)tiles + 4 * (size_t)a.nq * VW +
                         4 * ((size_t)a.nq + 1) + (a.map.table ? 4 * (size_t)a.map.max_blocks : 0);
     if (C::SCRATCH + book > 160 * 1024) return hipErrorInvalidValue;
-    const size_t shm = C::SCRATCH + book;
+    // hidden-key words under a mask, when the step writes more than two keys
+    // per 32 of the split on average (fewer are gated one at a time in the
+    // loop at less cost than the words' extra barrier and build) and the
+    // words fit beside the rest
+    const size_t hid = 4 * (size_t)a.nq * (a.keys_per_split / 32) + 4 * 32 * (size_t)VW + 4 * (size_t)VW;
+    a.hid_words = a.vis != nullptr && a.nq > 2 * (a.keys_per_split / 32) && C::SCRATCH + book + hid <= 160 * 1024;
+    const size_t shm = C::SCRATCH + book + (a.hid_words ? hid : 0);
     const int total = a.B * a.Hkv * a.splits;
     const int grid = ((total + 7) / 8) * 8;
     constexpr auto kern = attn_mfma_kernel<RG, NWR, NWK, NPROD, RING>;

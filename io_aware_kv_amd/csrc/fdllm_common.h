@@ -80,6 +80,7 @@ struct AttnArgs {
     const int32_t* seq_len; // [B] valid cache positions of each sequence (>= 1) or NULL (all N)
     const int32_t* nq_seq;  // [B] query rows of each sequence or NULL (all nq)
     const int8_t* own;      // [B, nq] the step's ownership flags, as the projection recorded them
+    int hid_words;          // set by the MFMA launcher: per-row hidden-key words are built in LDS
 };
 
 // Tracked-set scores after a step: attention mass of the selected query rows
