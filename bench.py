@@ -1,11 +1,14 @@
 #!/usr/bin/env python3
 """Bench of the fused KV-cache step (one MI355X).
 
-A step is one pass of the whole hot path over one batch: gather X[Q] + QKV
-projection + rotary + in-place k/v write (first launch), then split-N
-attention over the whole cache with the view mask and the split combine
-(second launch).  Inputs are seeded synthetic tensors shaped like the layer
-workloads (io_aware_kv_amd.workloads) and already resident in HBM.  Several
+A step is one pass of the whole hot path over one batch through the
+library's step entry point (fdllm_fused_step): gather X[Q] + QKV projection +
+rotary + in-place k/v write (first launch), then split-N attention over the
+whole cache with the view mask and the split combine (second launch).  The
+phase figures time the two launches through the step's halves
+(fdllm_step_project, fdllm_step_attend).  Inputs are seeded synthetic
+tensors shaped like the layer workloads (io_aware_kv_amd.workloads) and
+already resident in HBM.  Several
 independent buffer sets (weights, hidden states, caches, outputs) are used
 round robin so that no step finds its data in the 256 MB Infinity Cache.
 
@@ -344,8 +347,7 @@ def time_graph_steps(fk, sets, steps, warmup):
     cs.wait_stream(torch.cuda.current_stream())
 
     def step(st):
-        fk.project(st["X"], st["Q"], st["P"], st["W"], st["Kc"], st["Vc"], stream=cs)
-        fk.attend(st["P"], st["vis"], st["Kc"], st["Vc"], st["O"], st["LSE"], stream=cs)
+        fk.step(st["X"], st["Q"], st["P"], st["vis"], st["W"], st["Kc"], st["Vc"], st["O"], st["LSE"], stream=cs)
 
     with torch.cuda.stream(cs):
         for st in sets:
@@ -427,8 +429,7 @@ def measure_config(cid, steps, warmup, dev, read_GBps=None):
         fk.attend(st["P"], st["vis"], st["Kc"], st["Vc"], st["O"], st["LSE"], stream=stream)
 
     def step(st):
-        proj(st)
-        attn(st)
+        fk.step(st["X"], st["Q"], st["P"], st["vis"], st["W"], st["Kc"], st["Vc"], st["O"], st["LSE"], stream=stream)
 
     step_ms = time_launches(step, sets, stream, steps, warmup)
     proj_ms = time_launches(proj, sets, stream, steps, warmup)
@@ -567,14 +568,17 @@ def main():
         fk.attend(st["P"], st["vis"], st["Kc"], st["Vc"], st["O"], st["LSE"], stream=stream)
 
     def step(st, evs=None):
-        if evs is not None:
-            evs[0].record(stream)
+        if evs is None:
+            # the library's step entry point
+            fk.step(st["X"], st["Q"], st["P"], st["vis"], st["W"], st["Kc"], st["Vc"], st["O"], st["LSE"],
+                    stream=stream)
+            return
+        # the phases as separate launches, an event around each
+        evs[0].record(stream)
         proj(st)
-        if evs is not None:
-            evs[1].record(stream)
+        evs[1].record(stream)
         attn(st)
-        if evs is not None:
-            evs[2].record(stream)
+        evs[2].record(stream)
 
     for i in range(args.warmup):
         step(sets[i % n_sets])

@@ -78,11 +78,15 @@ __global__ void __launch_bounds__(kGenThreads) proj_generic_kernel(ProjArgs a)
 #pragma unroll
             for (int u = 0; u < kCols; ++u) y[u] = fmaf(wv[u], xv, y[u]);
         }
+        // the eight columns' reduction steps interleaved, so each step waits
+        // once for its eight cross-lane reads (same sums, same order per column)
 #pragma unroll
-        for (int u = 0; u < kCols; ++u) {
-            for (int o = 32; o > 0; o >>= 1) y[u] += __shfl_xor(y[u], o);
+        for (int o = 32; o > 0; o >>= 1)
+#pragma unroll
+            for (int u = 0; u < kCols; ++u) y[u] += __shfl_xor(y[u], o);
+#pragma unroll
+        for (int u = 0; u < kCols; ++u)
             if (lane == 0 && c0 + u < a.dh) sy[c0 + u] = y[u];
-        }
     }
     __syncthreads();
 
