@@ -41,6 +41,8 @@ constexpr int kMassTK = 16 * kMassWaves;      // keys per ring stage
 constexpr int kMassStage = kMassTK * 256;     // bytes per stage (K rows of 256 B)
 constexpr int kMassMinStages = 3;
 constexpr int kMassUnroll = 4;                // direct form: 16-key blocks a wave loads before computing
+constexpr int kRowsWaves = 4;                 // pair-split ring form: consumer waves
+constexpr int kRowsBlocks = 4;                // ... and row blocks of 16 pairs each wave can hold
 
 __device__ __forceinline__ float sum4x(float x)
 {
@@ -238,6 +240,189 @@ __global__ void __launch_bounds__((kMassWaves + 1) * 64) key_mass_ring_kernel(Ma
         const int key = kt + wave * 16 + lr;
         const float cs = colsum_of(st, wave * 16 + lr, key);
         if (lg == 0 && key < k1) part[key] = cs;
+    }
+}
+
+// Ring form with the (selected row, head) pairs split across the consumer
+// waves, for up to NW * RBW * 16 pairs: the producer wave streams 64-key K
+// tiles into the LDS ring as in key_mass_ring_kernel; consumer wave w holds
+// its share of the pairs' row blocks (at most RBW of 16 pairs) in registers
+// and scores every key of each tile against them, so each K row is read
+// from HBM once and from LDS once per wave.  A wave's per-key sums stay in
+// LDS for the whole split and are added in wave order at the end (the same
+// bits on every run).
+template <int NW, int RBW>
+__global__ void __launch_bounds__((NW + 1) * 64) key_mass_rows_kernel(MassArgs a, int ns)
+{
+    constexpr int NT = (NW + 1) * 64;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    __shared__ int sNsel;
+    const int nq = a.nq, G = a.G;
+    const int VW = (nq + 31) >> 5;
+    const int kps = a.keys_per_split;
+    int* sSel = (int*)(smem + (size_t)ns * kMassStage);
+    int* sOwner = sSel + nq;
+    uint32_t* sVis = (uint32_t*)(sOwner + kps);
+    float* sAcc = (float*)(sVis + (size_t)nq * VW);   // [NW][kps] per-wave key sums
+
+    const int split = blockIdx.x % a.splits;
+    const int bg = blockIdx.x / a.splits;
+    const int b = bg / a.Hkv, g = bg - b * a.Hkv;
+    const int k0 = split * kps;
+    const int k1 = min(a.N, k0 + kps);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool producer = wave == NW;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int32_t* pos_b = a.pos_ids + (size_t)b * nq;
+    const uint8_t* sel_b = a.sel + (size_t)b * nq;
+    const uint8_t* vis_b = a.vis ? a.vis + (size_t)b * nq * nq : nullptr;
+
+    // selected rows in Q order (wave 0, 64 rows per ballot)
+    if (wave == 0) {
+        int n = 0;
+        for (int c = 0; c < nq; c += 64) {
+            const int j = c + lane;
+            const bool sl = j < nq && sel_b[j] != 0;
+            const uint64_t m = __builtin_amdgcn_ballot_w64(sl);
+            const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (sl) sSel[n + below] = j;
+            n += __builtin_popcountll(m);
+        }
+        if (lane == 0) sNsel = n;
+    }
+    // owner row of each position of the split: the first row in Q order
+    for (int k = tid; k < k1 - k0; k += NT) sOwner[k] = 0x7fffffff;
+    __syncthreads();
+    for (int j = tid; j < nq; j += NT) {
+        const int p = pos_b[j];
+        if (p >= k0 && p < k1) atomicMin(&sOwner[p - k0], j);
+    }
+    const int nsel = sNsel;
+    if (vis_b) {
+        for (int t = tid; t < nsel * VW; t += NT) {
+            const int sr = t / VW, w = t - sr * VW;
+            const uint8_t* row = vis_b + (size_t)sSel[sr] * nq;
+            uint32_t bits = 0u;
+            for (int e = 0; e < 32 && 32 * w + e < nq; ++e) bits |= (row[32 * w + e] != 0 ? 1u : 0u) << e;
+            sVis[t] = bits;
+        }
+    }
+    __syncthreads();
+
+    const int R = nsel * G;                       // selected (row, head) pairs (<= NW * RBW * 16)
+    const int nrb = (R + 15) >> 4;
+    const int per = (nrb + NW - 1) / NW;          // row blocks per consumer wave
+    const int ntile = (k1 - k0 + kMassTK - 1) / kMassTK;
+    const unsigned char* Kg = (const unsigned char*)((const bf16*)a.Kc + (size_t)bg * a.N * kDH);
+
+    if (producer) {
+        const int srow = lane >> 4, slot = lane & 15;
+        auto issue = [&](int t) {
+            unsigned char* st = smem + (size_t)(t % ns) * kMassStage;
+            const int kt = k0 + t * kMassTK;
+#pragma unroll
+            for (int i = 0; i < kMassTK / 4; ++i) {
+                const int row = 4 * i + srow;
+                const int key = min(kt + row, k1 - 1);       // rows past the split repeat its last key
+                __builtin_amdgcn_global_load_lds((glb_void*)(Kg + (size_t)key * 256 + ((slot ^ (row & 15)) << 4)),
+                                                 (lds_void*)(st + i * 1024), 16, 0, 0);
+            }
+        };
+        int issued = 0;
+        for (; issued < min(ns - 1, ntile); ++issued) issue(issued);
+        for (int t = 0; t < ntile; ++t) {
+            ring_producer_sync((issued - t - 1) * (kMassTK / 4));
+            if (issued < ntile && issued < t + ns) issue(issued++);
+        }
+    } else {
+        // this wave's row blocks rb0 .. rb0 + nrbw - 1 (none past the pairs)
+        const int rb0 = wave * per;
+        const int nrbw = max(0, min(per, nrb - rb0));
+        auto selrow = [&](int sr) { return nsel > 0 ? sSel[min(sr, nsel - 1)] : 0; };
+        const float* qbase = a.qbuf + (size_t)bg * a.q_max * G * kDH;
+        const float kLog2e = 1.4426950408889634f;
+        bf16x8 qh[RBW][4], ql[RBW][4];
+        float l2[RBW][4];
+        int srow[RBW][4];
+#pragma unroll
+        for (int j = 0; j < RBW; ++j) {
+            const int row = (rb0 + j) * 16 + lr;
+            const bool ok = j < nrbw && row < R;
+            const int rr = ok ? row : 0;
+            const int sr = rr / G, hl = rr - sr * G;
+            const float* qp = qbase + ((size_t)selrow(sr) * G + hl) * kDH;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const f32x4 x0 = *(const f32x4*)(qp + 32 * c + 8 * lg);
+                const f32x4 x1 = *(const f32x4*)(qp + 32 * c + 8 * lg + 4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = ok ? (e < 4 ? x0[e] : x1[e - 4]) * a.scale_log2 : 0.f;
+                    const bf16 hi = (bf16)x;
+                    qh[j][c][e] = hi;
+                    ql[j][c][e] = (bf16)(x - (float)hi);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int rowi = (rb0 + j) * 16 + 4 * lg + i;
+                const bool oki = j < nrbw && rowi < R;
+                const int ri = oki ? rowi : 0;
+                const int si = ri / G, hli = ri - si * G;
+                const float lse = a.LSE[((size_t)b * nq + selrow(si)) * a.H + g * G + hli];
+                // an empty key set (-inf) or a padding row contributes nothing
+                l2[j][i] = (oki && lse > -INFINITY) ? lse * kLog2e : INFINITY;
+                srow[j][i] = oki ? si : 0;
+            }
+        }
+        float* acc = sAcc + (size_t)wave * kps;
+        for (int t = 0; t < ntile; ++t) {
+            ring_consumer_sync();
+            const unsigned char* st = smem + (size_t)(t % ns) * kMassStage;
+            const int kt = k0 + t * kMassTK;
+#pragma unroll
+            for (int kb = 0; kb < kMassTK / 16; ++kb) {
+                const int krow = kb * 16 + lr;
+                const int key = kt + krow;
+                bf16x8 kf[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    kf[c] = *(const bf16x8*)(st + krow * 256 + (((c * 4 + lg) ^ (krow & 15)) << 4));
+                const int ow = sOwner[min(key, k1 - 1) - k0];
+                const int owner = ow == 0x7fffffff ? -1 : ow;
+                const bool gated = vis_b != nullptr && owner >= 0;
+                float cs = 0.f;
+#pragma unroll
+                for (int j = 0; j < RBW; ++j) {
+                    if (j >= nrbw) break;                    // (uniform)
+                    f32x4 sc = f32x4{-l2[j][0], -l2[j][1], -l2[j][2], -l2[j][3]};
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qh[j][c], kf[c], sc, 0, 0, 0);
+                        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ql[j][c], kf[c], sc, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        bool keep = key < k1;
+                        if (gated) keep = keep && ((sVis[srow[j][i] * VW + (owner >> 5)] >> (owner & 31)) & 1u);
+                        const float pv = __builtin_amdgcn_exp2f(sc[i]);   // 2^-inf = 0
+                        cs += keep ? pv : 0.f;
+                    }
+                }
+                cs = sum4x(cs);
+                if (lg == 0 && key < k1) acc[key - k0] = cs;
+            }
+        }
+    }
+    __syncthreads();
+    // the waves' sums of each key, added in wave order
+    float* part = a.part + (size_t)bg * a.N;
+    for (int k = tid; k < k1 - k0; k += NT) {
+        float v = sAcc[k];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) v += sAcc[(size_t)w * kps + k];
+        part[k0 + k] = v;
     }
 }
 
@@ -719,7 +904,23 @@ hipError_t launch_key_mass(const MassArgs& a, hipStream_t s)
     // workgroups than CUs
     const unsigned wgs = (unsigned)(a.B * a.Hkv * a.splits);
     hipError_t e;
-    if ((long)a.nq * a.G <= 48) {
+    const size_t rows_book = book + (size_t)kRowsWaves * a.keys_per_split * 4;
+    if ((long)a.nq * a.G > 192 && (long)a.nq * a.G <= 16L * kRowsWaves * kRowsBlocks &&
+        rows_book + (size_t)kMassMinStages * kMassStage + 256 <= 160 * 1024) {
+        // 193 to 256 pairs, which the direct form would take in four rounds
+        // (each reloading K and q): the ring with the pairs split across the
+        // waves.  With fewer pairs the direct form is as fast or faster
+        // (measured: 144 and 176 pairs per kv head 25 and 30 us direct against
+        // 35 and 44 us here; 224 pairs 50 against about 36 us).
+        const size_t budget = (wgs > 256 ? 80 : 160) * 1024 - 256 - rows_book;
+        int ns = (int)std::min<size_t>(8, budget / kMassStage);
+        if (ns < kMassMinStages) ns = (int)std::min<size_t>(8, (160 * 1024 - 256 - rows_book) / kMassStage);
+        const size_t shm = (size_t)ns * kMassStage + rows_book;
+        constexpr auto kern = key_mass_rows_kernel<kRowsWaves, kRowsBlocks>;
+        (void)allow_full_lds<kern>();
+        (void)hipGetLastError();
+        hipLaunchKernelGGL(kern, dim3(wgs), dim3((kRowsWaves + 1) * 64), shm, s, a, ns);
+    } else if ((long)a.nq * a.G <= 48) {
         // at most 48 (row, head) pairs can be selected: the K stream through
         // the LDS ring, all pairs in the registers of every wave
         const size_t budget = (wgs > 256 ? 80 : 160) * 1024 - 256 - book;

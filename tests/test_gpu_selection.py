@@ -90,7 +90,7 @@ def check_selection(wl, label, k=80):
             assert lo >= hi - 2 * (RTOL * hi + ATOL_REL * ref.max()), label + ": selection not a top-k"
 
 
-@pytest.mark.parametrize("cid", [2, 3, 6, 7, 1])
+@pytest.mark.parametrize("cid", [2, 3, 4, 6, 7, 1])
 def test_tracked_scores_layer_workloads(cid):
     log("case: tracked scores, workload %d" % cid)
     check_selection(make_workload(cid), "workload%d" % cid, k=80 if cid != 1 else 5)
@@ -114,12 +114,21 @@ def test_tracked_scores_ring_form_gqa_splits():
 
 
 def test_tracked_scores_many_rows_two_groups():
-    """More than 64 selected (row, head) pairs: the rows go through the
-    registers in two groups."""
+    """Up to 240 selected (row, head) pairs: the ring form with the pairs
+    split across its consumer waves (several row blocks per wave)."""
     log("case: tracked scores, 100 selected rows x G=2")
     ls = LayerShape(B=2, N=300, d_model=128, H=4, Hkv=2, dh=128)
     wl = make_random_case(ls, 120, seed=42, masked_vis=True, w_std=0.05)
     check_selection(wl, "two-row-groups", k=50)
+
+
+def test_tracked_scores_more_pairs_than_the_ring_forms_hold():
+    """More than 256 possible (row, head) pairs (70 rows x G = 4): the direct
+    form, which loads its key blocks straight into MFMA fragments."""
+    log("case: tracked scores, 70 rows x G=4")
+    ls = LayerShape(B=2, N=300, d_model=128, H=8, Hkv=2, dh=128)
+    wl = make_random_case(ls, 70, seed=49, n_extra_rows=4, dup_frac=0.1, masked_vis=True, w_std=0.05)
+    check_selection(wl, "direct-form", k=40)
 
 
 def test_select_top_ties_and_short_candidate_lists():
