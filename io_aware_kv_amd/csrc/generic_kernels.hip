@@ -43,8 +43,25 @@ __global__ void __launch_bounds__(kGenThreads) proj_generic_kernel(ProjArgs a)
         }
         return;
     }
+    // the first two d_model steps of this wave's first eight head columns are
+    // loaded before the row is staged (they do not depend on it), so the
+    // weights and the row arrive in one memory round trip
+    const T* W = (const T*)a.W + (size_t)head * a.dh * a.d;
+    constexpr int kCols = 8;
+    constexpr int kPre = 2;
+    float wpre[kPre][kCols];
+#pragma unroll
+    for (int i = 0; i < kPre; ++i)
+#pragma unroll
+        for (int u = 0; u < kCols; ++u) {
+            const int c = min(wave * kCols + u, a.dh - 1), k = min(lane + 64 * i, a.d - 1);
+            wpre[i][u] = to_f32(W[(size_t)c * a.d + k]);
+        }
     const int xrow = a.prefill ? j : a.Q_idx[m];
     const int pos = a.prefill ? j : a.pos_ids[m];
+    // this thread's rotary pair of the row's position, also ahead of the row
+    const bool rot = head < a.H + a.Hkv;
+    const float2 cs0 = rot && tid < a.dh / 2 ? a.rope[(size_t)pos * (a.dh / 2) + tid] : make_float2(1.f, 0.f);
 
     const T* x = (const T*)a.X + ((size_t)b * a.x_rows + xrow) * a.d;
     for (int k = tid; k < a.d; k += kGenThreads) sx[k] = to_f32(x[k]);
@@ -60,8 +77,6 @@ __global__ void __launch_bounds__(kGenThreads) proj_generic_kernel(ProjArgs a)
 
     // each wave takes eight head columns at a time, so every step of its
     // d_model loop has eight independent weight loads in flight
-    const T* W = (const T*)a.W + (size_t)head * a.dh * a.d;
-    constexpr int kCols = 8;
     for (int c0 = wave * kCols; c0 < a.dh; c0 += (kGenThreads / 64) * kCols) {
         float y[kCols];
         const T* w[kCols];
@@ -70,10 +85,16 @@ __global__ void __launch_bounds__(kGenThreads) proj_generic_kernel(ProjArgs a)
             y[u] = 0.f;
             w[u] = W + (size_t)min(c0 + u, a.dh - 1) * a.d;
         }
-        for (int k = lane; k < a.d; k += 64) {
+        const bool first = c0 == wave * kCols;
+        for (int k = lane, i = 0; k < a.d; k += 64, ++i) {
             float wv[kCols];
+            if (first && i < kPre) {
 #pragma unroll
-            for (int u = 0; u < kCols; ++u) wv[u] = to_f32(w[u][k]);
+                for (int u = 0; u < kCols; ++u) wv[u] = i == 0 ? wpre[0][u] : wpre[1][u];
+            } else {
+#pragma unroll
+                for (int u = 0; u < kCols; ++u) wv[u] = to_f32(w[u][k]);
+            }
             const float xv = sx[k];
 #pragma unroll
             for (int u = 0; u < kCols; ++u) y[u] = fmaf(wv[u], xv, y[u]);
@@ -108,7 +129,7 @@ __global__ void __launch_bounds__(kGenThreads) proj_generic_kernel(ProjArgs a)
     for (int c = tid; c < half; c += kGenThreads) {
         float y0 = sy[c], y1 = sy[c + half];
         if (rotate) {
-            const float2 cs = a.rope[(size_t)pos * half + c];
+            const float2 cs = c == tid ? cs0 : a.rope[(size_t)pos * half + c];
             const float r0 = y0 * cs.x - y1 * cs.y;
             const float r1 = y1 * cs.x + y0 * cs.y;
             y0 = r0;
@@ -163,32 +184,6 @@ __global__ void __launch_bounds__(kGenThreads) attn_generic_kernel(AttnArgs a)
     const int nqb = a.nq_seq ? a.nq_seq[b] : nq;       // rows of this sequence
     const int L = a.seq_len ? a.seq_len[b] : a.N;      // its valid cache positions
 
-    const int32_t* pos_b = a.pos_ids + (size_t)b * nq;
-    for (int jj = tid; jj < nqb; jj += kGenThreads) spos[jj] = pos_b[jj];
-    const float* qb = a.qbuf + ((size_t)b * a.Hkv + g) * a.q_max * G * dh;
-    for (int e = tid; e < kGR * dh; e += kGenThreads) {
-        const int rr = e / dh, d = e - rr * dh;
-        const int r = rb * kGR + rr;
-        sq[e] = (r < a.R && r / G < nqb) ? qb[(size_t)r * dh + d] : 0.f;
-    }
-    __syncthreads();
-    for (int jj = tid; jj < nqb; jj += kGenThreads) {
-        int f = jj;
-        for (int q = 0; q < jj; ++q)
-            if (spos[q] == spos[jj]) { f = q; break; }
-        sown[jj] = f;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        int n = 0;
-        for (int jj = 0; jj < nqb; ++jj)
-            if (sown[jj] != jj) sdup[n++] = jj;
-        sndup[0] = n;
-    }
-    __syncthreads();
-    const int ndup = sndup[0];
-    const int nkeys = L + ndup;
-
     // thread roles: query row rr of the block, key pair kq / kq + 16 for the
     // scores, dims dq + 16 u for the output
     const int rr = tid >> 4, kq = tid & 15;
@@ -218,6 +213,9 @@ __global__ void __launch_bounds__(kGenThreads) attn_generic_kernel(AttnArgs a)
     const int k_first = tid / U, c_first = tid - k_first * U;
     const int k_step = kGenThreads / U, c_step = kGenThreads - k_step * U;
     u32x4 pku[kUPT], pvu[kUPT];
+    // keys past L are the side buffer's rows; their count is known after the
+    // ownership pass below (until then no fetch reaches past L)
+    int nkeys = L;
     auto fetch = [&](int base) {
         int k = k_first, c = c_first;
 #pragma unroll
@@ -255,7 +253,38 @@ __global__ void __launch_bounds__(kGenThreads) attn_generic_kernel(AttnArgs a)
             }
         }
     };
-    fetch(0);
+    // the first chunk's K and V rows (cache positions only) are fetched
+    // before the q rows and positions are staged, so both take one memory
+    // round trip
+    if (L >= kGK) fetch(0);
+
+
+    const int32_t* pos_b = a.pos_ids + (size_t)b * nq;
+    for (int jj = tid; jj < nqb; jj += kGenThreads) spos[jj] = pos_b[jj];
+    const float* qb = a.qbuf + ((size_t)b * a.Hkv + g) * a.q_max * G * dh;
+    for (int e = tid; e < kGR * dh; e += kGenThreads) {
+        const int rr = e / dh, d = e - rr * dh;
+        const int r = rb * kGR + rr;
+        sq[e] = (r < a.R && r / G < nqb) ? qb[(size_t)r * dh + d] : 0.f;
+    }
+    __syncthreads();
+    for (int jj = tid; jj < nqb; jj += kGenThreads) {
+        int f = jj;
+        for (int q = 0; q < jj; ++q)
+            if (spos[q] == spos[jj]) { f = q; break; }
+        sown[jj] = f;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int n = 0;
+        for (int jj = 0; jj < nqb; ++jj)
+            if (sown[jj] != jj) sdup[n++] = jj;
+        sndup[0] = n;
+    }
+    __syncthreads();
+    const int ndup = sndup[0];
+    nkeys = L + ndup;
+    if (L < kGK) fetch(0);   // the first chunk reaches the side buffer
     for (int base = 0; base < nkeys; base += kGK) {
         // written positions of the chunk and their owner rows
         if (tid < kGK) sslot[tid] = -1;
