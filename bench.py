@@ -26,6 +26,7 @@ other layer workloads of the target set;
                   [--other-configs 1,2,4]
   python bench.py --mode copy      # plain device copy, for counter calibration
   python bench.py --mode stream    # the device's streaming read and copy rates
+  python bench.py --mode stack --steps 5 --warmup 1   # the large-batch workload's 32-layer stack
 """
 import argparse
 import hashlib
@@ -513,6 +514,53 @@ def run_probes(args):
                       "lds_dma_l2_resident": dma, "hbm_peak_GBps": HBM_PEAK_GBPS}))
 
 
+def run_stack(args):
+    """The large-batch workload as a whole stack: --layers consecutive layers
+    (32 by default), each with its own weights and its own K/V cache in HBM,
+    the same hidden states and query rows, one fused step per layer back to
+    back.  Layer l's weights are drawn on the device from seed 20265 + 1000 l
+    (N(0, 0.02^2), cast once to bf16); every layer's cache starts from the
+    layer-0 seeded content (the step's timing does not depend on the values).
+    Reports the stack's time, the time per layer and the algorithmic bytes of
+    the stack over that time."""
+    import torch
+    from io_aware_kv_amd.binding import FusedKVCache
+    from io_aware_kv_amd.workloads import initial_cache, make_workload
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    log("bench: stack of %d layers, generating inputs" % args.layers)
+    wl = make_workload(5)
+    ls = wl.shape
+    ab = algorithmic_bytes(wl)
+    K0, V0 = initial_cache(wl)
+    X, Q, P = wl.X.to(dev), wl.Q_idx.to(dev), wl.pos_ids.to(dev)
+    layers = []
+    for l in range(args.layers):
+        g = torch.Generator(device=dev).manual_seed(20265 + 1000 * l)
+        W = (torch.randn(tuple(wl.W.shape), generator=g, device=dev) * 0.02).to(ls.dtype)
+        layers.append(dict(W=W, Kc=K0.to(dev).contiguous(), Vc=V0.to(dev).contiguous(),
+                           O=torch.empty((ls.B, wl.nq, ls.H, ls.dh), dtype=ls.dtype, device=dev),
+                           LSE=torch.empty((ls.B, wl.nq, ls.H), dtype=torch.float32, device=dev)))
+    fk = FusedKVCache(ls.B, ls.N, ls.d_model, ls.H, ls.Hkv, ls.dh, wl.nq, ls.dtype, ls.rope_base)
+    torch.cuda.synchronize()
+    hbm = sum(t.numel() * t.element_size() for st in layers for t in st.values()) + X.numel() * X.element_size()
+    log("bench: %.1f GB of weights, caches and outputs in HBM" % (hbm / 1e9))
+
+    def stack(_):
+        for st in layers:
+            fk.step(X, Q, P, None, st["W"], st["Kc"], st["Vc"], st["O"], st["LSE"], stream=stream)
+
+    ms = time_launches(stack, [None], stream, args.steps, args.warmup)
+    fk.close()
+    total = ab["total"] * args.layers
+    print(json.dumps({"mode": "stack", "workload": wl.name, "layers": args.layers, "steps": args.steps,
+                      "stack_ms": round(ms, 4), "layer_us": round(ms * 1e3 / args.layers, 3),
+                      "queries_per_s": round(ls.B * wl.nq / (ms * 1e-3), 1),
+                      "algorithmic_bytes_per_stack": total, "GBps": round(total / (ms * 1e-3) / 1e9, 1),
+                      "hbm_resident_GB": round(hbm / 1e9, 2)}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -528,7 +576,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--attn-splits", type=int, default=0)
     ap.add_argument("--gemm-splitk", type=int, default=0)
-    ap.add_argument("--mode", default="step", choices=["step", "copy", "stream", "probes"])
+    ap.add_argument("--mode", default="step", choices=["step", "copy", "stream", "probes", "stack"])
+    ap.add_argument("--layers", type=int, default=32, help="--mode stack: layers of the large-batch stack")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     args = ap.parse_args()
 
@@ -544,6 +593,8 @@ def main():
         return run_stream(args)
     if args.mode == "probes":
         return run_probes(args)
+    if args.mode == "stack":
+        return run_stack(args)
 
     from io_aware_kv_amd.workloads import make_workload
 
