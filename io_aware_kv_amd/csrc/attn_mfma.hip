@@ -964,7 +964,13 @@ hipError_t launch_attn_mfma(const AttnArgs& a, hipStream_t s)
     const int r16 = (a.R + 15) / 16;
     if (r16 <= 1) return launch_cfg<1, 1, 2, 1>(a, s);
     if (r16 <= 2) return launch_cfg<1, 2, 2, 2>(a, s);
-    if (r16 <= 3) return launch_cfg<1, 3, 2, 2>(a, s);
+    // up to three row groups: with the cache split (few kv heads, as in a
+    // draft pass of one sequence) each workgroup streams only a few tiles,
+    // and one wave per row group taking all keys of a tile avoids the
+    // key-split waves' merge at the end (draft pass: step 35.8 -> 34.8 us);
+    // over whole caches the key split's two waves per SIMD are faster
+    // (verification layer: 54 against 61 us)
+    if (r16 <= 3) return a.splits > 1 ? launch_cfg<1, 3, 1, 2>(a, s) : launch_cfg<1, 3, 2, 2>(a, s);
     if (r16 <= 4) {
         // more workgroups than CUs: 32-key tiles in a 64 KB ring, so two
         // workgroups share a CU and the launch runs in one round
