@@ -289,7 +289,7 @@ def time_paged(fk, wl, stream, iters, n_sets, warmup, block_size=16):
     return {"block_size": block_size, "step_us": round(e0.elapsed_time(e1) / iters * 1e3, 3)}
 
 
-def build_sets(wl, n_sets, dev, attn_splits=0, gemm_splitk=0):
+def build_sets(wl, n_sets, dev, attn_splits=0, gemm_splitk=0, proj_tile=0):
     """The layer's handle and n_sets independent buffer sets (hidden states,
     weights, caches from the seeded initial cache, outputs, indices)."""
     import torch
@@ -298,8 +298,8 @@ def build_sets(wl, n_sets, dev, attn_splits=0, gemm_splitk=0):
     ls = wl.shape
     K0, V0 = initial_cache(wl)
     fk = FusedKVCache(ls.B, ls.N, ls.d_model, ls.H, ls.Hkv, ls.dh, wl.nq, ls.dtype, ls.rope_base)
-    if attn_splits or gemm_splitk:
-        fk.set_tuning(attn_splits=attn_splits, gemm_splitk=gemm_splitk)
+    if attn_splits or gemm_splitk or proj_tile:
+        fk.set_tuning(attn_splits=attn_splits, gemm_splitk=gemm_splitk, proj_tile=proj_tile)
     sets = []
     for _ in range(n_sets):
         Kc = K0.to(dev).contiguous()
@@ -576,6 +576,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--attn-splits", type=int, default=0)
     ap.add_argument("--gemm-splitk", type=int, default=0)
+    ap.add_argument("--proj-tile", type=int, default=0, help="projection tile choice override (0: the library's)")
     ap.add_argument("--mode", default="step", choices=["step", "copy", "stream", "probes", "stack"])
     ap.add_argument("--layers", type=int, default=32, help="--mode stack: layers of the large-batch stack")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
@@ -606,7 +607,7 @@ def main():
     ab = algorithmic_bytes(wl)
     per_set = ab["total"] + ls.B * wl.x_rows * ls.d_model * (2 if ls.dtype == torch.bfloat16 else 4)
     n_sets = args.sets or n_sets_for(ab)
-    fk, sets, K0, V0 = build_sets(wl, n_sets, dev, args.attn_splits, args.gemm_splitk)
+    fk, sets, K0, V0 = build_sets(wl, n_sets, dev, args.attn_splits, args.gemm_splitk, args.proj_tile)
     plan = fk.plan(wl.nq)
     log("bench: %d buffer sets of %.1f MB, plan %s" % (n_sets, per_set / 1e6, plan))
 
