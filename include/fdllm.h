@@ -233,6 +233,12 @@ int fdllm_select_tracked(fdllm_handle_t h, const float* scores, const uint8_t* c
  * exploratory set (0); with thr = gamma it is the mask view's confidence test.
  * At least one logit of a row must be finite.  pred int32 [rows], conf fp32
  * [rows], over uint8 [rows], caller-owned device pointers.
+ * With fewer rows than CUs a row is spread over several workgroups that meet
+ * in a small table of the library's own device memory (8192 row slots per
+ * device, each set back to zero by the row's last workgroup); each call takes
+ * its rows' slots in turn, so calls in flight together on one device (other
+ * streams) stay apart unless they hold more than 8192 such rows between them.
+ * Results do not depend on the order the workgroups finish in.
  * Statuses: ARG (NULL pointer, V < 1, rows < 0, dtype), ALIGN, HIP. */
 int fdllm_confidence(const void* logits, int32_t dtype, int64_t rows, int32_t V, int32_t mask_id, float thr,
                      int32_t* pred, float* conf, uint8_t* over, void* stream);

@@ -11,10 +11,13 @@
 // decoding order while the mask view agrees with the draft and its own
 // confidence is >= gamma, up to the first failure.
 //
-//  * confidence_kernel: one workgroup per row of logits, 16-byte loads, an
-//    online (max, sum of 2^(x - max)) over the whole vocabulary and the
-//    argmax over the non-[MASK] ids (ties to the lowest id); the confidence
-//    is that token's probability under the softmax over every id.
+//  * confidence_kernel: one or more workgroups per row of logits, 16-byte
+//    loads, an online (max, sum of 2^(x - max)) over the whole vocabulary
+//    and the argmax over the non-[MASK] ids (ties to the lowest id); the
+//    confidence is that token's probability under the softmax over every id.
+//    A CU streams a row's misses at ~25 GB/s, so with fewer rows than CUs a
+//    row is cut into up to eight id ranges on separate workgroups; the last
+//    of them to finish merges the ranges' partial results in range order.
 //  * accept_kernel: one lane per sequence walks its exploratory rows in
 //    decoding order.
 #include "fdllm_common.h"
@@ -25,6 +28,8 @@ namespace {
 
 constexpr int kConfThreads = 1024;
 constexpr int kConfLoads = 4;        // 16-byte loads per thread per round
+constexpr int kConfMaxSplit = 8;     // id ranges per row at most
+constexpr int kConfSlots = 8192;     // rows of the per-device meeting table
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -33,6 +38,14 @@ struct Best {
     float bl;        // best non-[MASK] logit (as given: the argmax compares raw values)
     int bi;          // its id (lowest among equal logits)
 };
+
+// Where the id ranges of a split row meet: a count of finished ranges per row
+// slot (back to zero once the row is merged) and each range's partial result.
+// A call takes rows' worth of consecutive slots from a host-side ticket, so
+// calls in flight together on one device meet in separate slots unless they
+// hold more than kConfSlots split rows between them.
+__device__ unsigned conf_count[kConfSlots];
+__device__ Best conf_part[kConfSlots * kConfMaxSplit];
 
 __device__ __forceinline__ void take(Best& b, float raw, int id, int mask_id)
 {
@@ -62,99 +75,126 @@ __device__ __forceinline__ Best merge(const Best& a, const Best& b)
     return r;
 }
 
+// A lane's state over the vector rounds: the running max, four partial sums
+// of 2^(x - m) (four independent add chains), the best non-[MASK] logit and
+// the first id of the round that holds it.
+struct Acc {
+    float m, s[4], bl;
+    int bround;
+};
+
+// One round of a lane: NL 16-byte chunks, chunk u holding ids id0 + u * US ...
+// Per element only the raw max and one fused multiply-add + exp2 + add: the
+// round's raw max gives the rescale (scaling by log2 e and rounding are
+// monotonic, so it bounds every scaled logit of the round), and the lane keeps
+// the raw data of the round that holds its best non-[MASK] logit, so the
+// first id holding it is found once after the range (ids grow along a lane's
+// walk).  FULL: every chunk lies below hi (no range checks).
+template <typename T, int NL, int US, bool FULL>
+__device__ __forceinline__ void take_round(Acc& a, u32x4 (&keep)[NL], const u32x4 (&raw)[NL], int id0, int hi,
+                                           int mask_id)
+{
+    constexpr int PER = 16 / sizeof(T);
+    float f[NL * PER];
+    float rmax = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+        const bool in = FULL || id0 + u * US < hi;
+        const T* e = (const T*)&raw[u];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            f[u * PER + k] = in ? to_f32(e[k]) : -INFINITY;
+            rmax = fmaxf(rmax, f[u * PER + k]);
+        }
+    }
+    // the [MASK] id is left out of the argmax only
+    float amax = rmax;
+    const int d = mask_id - id0;
+    if (d >= 0 && d < NL * US && (d & (US - 1)) < PER) {
+        amax = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < NL; ++u)
+#pragma unroll
+            for (int k = 0; k < PER; ++k)
+                if (id0 + u * US + k != mask_id) amax = fmaxf(amax, f[u * PER + k]);
+    }
+    // a round's first chunk is in range, so it holds a non-[MASK] id
+    const bool better = amax > a.bl || a.bround < 0;
+    if (better) {
+        a.bl = amax;
+        a.bround = id0;
+    }
+#pragma unroll
+    for (int u = 0; u < NL; ++u) keep[u] = better ? raw[u] : keep[u];
+    if (rmax > -INFINITY) {
+        const float rm = rmax * kLog2e;
+        if (rm > a.m) {
+            const float c = __builtin_amdgcn_exp2f(a.m - rm);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) a.s[j] *= c;
+            a.m = rm;
+        }
+        const float nm = -a.m;
+#pragma unroll
+        for (int k = 0; k < NL * PER; ++k) a.s[k & 3] += __builtin_amdgcn_exp2f(__builtin_fmaf(f[k], kLog2e, nm));
+    }
+}
+
+// grid: rows x nsplit workgroups; workgroup (row, sp) takes ids
+// [sp * rlen, min(V, (sp + 1) * rlen)) of its row; rlen is a multiple of
+// 1024 * NL * 16 / sizeof(T) ids unless nsplit == 1.
 template <typename T, int NL>
 __global__ void __launch_bounds__(kConfThreads) confidence_kernel(const T* __restrict__ logits, int V, int mask_id,
                                                                   float thr, int32_t* __restrict__ pred,
-                                                                  float* __restrict__ conf, uint8_t* __restrict__ over)
+                                                                  float* __restrict__ conf, uint8_t* __restrict__ over,
+                                                                  int nsplit, int rlen, unsigned slot0)
 {
-    const size_t row = blockIdx.x;
+    const size_t row = blockIdx.x / nsplit;
+    const int sp = blockIdx.x - (int)row * nsplit;
+    const int lo = sp * rlen, hi = min(V, lo + rlen);
     const T* x = logits + row * (size_t)V;
     Best b{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
     constexpr int PER = 16 / sizeof(T);                 // elements per 16-byte load
-    const bool vec = (V % PER) == 0;
+    constexpr int US = kConfThreads * PER;              // id stride between a lane's loads
+    constexpr int RSTEP = US * NL;                      // ids per round of the workgroup
     const int tid = threadIdx.x;
-    if (vec) {
-        // kConfLoads 16-byte loads in flight per thread per round.  Per
-        // element only the raw max and the exp2 sum: the round's max of the
-        // raw logits gives the rescale (scaling by log2 e and rounding are
-        // monotonic, so it bounds every scaled logit of the round), and a
-        // lane keeps its best non-[MASK] logit with the raw data of the round
-        // that holds it; after the row the first id holding it is found in
-        // that copy (ids grow along a lane's walk, so the lowest id wins
-        // ties).  The [MASK] id is left out of the argmax only, by a check
-        // per load.
-        int bround = -1;                                // round of the lane's best logit
-        u32x4 keep[NL];                                 // ... and its raw logits
-        for (int v0 = tid * PER; v0 < V; v0 += kConfThreads * PER * NL) {
+    if ((V % PER) == 0) {
+        Acc a{-INFINITY, {0.f, 0.f, 0.f, 0.f}, -INFINITY, -1};
+        u32x4 keep[NL];
+        const int nfull = hi > lo ? (hi - lo) / RSTEP : 0;
+        int v0 = lo + tid * PER;
+        for (int r = 0; r < nfull; ++r, v0 += RSTEP) {
             u32x4 raw[NL];
 #pragma unroll
-            for (int u = 0; u < NL; ++u) {
-                const int v = min(v0 + u * kConfThreads * PER, V - PER);
-                raw[u] = *(const u32x4*)(x + v);
-            }
-            float f[NL * PER];
-            float rmax = -INFINITY;
-            bool has_mask = false;
-#pragma unroll
-            for (int u = 0; u < NL; ++u) {
-                const int base = v0 + u * kConfThreads * PER;
-                const bool in = base < V;
-                has_mask = has_mask || (in && mask_id >= base && mask_id < base + PER);
-                const T* e = (const T*)&raw[u];
-#pragma unroll
-                for (int k = 0; k < PER; ++k) {
-                    f[u * PER + k] = in ? to_f32(e[k]) : -INFINITY;
-                    rmax = fmaxf(rmax, f[u * PER + k]);
-                }
-            }
-            float amax = rmax;                          // best non-[MASK] logit of the round
-            if (has_mask) {
-                amax = -INFINITY;
-#pragma unroll
-                for (int u = 0; u < NL; ++u)
-#pragma unroll
-                    for (int k = 0; k < PER; ++k)
-                        if (v0 + u * kConfThreads * PER + k != mask_id) amax = fmaxf(amax, f[u * PER + k]);
-            }
-            // a new best for this lane: remember the round (its id is found
-            // after the row, from one re-read of that round)
-            // (a round's first load is in range, so it holds a non-[MASK] id)
-            const bool better = amax > b.bl || bround < 0;
-            if (better) {
-                b.bl = amax;
-                bround = v0;
-            }
-#pragma unroll
-            for (int u = 0; u < NL; ++u) keep[u] = better ? raw[u] : keep[u];
-            if (rmax > -INFINITY) {
-                const float rm = rmax * kLog2e;
-                if (rm > b.m) {
-                    b.s *= __builtin_amdgcn_exp2f(b.m - rm);
-                    b.m = rm;
-                }
-                const float nm = -b.m;
-#pragma unroll
-                for (int k = 0; k < NL * PER; ++k) b.s += __builtin_amdgcn_exp2f(__builtin_fmaf(f[k], kLog2e, nm));
-            }
+            for (int u = 0; u < NL; ++u) raw[u] = *(const u32x4*)(x + v0 + u * US);
+            take_round<T, NL, US, true>(a, keep, raw, v0, hi, mask_id);
         }
-        if (bround >= 0) {
+        if (v0 < hi) {
+            u32x4 raw[NL];
+#pragma unroll
+            for (int u = 0; u < NL; ++u) raw[u] = *(const u32x4*)(x + min(v0 + u * US, hi - PER));
+            take_round<T, NL, US, false>(a, keep, raw, v0, hi, mask_id);
+        }
+        b.m = a.m;
+        b.s = (a.s[0] + a.s[1]) + (a.s[2] + a.s[3]);
+        b.bl = a.bl;
+        if (a.bround >= 0) {
             // the first in-range non-[MASK] id of that round holding the best
             // logit (the round holds one when the best is -inf too)
 #pragma unroll
             for (int u = 0; u < NL; ++u) {
-                const int base = bround + u * kConfThreads * PER;
-                if (base >= V) break;
                 const T* e = (const T*)&keep[u];
 #pragma unroll
                 for (int k = 0; k < PER; ++k) {
-                    const int id = base + k;
+                    const int id = a.bround + u * US + k;
                     const float fv = to_f32(e[k]);
-                    if (b.bi == 0x7fffffff && id != mask_id && (fv == b.bl || b.bl == -INFINITY)) b.bi = id;
+                    if (b.bi == 0x7fffffff && id < hi && id != mask_id && (fv == b.bl || b.bl == -INFINITY))
+                        b.bi = id;
                 }
             }
         }
     } else {
-        for (int v = tid; v < V; v += kConfThreads) take(b, to_f32(x[v]), v, mask_id);
+        for (int v = lo + tid; v < hi; v += kConfThreads) take(b, to_f32(x[v]), v, mask_id);
     }
     // workgroup merge: lanes, then waves through LDS
 #pragma unroll
@@ -169,15 +209,46 @@ __global__ void __launch_bounds__(kConfThreads) confidence_kernel(const T* __res
     __shared__ Best sb[kConfThreads / 64];
     if ((tid & 63) == 0) sb[tid >> 6] = b;
     __syncthreads();
-    if (tid == 0) {
-        Best r = sb[0];
-        for (int w = 1; w < kConfThreads / 64; ++w) r = merge(r, sb[w]);
-        // probability of the best non-[MASK] id under the softmax over all ids
-        const float c = (r.bi == 0x7fffffff || !(r.s > 0.f)) ? 0.f : __builtin_amdgcn_exp2f(r.bl * kLog2e - r.m) / r.s;
-        pred[row] = r.bi == 0x7fffffff ? -1 : r.bi;
-        conf[row] = c;
-        if (over) over[row] = c >= thr ? 1 : 0;
+    if (tid != 0) return;
+    Best r = sb[0];
+    for (int w = 1; w < kConfThreads / 64; ++w) r = merge(r, sb[w]);
+    if (nsplit > 1) {
+        // Publish this range's result; the last range of the row to arrive
+        // merges all of them in range order, so the result does not depend
+        // on the arrival order.  The partials are written and read only as
+        // agent-scope atomics (coherent across the XCDs' L2s, no cached copy
+        // to write back or invalidate), and the count is taken once those
+        // stores have completed (vmcnt 0): the ordering an agent-scope
+        // release gives, without its write-back of the whole L2 (measured
+        // 1-3 us slower as a plain acquire-release count).
+        const unsigned slot = (slot0 + (unsigned)row) % kConfSlots;
+        float* mine = (float*)&conf_part[slot * kConfMaxSplit + sp];
+        __hip_atomic_store(mine + 0, r.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(mine + 1, r.s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(mine + 2, r.bl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store((int*)mine + 3, r.bi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        const unsigned done = __hip_atomic_fetch_add(&conf_count[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (done != (unsigned)nsplit - 1) return;
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        auto part = [&](int k) {
+            const float* q = (const float*)&conf_part[slot * kConfMaxSplit + k];
+            Best t;
+            t.m = __hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            t.s = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            t.bl = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            t.bi = __hip_atomic_load((const int*)q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return t;
+        };
+        r = part(0);
+        for (int k = 1; k < nsplit; ++k) r = merge(r, part(k));
+        __hip_atomic_store(&conf_count[slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    // probability of the best non-[MASK] id under the softmax over all ids
+    const float c = (r.bi == 0x7fffffff || !(r.s > 0.f)) ? 0.f : __builtin_amdgcn_exp2f(r.bl * kLog2e - r.m) / r.s;
+    pred[row] = r.bi == 0x7fffffff ? -1 : r.bi;
+    conf[row] = c;
+    if (over) over[row] = c >= thr ? 1 : 0;
 }
 
 __global__ void __launch_bounds__(64) accept_kernel(const int32_t* __restrict__ x_hat, const int32_t* __restrict__ x_tilde,
@@ -200,12 +271,28 @@ hipError_t launch_confidence(const void* logits, int dtype, int64_t rows, int V,
                              int32_t* pred, float* conf, uint8_t* over, hipStream_t s)
 {
     if (rows == 0) return hipSuccess;
+    // with fewer rows than CUs, cut each row into up to eight ranges of
+    // whole rounds (at least one round each) so that about one row-range runs
+    // per CU; the ranges of a row meet in slots taken from a ticket
+    const int esz = dtype == 1 ? 2 : 4;
+    const int round_ids = kConfThreads * kConfLoads * (16 / esz);
+    const int rounds = (V + round_ids - 1) / round_ids;
+    int nsplit = 1;
+    while (nsplit < kConfMaxSplit && rows * nsplit * 2 <= 256 && nsplit * 2 <= rounds) nsplit *= 2;
+    int rlen = V;
+    unsigned slot0 = 0;
+    if (nsplit > 1) {
+        rlen = ((rounds + nsplit - 1) / nsplit) * round_ids;
+        static std::atomic<unsigned> ticket{0};
+        slot0 = ticket.fetch_add((unsigned)rows) % kConfSlots;
+    }
+    const dim3 grid((unsigned)(rows * nsplit));
     if (dtype == 1)
-        hipLaunchKernelGGL((confidence_kernel<bf16, kConfLoads>), dim3((unsigned)rows), dim3(kConfThreads), 0, s,
-                           (const bf16*)logits, V, mask_id, thr, pred, conf, over);
+        hipLaunchKernelGGL((confidence_kernel<bf16, kConfLoads>), grid, dim3(kConfThreads), 0, s, (const bf16*)logits,
+                           V, mask_id, thr, pred, conf, over, nsplit, rlen, slot0);
     else
-        hipLaunchKernelGGL((confidence_kernel<float, kConfLoads>), dim3((unsigned)rows), dim3(kConfThreads), 0, s,
-                           (const float*)logits, V, mask_id, thr, pred, conf, over);
+        hipLaunchKernelGGL((confidence_kernel<float, kConfLoads>), grid, dim3(kConfThreads), 0, s,
+                           (const float*)logits, V, mask_id, thr, pred, conf, over, nsplit, rlen, slot0);
     return hipGetLastError();
 }
 

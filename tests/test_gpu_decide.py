@@ -121,6 +121,63 @@ def test_confidence_argmax_corner_rows(dtype, V):
     assert rel.max() <= 1e-5
 
 
+SPLIT_CASES = [
+    # (label, rows, V, dtype): rows few enough that each row is cut into id
+    # ranges (ranges of whole rounds of 1024 threads x four 16-byte loads)
+    ("bf16-4-ranges", 5, 131072, torch.bfloat16),     # rounds of 32768 ids
+    ("bf16-2-ranges", 128, 131072, torch.bfloat16),
+    ("f32-8-ranges", 3, 131072, torch.float32),       # rounds of 16384 ids
+    ("f32-ragged", 2, 131072 - 4, torch.float32),     # last range short
+    ("bf16-ragged-scalar", 4, 70001, torch.bfloat16), # V not a multiple of 8: element loads
+]
+
+
+@pytest.mark.parametrize("label,rows,V,dtype", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_confidence_rows_split_over_workgroups(label, rows, V, dtype):
+    """Few rows: each row's ids are cut into ranges on separate workgroups and
+    the last range to finish merges them.  Corner rows put equal maxima in
+    different ranges (the lowest id wins), the maximum on both sides of a
+    range boundary, the [MASK] id holding the maximum in a later range, and a
+    row whose only finite logit sits in the last range.  Three calls in a row
+    (the meeting slots must be back at zero) give the same bits."""
+    log("case: confidence split rows %s" % label)
+    e = 16 // (4 if dtype == torch.float32 else 2)
+    rnd = 1024 * 4 * e                                    # ids per round
+    x = decision_logits(rows, V, seed=V + rows, dtype=torch.float32)
+    top = float(x.max()) + 1.0
+    mask_id = min(rnd + 77, V - 1)
+    x[0, 3 * rnd // 2 + 9] = top                           # equal maxima in two ranges: the lower id wins
+    x[0, V - 5] = top
+    if rows > 1:
+        x[1, rnd - 1] = top                               # last id of a range ...
+        x[1, rnd] = top                                   # ... and the first of the next: rnd - 1 wins
+    if rows > 2:
+        x[2, mask_id] = top + 3.0                         # [MASK] holds the maximum
+        x[2, 11] = top
+    if rows > 3:
+        x[3, :] = float("-inf")
+        x[3, V - 2] = -2.0                                # only finite logit in the last range
+    x = x.to(dtype)
+    runs = [gpu_confidence(x, mask_id, 0.5) for _ in range(3)]
+    pred, conf, over = runs[0]
+    for p2, c2, o2 in runs[1:]:
+        assert np.array_equal(p2, pred) and np.array_equal(c2.view(np.int32), conf.view(np.int32))
+        assert np.array_equal(o2, over)
+    rp, rc = decode.confidences(x.double().numpy(), mask_id)
+    assert np.array_equal(pred, rp), "predictions differ"
+    assert pred[0] == 3 * rnd // 2 + 9
+    if rows > 1:
+        assert pred[1] == rnd - 1
+    if rows > 2:
+        assert pred[2] == 11
+    if rows > 3:
+        assert pred[3] == V - 2 and conf[3] == pytest.approx(1.0, rel=1e-6)
+    rel = np.abs(conf - rc) / np.maximum(rc, 1e-30)
+    log("conf max rel err %.2e" % rel.max())
+    assert rel.max() <= 1e-5
+    assert np.array_equal(over.astype(bool), conf >= 0.5)
+
+
 def test_accept_matches_oracle():
     log("case: sequential acceptance")
     rng = np.random.default_rng(11)
