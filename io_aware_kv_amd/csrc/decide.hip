@@ -15,9 +15,10 @@
 //    loads, an online (max, sum of 2^(x - max)) over the whole vocabulary
 //    and the argmax over the non-[MASK] ids (ties to the lowest id); the
 //    confidence is that token's probability under the softmax over every id.
-//    A CU streams a row's misses at ~25 GB/s, so with fewer rows than CUs a
-//    row is cut into up to eight id ranges on separate workgroups; the last
-//    of them to finish merges the ranges' partial results in range order.
+//    With fewer rows than CUs a row is cut into up to eight id ranges on
+//    separate workgroups (each round of loads is a memory round trip the
+//    next round waits for); the last of them to finish merges the ranges'
+//    partial results.
 //  * accept_kernel: one lane per sequence walks its exploratory rows in
 //    decoding order.
 #include "fdllm_common.h"
@@ -26,7 +27,8 @@ namespace fdllm {
 
 namespace {
 
-constexpr int kConfThreads = 1024;
+constexpr int kConfThreads = 1024;   // threads of a workgroup that takes a whole row
+constexpr int kConfRangeThreads = 512;  // ... and of one that takes a range (two per CU)
 constexpr int kConfLoads = 4;        // 16-byte loads per thread per round
 constexpr int kConfMaxSplit = 8;     // id ranges per row at most
 constexpr int kConfSlots = 8192;     // rows of the per-device meeting table
@@ -140,11 +142,11 @@ __device__ __forceinline__ void take_round(Acc& a, u32x4 (&keep)[NL], const u32x
     }
 }
 
-// grid: rows x nsplit workgroups; workgroup (row, sp) takes ids
+// grid: rows x nsplit workgroups of NT threads; workgroup (row, sp) takes ids
 // [sp * rlen, min(V, (sp + 1) * rlen)) of its row; rlen is a multiple of
-// 1024 * NL * 16 / sizeof(T) ids unless nsplit == 1.
-template <typename T, int NL>
-__global__ void __launch_bounds__(kConfThreads) confidence_kernel(const T* __restrict__ logits, int V, int mask_id,
+// NT * NL * 16 / sizeof(T) ids unless nsplit == 1.
+template <typename T, int NL, int NT>
+__global__ void __launch_bounds__(NT) confidence_kernel(const T* __restrict__ logits, int V, int mask_id,
                                                                   float thr, int32_t* __restrict__ pred,
                                                                   float* __restrict__ conf, uint8_t* __restrict__ over,
                                                                   int nsplit, int rlen, unsigned slot0)
@@ -155,7 +157,7 @@ __global__ void __launch_bounds__(kConfThreads) confidence_kernel(const T* __res
     const T* x = logits + row * (size_t)V;
     Best b{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
     constexpr int PER = 16 / sizeof(T);                 // elements per 16-byte load
-    constexpr int US = kConfThreads * PER;              // id stride between a lane's loads
+    constexpr int US = NT * PER;                        // id stride between a lane's loads
     constexpr int RSTEP = US * NL;                      // ids per round of the workgroup
     const int tid = threadIdx.x;
     if ((V % PER) == 0) {
@@ -194,7 +196,7 @@ __global__ void __launch_bounds__(kConfThreads) confidence_kernel(const T* __res
             }
         }
     } else {
-        for (int v = lo + tid; v < hi; v += kConfThreads) take(b, to_f32(x[v]), v, mask_id);
+        for (int v = lo + tid; v < hi; v += NT) take(b, to_f32(x[v]), v, mask_id);
     }
     // workgroup merge: lanes, then waves through LDS
 #pragma unroll
@@ -206,44 +208,68 @@ __global__ void __launch_bounds__(kConfThreads) confidence_kernel(const T* __res
         o.bi = __shfl_xor(b.bi, off);
         b = merge(b, o);
     }
-    __shared__ Best sb[kConfThreads / 64];
+    constexpr int NW = NT / 64;
+    __shared__ Best sb[NW];
     if ((tid & 63) == 0) sb[tid >> 6] = b;
     __syncthreads();
-    if (tid != 0) return;
-    Best r = sb[0];
-    for (int w = 1; w < kConfThreads / 64; ++w) r = merge(r, sb[w]);
+    if (tid >= 64) return;
+    // wave 0 merges the waves' results over a fixed tree of lanes (lanes past
+    // the wave count hold the empty result)
+    const Best none{-INFINITY, 0.f, -INFINITY, 0x7fffffff};
+    Best r = tid < NW ? sb[tid] : none;
+#pragma unroll
+    for (int off = NW / 2; off >= 1; off >>= 1) {
+        Best o;
+        o.m = __shfl_xor(r.m, off);
+        o.s = __shfl_xor(r.s, off);
+        o.bl = __shfl_xor(r.bl, off);
+        o.bi = __shfl_xor(r.bi, off);
+        r = merge(r, o);
+    }
     if (nsplit > 1) {
         // Publish this range's result; the last range of the row to arrive
-        // merges all of them in range order, so the result does not depend
-        // on the arrival order.  The partials are written and read only as
+        // merges all of them over a fixed tree of lanes, so the result does
+        // not depend on the arrival order.  The partials are written and read only as
         // agent-scope atomics (coherent across the XCDs' L2s, no cached copy
         // to write back or invalidate), and the count is taken once those
         // stores have completed (vmcnt 0): the ordering an agent-scope
         // release gives, without its write-back of the whole L2 (measured
         // 1-3 us slower as a plain acquire-release count).
         const unsigned slot = (slot0 + (unsigned)row) % kConfSlots;
-        float* mine = (float*)&conf_part[slot * kConfMaxSplit + sp];
-        __hip_atomic_store(mine + 0, r.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(mine + 1, r.s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(mine + 2, r.bl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store((int*)mine + 3, r.bi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (tid == 0) {
+            float* mine = (float*)&conf_part[slot * kConfMaxSplit + sp];
+            __hip_atomic_store(mine + 0, r.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(mine + 1, r.s, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(mine + 2, r.bl, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store((int*)mine + 3, r.bi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        const unsigned done = __hip_atomic_fetch_add(&conf_count[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        unsigned done = 0;
+        if (tid == 0) done = __hip_atomic_fetch_add(&conf_count[slot], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        done = __shfl(done, 0);
         if (done != (unsigned)nsplit - 1) return;
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        auto part = [&](int k) {
-            const float* q = (const float*)&conf_part[slot * kConfMaxSplit + k];
-            Best t;
-            t.m = __hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            t.s = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            t.bl = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            t.bi = __hip_atomic_load((const int*)q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            return t;
-        };
-        r = part(0);
-        for (int k = 1; k < nsplit; ++k) r = merge(r, part(k));
-        __hip_atomic_store(&conf_count[slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // lane k takes range k's partial
+        r = none;
+        if (tid < nsplit) {
+            const float* q = (const float*)&conf_part[slot * kConfMaxSplit + tid];
+            r.m = __hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            r.s = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            r.bl = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            r.bi = __hip_atomic_load((const int*)q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+#pragma unroll
+        for (int off = kConfMaxSplit / 2; off >= 1; off >>= 1) {
+            Best o;
+            o.m = __shfl_xor(r.m, off);
+            o.s = __shfl_xor(r.s, off);
+            o.bl = __shfl_xor(r.bl, off);
+            o.bi = __shfl_xor(r.bi, off);
+            r = merge(r, o);
+        }
+        if (tid == 0) __hip_atomic_store(&conf_count[slot], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    if (tid != 0) return;
     // probability of the best non-[MASK] id under the softmax over all ids
     const float c = (r.bi == 0x7fffffff || !(r.s > 0.f)) ? 0.f : __builtin_amdgcn_exp2f(r.bl * kLog2e - r.m) / r.s;
     pred[row] = r.bi == 0x7fffffff ? -1 : r.bi;
@@ -271,28 +297,35 @@ hipError_t launch_confidence(const void* logits, int dtype, int64_t rows, int V,
                              int32_t* pred, float* conf, uint8_t* over, hipStream_t s)
 {
     if (rows == 0) return hipSuccess;
-    // with fewer rows than CUs, cut each row into up to eight ranges of
-    // whole rounds (at least one round each) so that about one row-range runs
-    // per CU; the ranges of a row meet in slots taken from a ticket
+    // With fewer rows than CUs, cut each row into up to eight ranges of
+    // whole rounds of 512-thread workgroups (two run per CU), so that up to
+    // two row-ranges run per CU at once; the ranges of a row meet in slots
+    // taken from a ticket.  Otherwise one 1024-thread workgroup per row.
     const int esz = dtype == 1 ? 2 : 4;
-    const int round_ids = kConfThreads * kConfLoads * (16 / esz);
+    const int round_ids = kConfRangeThreads * kConfLoads * (16 / esz);
     const int rounds = (V + round_ids - 1) / round_ids;
     int nsplit = 1;
-    while (nsplit < kConfMaxSplit && rows * nsplit * 2 <= 256 && nsplit * 2 <= rounds) nsplit *= 2;
-    int rlen = V;
-    unsigned slot0 = 0;
-    if (nsplit > 1) {
-        rlen = ((rounds + nsplit - 1) / nsplit) * round_ids;
-        static std::atomic<unsigned> ticket{0};
-        slot0 = ticket.fetch_add((unsigned)rows) % kConfSlots;
-    }
+    if (rows < 256)
+        while (nsplit < kConfMaxSplit && rows * nsplit * 2 <= 512 && nsplit * 2 <= rounds) nsplit *= 2;
     const dim3 grid((unsigned)(rows * nsplit));
+    if (nsplit == 1) {
+        if (dtype == 1)
+            hipLaunchKernelGGL((confidence_kernel<bf16, kConfLoads, kConfThreads>), grid, dim3(kConfThreads), 0, s,
+                               (const bf16*)logits, V, mask_id, thr, pred, conf, over, 1, V, 0u);
+        else
+            hipLaunchKernelGGL((confidence_kernel<float, kConfLoads, kConfThreads>), grid, dim3(kConfThreads), 0, s,
+                               (const float*)logits, V, mask_id, thr, pred, conf, over, 1, V, 0u);
+        return hipGetLastError();
+    }
+    const int rlen = ((rounds + nsplit - 1) / nsplit) * round_ids;
+    static std::atomic<unsigned> ticket{0};
+    const unsigned slot0 = ticket.fetch_add((unsigned)rows) % kConfSlots;
     if (dtype == 1)
-        hipLaunchKernelGGL((confidence_kernel<bf16, kConfLoads>), grid, dim3(kConfThreads), 0, s, (const bf16*)logits,
-                           V, mask_id, thr, pred, conf, over, nsplit, rlen, slot0);
+        hipLaunchKernelGGL((confidence_kernel<bf16, kConfLoads, kConfRangeThreads>), grid, dim3(kConfRangeThreads),
+                           0, s, (const bf16*)logits, V, mask_id, thr, pred, conf, over, nsplit, rlen, slot0);
     else
-        hipLaunchKernelGGL((confidence_kernel<float, kConfLoads>), grid, dim3(kConfThreads), 0, s,
-                           (const float*)logits, V, mask_id, thr, pred, conf, over, nsplit, rlen, slot0);
+        hipLaunchKernelGGL((confidence_kernel<float, kConfLoads, kConfRangeThreads>), grid, dim3(kConfRangeThreads),
+                           0, s, (const float*)logits, V, mask_id, thr, pred, conf, over, nsplit, rlen, slot0);
     return hipGetLastError();
 }
 

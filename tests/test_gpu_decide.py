@@ -121,36 +121,51 @@ def test_confidence_argmax_corner_rows(dtype, V):
     assert rel.max() <= 1e-5
 
 
+def row_ranges(rows, V, esz):
+    """The launch rule for rows of esz-byte logits: with fewer than 256 rows
+    a row is cut into up to eight ranges of whole rounds (512 threads x four
+    16-byte loads), while rows x ranges stays within two workgroups per CU."""
+    rid = 512 * 4 * (16 // esz)
+    rounds = -(-V // rid)
+    ns = 1
+    if rows < 256:
+        while ns < 8 and rows * ns * 2 <= 512 and ns * 2 <= rounds:
+            ns *= 2
+    return ns, (-(-rounds // ns)) * rid
+
+
 SPLIT_CASES = [
-    # (label, rows, V, dtype): rows few enough that each row is cut into id
-    # ranges (ranges of whole rounds of 1024 threads x four 16-byte loads)
-    ("bf16-4-ranges", 5, 131072, torch.bfloat16),     # rounds of 32768 ids
-    ("bf16-2-ranges", 128, 131072, torch.bfloat16),
-    ("f32-8-ranges", 3, 131072, torch.float32),       # rounds of 16384 ids
-    ("f32-ragged", 2, 131072 - 4, torch.float32),     # last range short
-    ("bf16-ragged-scalar", 4, 70001, torch.bfloat16), # V not a multiple of 8: element loads
+    # (label, rows, V, dtype)
+    ("bf16-8-ranges", 5, 131072, torch.bfloat16),
+    ("bf16-128-rows-4-ranges", 128, 131072, torch.bfloat16),
+    ("bf16-200-rows-2-ranges", 200, 131072, torch.bfloat16),
+    ("f32-8-ranges", 3, 131072, torch.float32),
+    ("f32-ragged", 2, 131072 - 4, torch.float32),      # last range short
+    ("bf16-ragged-scalar", 4, 70001, torch.bfloat16),  # V not a multiple of 8: element loads; last range empty
 ]
 
 
 @pytest.mark.parametrize("label,rows,V,dtype", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
 def test_confidence_rows_split_over_workgroups(label, rows, V, dtype):
-    """Few rows: each row's ids are cut into ranges on separate workgroups and
-    the last range to finish merges them.  Corner rows put equal maxima in
-    different ranges (the lowest id wins), the maximum on both sides of a
-    range boundary, the [MASK] id holding the maximum in a later range, and a
-    row whose only finite logit sits in the last range.  Three calls in a row
-    (the meeting slots must be back at zero) give the same bits."""
+    """Fewer rows than CUs: each row's ids are cut into ranges on separate
+    workgroups and the last range to finish merges them.  Corner rows put
+    equal maxima in different ranges (the lowest id wins), the maximum on both
+    sides of a range boundary, the [MASK] id holding the maximum in a later
+    range, and a row whose only finite logit sits in the last range.  Three
+    calls in a row (the meeting slots must be back at zero) give the same
+    bits."""
     log("case: confidence split rows %s" % label)
-    e = 16 // (4 if dtype == torch.float32 else 2)
-    rnd = 1024 * 4 * e                                    # ids per round
+    ns, rlen = row_ranges(rows, V, 4 if dtype == torch.float32 else 2)
+    assert ns > 1
     x = decision_logits(rows, V, seed=V + rows, dtype=torch.float32)
     top = float(x.max()) + 1.0
-    mask_id = min(rnd + 77, V - 1)
-    x[0, 3 * rnd // 2 + 9] = top                           # equal maxima in two ranges: the lower id wins
+    mask_id = min(2 * rlen + 77, V - 1)
+    first = rlen + rlen // 2 + 9
+    x[0, first] = top                                     # equal maxima in two ranges: the lower id wins
     x[0, V - 5] = top
     if rows > 1:
-        x[1, rnd - 1] = top                               # last id of a range ...
-        x[1, rnd] = top                                   # ... and the first of the next: rnd - 1 wins
+        x[1, rlen - 1] = top                              # last id of a range ...
+        x[1, rlen] = top                                  # ... and the first of the next: rlen - 1 wins
     if rows > 2:
         x[2, mask_id] = top + 3.0                         # [MASK] holds the maximum
         x[2, 11] = top
@@ -165,15 +180,15 @@ def test_confidence_rows_split_over_workgroups(label, rows, V, dtype):
         assert np.array_equal(o2, over)
     rp, rc = decode.confidences(x.double().numpy(), mask_id)
     assert np.array_equal(pred, rp), "predictions differ"
-    assert pred[0] == 3 * rnd // 2 + 9
+    assert pred[0] == first
     if rows > 1:
-        assert pred[1] == rnd - 1
+        assert pred[1] == rlen - 1
     if rows > 2:
         assert pred[2] == 11
     if rows > 3:
         assert pred[3] == V - 2 and conf[3] == pytest.approx(1.0, rel=1e-6)
     rel = np.abs(conf - rc) / np.maximum(rc, 1e-30)
-    log("conf max rel err %.2e" % rel.max())
+    log("%d ranges of %d ids, conf max rel err %.2e" % (ns, rlen, rel.max()))
     assert rel.max() <= 1e-5
     assert np.array_equal(over.astype(bool), conf >= 0.5)
 
