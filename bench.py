@@ -208,7 +208,9 @@ def time_selection(fk, wl, sets, stream, iters):
 def time_decision(wl, stream, iters):
     """Time the draft-pass decisions for the step's masked rows over the
     synthetic vocabulary: per-row prediction and confidence with the eps
-    split, then the sequential acceptance over the same rows."""
+    split, then the sequential acceptance over the same rows, each call
+    repeated back to back on the stream (the acceptance kernel is shorter
+    than a host call, so its figure is the call rate)."""
     import torch
     from io_aware_kv_amd import binding
     from io_aware_kv_amd.workloads import SYNTH_VOCAB, decision_logits, selection_inputs
