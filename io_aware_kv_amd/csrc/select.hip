@@ -711,7 +711,8 @@ __device__ __forceinline__ int top_scan(int x, int* sTmp, int& total)
 // One workgroup per sequence.  Candidate p has the key (ordered score bits,
 // then the inverted position), so larger keys rank first and equal scores
 // rank the lower position first.  The k-th largest score bits come from a
-// radix select (four 8-bit passes over per-wave LDS histograms); the
+// radix select (four 8-bit passes over per-wave LDS histograms, three
+// barriers a pass); the
 // candidates above it, and the lowest-position ones equal to it, are
 // compacted in position order and only those (a power of two >= min(k, N)
 // slots) are sorted with a bitonic network in LDS.
@@ -726,15 +727,19 @@ __global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __
     uint32_t* sU = (uint32_t*)smem;
     uint32_t* sValid = sU + ((N + 3) & ~3);
     uint64_t* key = (uint64_t*)smem;
-    __shared__ int sHist[kTopWaves][256];
+    // per-wave histograms, two sets used by alternate radix passes: one pass
+    // clears the next pass's set while it reduces its own, so a pass needs
+    // three barriers
+    __shared__ int sHist[2][kTopWaves][256];
     __shared__ int sTmp[kTopWaves + 1];
-    __shared__ int sBin, sNeed, sCount;
+    __shared__ int sBin[2], sNeed[2], sCount;
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* sc = scores + (size_t)b * N;
     const uint8_t* cd = cand + (size_t)b * N;
 
     if (tid == 0) sCount = 0;
+    for (int t = tid; t < kTopWaves * 256; t += kTopThreads) (&sHist[0][0][0])[t] = 0;
     __syncthreads();
     int cnt = 0;   // candidates seen by this wave
     for (int base = 0; base < N; base += kTopThreads) {
@@ -770,18 +775,37 @@ __global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __
     if (C > k) {
         uint32_t pmask = 0u;
         need = k;
-        for (int shift = 24; shift >= 0; shift -= 8) {
-            for (int t = tid; t < kTopWaves * 256; t += kTopThreads) (&sHist[0][0])[t] = 0;
-            __syncthreads();
+        for (int shift = 24, par = 0; shift >= 0; shift -= 8, par ^= 1) {
+            // sHist[par] was cleared before the first pass or during the pass
+            // before this one.  A thread counts runs of equal digits among its
+            // positions and adds each run once: the first pass (sign and
+            // exponent bits) puts nearly every key in a few bins, where one
+            // LDS atomic per key would serialise.
+            int rb = -1, rc = 0;
 #pragma unroll
-            for (int i = 0; i < kTopPer; ++i)
-                if (((valid >> i) & 1u) && (u[i] & pmask) == thr) atomicAdd(&sHist[wave][(u[i] >> shift) & 255u], 1);
+            for (int i = 0; i < kTopPer; ++i) {
+                if (((valid >> i) & 1u) && (u[i] & pmask) == thr) {
+                    const int bin = (int)((u[i] >> shift) & 255u);
+                    if (bin != rb) {
+                        if (rc) atomicAdd(&sHist[par][wave][rb], rc);
+                        rb = bin;
+                        rc = 1;
+                    } else {
+                        ++rc;
+                    }
+                }
+            }
+            if (rc) atomicAdd(&sHist[par][wave][rb], rc);
             __syncthreads();
             if (tid < 256) {
                 int h = 0;
 #pragma unroll
-                for (int w = 0; w < kTopWaves; ++w) h += sHist[w][tid];
-                sHist[0][tid] = h;
+                for (int w = 0; w < kTopWaves; ++w) h += sHist[par][w][tid];
+                sHist[par][0][tid] = h;
+            } else if (shift > 0) {
+                // the next pass's set: its last reads (the bin choice of the
+                // pass before this one) ended before this pass's first barrier
+                for (int t = tid - 256; t < kTopWaves * 256; t += kTopThreads - 256) (&sHist[par ^ 1][0][0])[t] = 0;
             }
             __syncthreads();
             if (wave == 0) {
@@ -789,7 +813,7 @@ __global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __
                 int c[4], s4 = 0;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    c[j] = sHist[0][255 - 4 * lane - j];
+                    c[j] = sHist[par][0][255 - 4 * lane - j];
                     s4 += c[j];
                 }
                 int incl = s4;
@@ -809,46 +833,48 @@ __global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __
                         }
                         acc += c[j];
                     }
-                    sBin = bin;
-                    sNeed = rest;
+                    sBin[par] = bin;
+                    sNeed[par] = rest;
                 }
             }
             __syncthreads();
-            thr |= (uint32_t)sBin << shift;
+            // sBin[par] is written again two passes on, after barriers every
+            // thread reaches only once it has read it here
+            thr |= (uint32_t)sBin[par] << shift;
             pmask |= 255u << shift;
-            need = sNeed;
-            __syncthreads();
+            need = sNeed[par];
         }
     }
 
     // the selected candidates, compacted in position order: all of them when
     // there are at most k, else those above the threshold and the first
-    // `need` equal to it
-    uint32_t sel = valid;
+    // `need` equal to it.  One scan gives both counts before each thread
+    // (above in the low 16 bits, equal in the high; N <= 16384): the keys
+    // selected before a thread are the ones above plus min(equal, need).
+    uint32_t above = valid, tie = 0u;
     if (C > k) {
-        uint32_t tie = 0u;
-#pragma unroll
-        for (int i = 0; i < kTopPer; ++i) tie |= ((((valid >> i) & 1u) && u[i] == thr) ? 1u : 0u) << i;
-        int ntie;
-        int r = top_scan(__builtin_popcount(tie), sTmp, ntie);
-        sel = 0u;
+        above = 0u;
 #pragma unroll
         for (int i = 0; i < kTopPer; ++i) {
             const bool v = (valid >> i) & 1u;
-            const bool t = (tie >> i) & 1u;
-            const bool take = v && (u[i] > thr || (t && r < need));
-            r += t ? 1 : 0;
-            sel |= (take ? 1u : 0u) << i;
+            above |= ((v && u[i] > thr) ? 1u : 0u) << i;
+            tie |= ((v && u[i] == thr) ? 1u : 0u) << i;
         }
     }
-    int nsel;
-    int w = top_scan(__builtin_popcount(sel), sTmp, nsel);
+    int tot;
+    const int pre = top_scan((__builtin_popcount(tie) << 16) | __builtin_popcount(above), sTmp, tot);
+    const int nsel = (tot & 0xffff) + min(tot >> 16, need);
+    int w = (pre & 0xffff) + min(pre >> 16, need);
+    int r = pre >> 16;                                  // equal keys before this position
 #pragma unroll
-    for (int i = 0; i < kTopPer; ++i)
-        if ((sel >> i) & 1u) {
+    for (int i = 0; i < kTopPer; ++i) {
+        const bool t = (tie >> i) & 1u;
+        if (((above >> i) & 1u) || (t && r < need)) {
             const uint32_t p = (uint32_t)(tid * kTopPer + i);
             key[w++] = ((uint64_t)u[i] << 32) | (uint64_t)(0xffffffffu - p);
         }
+        r += t ? 1 : 0;
+    }
     for (int t = nsel + tid; t < n2; t += kTopThreads) key[t] = 0;   // padding sorts last
     __syncthreads();
     if (n2 <= 256) {
