@@ -711,11 +711,11 @@ __device__ __forceinline__ int top_scan(int x, int* sTmp, int& total)
 // One workgroup per sequence.  Candidate p has the key (ordered score bits,
 // then the inverted position), so larger keys rank first and equal scores
 // rank the lower position first.  The k-th largest score bits come from a
-// radix select (four 8-bit passes over per-wave LDS histograms, three
-// barriers a pass); the
-// candidates above it, and the lowest-position ones equal to it, are
-// compacted in position order and only those (a power of two >= min(k, N)
-// slots) are sorted with a bitonic network in LDS.
+// radix select (up to four 8-bit passes over per-wave LDS histograms, three
+// barriers a pass; it stops early once every key of the chosen bin is
+// taken); the candidates above it, and the lowest-position ones equal to it,
+// are compacted in position order and only those (a power of two >=
+// min(k, N) slots) are ranked in LDS.
 __global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __restrict__ scores,
                                                                  const uint8_t* __restrict__ cand, int N, int n2,
                                                                  int k, int32_t* __restrict__ out)
@@ -732,7 +732,7 @@ __global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __
     // three barriers
     __shared__ int sHist[2][kTopWaves][256];
     __shared__ int sTmp[kTopWaves + 1];
-    __shared__ int sBin[2], sNeed[2], sCount;
+    __shared__ int sBin[2], sNeed[2], sAll[2], sCount;
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const float* sc = scores + (size_t)b * N;
@@ -770,10 +770,10 @@ __global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __
 
     // threshold: the k-th largest score bits among the candidates (when there
     // are more than k), and how many candidates equal to it are taken
-    uint32_t thr = 0u;
+    uint32_t thr = 0u, pmask = ~0u;
     int need = 0;
     if (C > k) {
-        uint32_t pmask = 0u;
+        pmask = 0u;
         need = k;
         for (int shift = 24, par = 0; shift >= 0; shift -= 8, par ^= 1) {
             // sHist[par] was cleared before the first pass or during the pass
@@ -824,17 +824,19 @@ __global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __
                 }
                 const int excl = incl - s4;
                 if (excl < need && need <= incl) {
-                    int acc = excl, bin = -1, rest = 0;
+                    int acc = excl, bin = -1, rest = 0, all = 0;
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         if (bin < 0 && acc + c[j] >= need) {
                             bin = 255 - 4 * lane - j;
                             rest = need - acc;
+                            all = c[j] == rest;
                         }
                         acc += c[j];
                     }
                     sBin[par] = bin;
                     sNeed[par] = rest;
+                    sAll[par] = all;
                 }
             }
             __syncthreads();
@@ -843,6 +845,9 @@ __global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __
             thr |= (uint32_t)sBin[par] << shift;
             pmask |= 255u << shift;
             need = sNeed[par];
+            // every key of the bin is taken: the digits below need not be
+            // known (the selection then compares the known digits only)
+            if (sAll[par]) break;
         }
     }
 
@@ -857,8 +862,8 @@ __global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __
 #pragma unroll
         for (int i = 0; i < kTopPer; ++i) {
             const bool v = (valid >> i) & 1u;
-            above |= ((v && u[i] > thr) ? 1u : 0u) << i;
-            tie |= ((v && u[i] == thr) ? 1u : 0u) << i;
+            above |= ((v && (u[i] & pmask) > thr) ? 1u : 0u) << i;
+            tie |= ((v && (u[i] & pmask) == thr) ? 1u : 0u) << i;
         }
     }
     int tot;

@@ -163,6 +163,7 @@ TOPK_CASES = [
     ("k-one", 4, 2048, 1, "ties"),
     ("k-256", 2, 4096, 256, "ties"),           # the rank-count sort's largest slot count
     ("k-257", 1, 4096, 257, "ties"),           # one past it: the bitonic network
+    ("first-digit-decides", 2, 3000, 5, "spikes"),  # each of the top 5 alone in its first-pass bin
 ]
 
 
@@ -170,7 +171,8 @@ TOPK_CASES = [
 def test_select_top_edge_cases(label, B, N, k, pattern):
     """The top-k against the oracle's ranking of the same fp32 scores: k at
     or past the candidate count, the largest N, N not a multiple of 16, a
-    single candidate, every score equal, negative scores and signed zeros."""
+    single candidate, every score equal, negative scores and signed zeros,
+    and a k-th score that the first radix digit already separates."""
     log("case: top-k %s" % label)
     rng = np.random.default_rng(44 + N + k)
     if pattern == "random":
@@ -186,6 +188,14 @@ def test_select_top_edge_cases(label, B, N, k, pattern):
     else:
         sc = rng.standard_normal((B, N)).astype(np.float32)
     cand = (rng.random((B, N)) < 0.6).astype(np.uint8)
+    if pattern == "spikes":
+        # scores 2^10, 2^14, ..., 2^26 fall in separate bins of the first
+        # radix digit (sign and high exponent bits), so the select can stop
+        # after one pass
+        sc = (rng.standard_normal((B, N)) * 0.1).astype(np.float32)
+        for j, p in enumerate((17, 2999, 1500, 4, 777)):
+            sc[:, p] = np.float32(2.0 ** (10 + 4 * j))
+            cand[:, p] = 1
     if pattern == "one":
         cand[:] = 0
         cand[:, N // 3] = 1
