@@ -884,9 +884,8 @@ __global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __
     __syncthreads();
     if (n2 <= 256) {
         // up to 256 keys (all distinct): the rank of a key is the number of
-        // larger keys, counted by 1024 / n2 threads per key; each key then
-        // goes to its rank
-        // (a power-of-two group of lanes of one wave per key)
+        // larger keys, counted by 1024 / n2 threads per key (a power-of-two
+        // group of lanes of one wave per key)
         const int tpk = min(min(n2, kTopThreads / n2), 64), per = n2 / tpk;
         const int i = tid / tpk, sub = tid - i * tpk;
         const bool live = i < n2;
@@ -895,12 +894,16 @@ __global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __
         if (live)
             for (int j = sub * per; j < (sub + 1) * per; ++j) rank += key[j] > mine ? 1 : 0;
         for (int o = 1; o < tpk; o <<= 1) rank += __shfl_xor(rank, o);
-        __syncthreads();
-        if (live && sub == 0) key[rank] = mine;
-        __syncthreads();
+        // the keys are distinct, so their ranks are 0 .. nsel - 1: each real
+        // key's position goes straight to its output slot, the slots past
+        // nsel get -1
+        if (live && sub == 0 && i < nsel)
+            out[(size_t)b * k + rank] = (int32_t)(0xffffffffu - (uint32_t)(mine & 0xffffffffu));
+        for (int t = nsel + tid; t < k; t += kTopThreads) out[(size_t)b * k + t] = -1;
+        return;
     }
     // bitonic network over the n2 slots, descending overall (more than 256)
-    for (int size = 2; n2 > 256 && size <= n2; size <<= 1) {
+    for (int size = 2; size <= n2; size <<= 1) {
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
             for (int t = tid; t < n2 / 2; t += kTopThreads) {
                 const int lo = 2 * t - (t & (stride - 1));
