@@ -721,16 +721,12 @@ __global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __
                                                                  int k, int32_t* __restrict__ out)
 {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-    // first the scores as order-preserving bits [N] and the candidate flags
-    // as bit words [N / 32], loaded coalesced; later, in the same space, the
-    // selected keys [n2]
-    uint32_t* sU = (uint32_t*)smem;
-    uint32_t* sValid = sU + ((N + 3) & ~3);
-    uint64_t* key = (uint64_t*)smem;
-    // per-wave histograms, two sets used by alternate radix passes: one pass
+    // per-wave histograms, two sets used by alternate radix passes (one pass
     // clears the next pass's set while it reduces its own, so a pass needs
-    // three barriers
-    __shared__ int sHist[2][kTopWaves][256];
+    // three barriers); after the radix select the same space holds the
+    // selected keys [n2]
+    int (*sHist)[kTopWaves][256] = (int (*)[kTopWaves][256])smem;
+    uint64_t* key = (uint64_t*)smem;
     __shared__ int sTmp[kTopWaves + 1];
     __shared__ int sBin[2], sNeed[2], sAll[2], sCount;
     const int b = blockIdx.x;
@@ -741,31 +737,30 @@ __global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __
     if (tid == 0) sCount = 0;
     for (int t = tid; t < kTopWaves * 256; t += kTopThreads) (&sHist[0][0][0])[t] = 0;
     __syncthreads();
-    int cnt = 0;   // candidates seen by this wave
-    for (int base = 0; base < N; base += kTopThreads) {
-        const int p = base + tid;
-        const bool in = p < N && cd[min(p, N - 1)] != 0;
-        if (p < N) sU[p] = ordered_bits(sc[p]);
-        const uint64_t m = __builtin_amdgcn_ballot_w64(in);
-        cnt += __builtin_popcountll(m);
-        if (lane == 0) {
-            const int w0 = (base + wave * 64) >> 5;
-            if (base + wave * 64 < N) sValid[w0] = (uint32_t)m;
-            if (base + wave * 64 + 32 < N) sValid[w0 + 1] = (uint32_t)(m >> 32);
-        }
-    }
-    if (lane == 0) atomicAdd(&sCount, cnt);
-    __syncthreads();
-    // each thread then takes kTopPer consecutive positions
+    // each thread takes kTopPer consecutive positions straight from memory
+    // (all its loads in flight at once; positions past N are not valid)
     uint32_t u[kTopPer];
     uint32_t valid = 0u;
-    {
-        const int p0 = tid * kTopPer;
-        if (p0 < N) valid = (sValid[p0 >> 5] >> (p0 & 31)) & 0xffffu;
-        if (p0 + kTopPer > N) valid &= p0 >= N ? 0u : (1u << (N - p0)) - 1u;
+    const int p0 = tid * kTopPer;
+    if (p0 + kTopPer <= N) {
 #pragma unroll
-        for (int i = 0; i < kTopPer; ++i) u[i] = sU[min(p0 + i, N - 1)];
+        for (int i = 0; i < kTopPer; ++i) {
+            u[i] = ordered_bits(sc[p0 + i]);
+            valid |= (cd[p0 + i] != 0 ? 1u : 0u) << i;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < kTopPer; ++i) {
+            const bool in = p0 + i < N;
+            u[i] = in ? ordered_bits(sc[p0 + i]) : 0u;
+            valid |= ((in && cd[p0 + i] != 0) ? 1u : 0u) << i;
+        }
     }
+    int cnt = __builtin_popcount(valid);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o);
+    if (lane == 0) atomicAdd(&sCount, cnt);
+    __syncthreads();
     const int C = sCount;
 
     // threshold: the k-th largest score bits among the candidates (when there
@@ -1004,8 +999,7 @@ hipError_t launch_select_top(const float* scores, const uint8_t* cand, int B, in
     const int m = std::min(k, N);
     int n2 = 1;
     while (n2 < m) n2 <<= 1;
-    const size_t staged = (size_t)((N + 3) & ~3) * 4 + (size_t)((N + 31) / 32) * 4;
-    const size_t shm = std::max((size_t)n2 * sizeof(uint64_t), staged);
+    const size_t shm = std::max((size_t)n2 * sizeof(uint64_t), (size_t)2 * kTopWaves * 256 * sizeof(int));
     (void)allow_full_lds<select_top_kernel>();
     (void)hipGetLastError();
     hipLaunchKernelGGL(select_top_kernel, dim3(B), dim3(kTopThreads), shm, s, scores, cand, N, n2, k, out);

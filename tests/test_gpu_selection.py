@@ -164,6 +164,7 @@ TOPK_CASES = [
     ("k-256", 2, 4096, 256, "ties"),           # the rank-count sort's largest slot count
     ("k-257", 1, 4096, 257, "ties"),           # one past it: the bitonic network
     ("first-digit-decides", 2, 3000, 5, "spikes"),  # each of the top 5 alone in its first-pass bin
+    ("k-9000-of-max-N", 1, 16384, 9000, "random"),  # 16384 key slots: the most LDS the kernel takes
 ]
 
 
