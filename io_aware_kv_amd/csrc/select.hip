@@ -654,7 +654,15 @@ __global__ void __launch_bounds__(256) key_mass_sum_kernel(const float* __restri
     const float* src = part + b * Hkv * (size_t)N + p;
     float s = 0.f;
     int g = 0;
-    // eight loads in flight, added in head order
+    // up to 32 loads in flight (one memory round trip for 32 kv heads),
+    // added in head order
+    for (; g + 32 <= Hkv; g += 32) {
+        float v[32];
+#pragma unroll
+        for (int u = 0; u < 32; ++u) v[u] = src[(size_t)(g + u) * N];
+#pragma unroll
+        for (int u = 0; u < 32; ++u) s += v[u];
+    }
     for (; g + 8 <= Hkv; g += 8) {
         float v[8];
 #pragma unroll
