@@ -193,6 +193,35 @@ def test_confidence_rows_split_over_workgroups(label, rows, V, dtype):
     assert np.array_equal(over.astype(bool), conf >= 0.5)
 
 
+def test_confidence_split_calls_on_two_streams():
+    """Split-row calls in flight together on two streams meet in separate
+    slots of the library's table: interleaved calls on two streams, with no
+    ordering between them, give the bits of the same calls made one by one."""
+    log("case: confidence split rows on two streams")
+    dev = torch.device("cuda")
+    xs = [decision_logits(24, 131072, seed=900 + i).to(dev) for i in range(4)]
+    want = [gpu_confidence(x, 126, 0.5) for x in xs]
+    streams = [torch.cuda.Stream(device=dev), torch.cuda.Stream(device=dev)]
+    outs = []
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, x in enumerate(xs):
+            st = streams[i % 2]
+            pred = torch.full((24,), -7, dtype=torch.int32, device=dev)
+            conf = torch.full((24,), float("nan"), dtype=torch.float32, device=dev)
+            over = torch.full((24,), 7, dtype=torch.uint8, device=dev)
+            # the output fills were made on the current stream: order them
+            st.wait_stream(torch.cuda.current_stream())
+            binding.confidence(x, 126, 0.5, pred, conf, over, stream=st)
+            outs.append((i, pred, conf, over))
+    torch.cuda.synchronize()
+    for i, pred, conf, over in outs:
+        wp, wc, wo = want[i]
+        assert np.array_equal(pred.cpu().numpy(), wp)
+        assert np.array_equal(conf.cpu().numpy().view(np.int32), wc.view(np.int32))
+        assert np.array_equal(over.cpu().numpy(), wo)
+
+
 def test_accept_matches_oracle():
     log("case: sequential acceptance")
     rng = np.random.default_rng(11)
