@@ -159,8 +159,9 @@ def cpu_oracle_baseline(wl, K0, V0, budget_s):
 
 def time_selection(fk, wl, sets, stream, iters):
     """Time the tracked-set scores and the top-k selection that follow the
-    step (beta_t = 80), over the rotating buffer sets; the handle's q staging
-    holds the last step's q, and every set carries the same step inputs."""
+    step (beta_t = 80), over the rotating buffer sets, each call repeated back
+    to back on the stream; the handle's q staging holds the last step's q, and
+    every set carries the same step inputs."""
     import torch
     from io_aware_kv_amd.workloads import selection_inputs
     ls = wl.shape
@@ -172,26 +173,28 @@ def time_selection(fk, wl, sets, stream, iters):
     scores = [torch.empty((ls.B, ls.N), dtype=torch.float32, device=dev) for _ in range(n)]
     outs = [torch.empty((ls.B, k), dtype=torch.int32, device=dev) for _ in range(n)]
 
-    def run(i, evs=None):
+    def scores_call(i):
         st = sets[i % n]
-        if evs is not None:
-            evs[0].record(stream)
         fk.tracked_scores(st["P"], st["vis"], sel_d, st["Kc"], st["LSE"], scores[i % n], stream=stream)
-        if evs is not None:
-            evs[1].record(stream)
-        fk.select_tracked(scores[i % n], cand_d, k, outs[i % n], stream=stream)
-        if evs is not None:
-            evs[2].record(stream)
 
-    for i in range(3):
-        run(i)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(iters)]
-    for i in range(iters):
-        run(i, evs[i])
-    torch.cuda.synchronize()
-    sc_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / iters
-    tk_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / iters
+    def select_call(i):
+        fk.select_tracked(scores[i % n], cand_d, k, outs[i % n], stream=stream)
+
+    def timed(call):
+        # back to back on the stream, one event pair around all the calls
+        for i in range(3):
+            call(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(iters):
+            call(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    sc_ms = timed(scores_call)
+    tk_ms = timed(select_call)
     elt = 2 if ls.dtype == torch.bfloat16 else 4
     G = ls.H // ls.Hkv
     nsel = int(sel.sum())
