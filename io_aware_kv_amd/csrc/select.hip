@@ -685,27 +685,33 @@ constexpr int kTopThreads = 1024;
 constexpr int kTopWaves = kTopThreads / 64;
 constexpr int kTopPer = 16;           // consecutive positions per thread (N <= 16384)
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no trip
+// through LDS as a lane shuffle would take): shifts by 1, 2, 4, 8 inside each
+// row of 16 lanes (lanes shifted in from outside the row add 0), then the last
+// lane of row 0 added to row 1, and of row 2 to row 3, then the last lane of
+// row 1 added to rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int x)
+{
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);   // row_bcast:15 into rows 1, 3
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);   // row_bcast:31 into rows 2, 3
+    return x;
+}
+
 // Exclusive prefix sum of x over the workgroup in thread order; `total` gets
 // the sum.  sTmp holds kTopWaves + 1 ints.
 __device__ __forceinline__ int top_scan(int x, int* sTmp, int& total)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = x;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o);
-        if (lane >= o) incl += y;
-    }
+    const int incl = wave_incl_scan(x);
     if (lane == 63) sTmp[wave] = incl;
     __syncthreads();
     if (wave == 0) {
         const int w = lane < kTopWaves ? sTmp[lane] : 0;
-        int wi = w;
-#pragma unroll
-        for (int o = 1; o < kTopWaves; o <<= 1) {
-            const int y = __shfl_up(wi, o);
-            if (lane >= o) wi += y;
-        }
+        const int wi = wave_incl_scan(w);
         if (lane < kTopWaves) sTmp[lane] = wi - w;
         if (lane == kTopWaves - 1) sTmp[kTopWaves] = wi;
     }
@@ -819,12 +825,7 @@ __global__ void __launch_bounds__(kTopThreads) select_top_kernel(const float* __
                     c[j] = sHist[par][0][255 - 4 * lane - j];
                     s4 += c[j];
                 }
-                int incl = s4;
-#pragma unroll
-                for (int o = 1; o < 64; o <<= 1) {
-                    const int y = __shfl_up(incl, o);
-                    if (lane >= o) incl += y;
-                }
+                const int incl = wave_incl_scan(s4);
                 const int excl = incl - s4;
                 if (excl < need && need <= incl) {
                     int acc = excl, bin = -1, rest = 0, all = 0;
