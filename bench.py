@@ -522,6 +522,45 @@ def run_probes(args):
                       "lds_dma_l2_resident": dma, "hbm_peak_GBps": HBM_PEAK_GBPS}))
 
 
+def run_decisions(args):
+    """The decision kernel over the synthetic vocabulary (131,072 seeded bf16
+    logits per row) at several row counts: below the CU count each row is
+    spread over id ranges, from 256 rows on every row has its own workgroup.
+    Each count is timed over 50 calls back to back (two buffers alternated, so
+    no call finds its rows cached); one JSON line with the per-count times and
+    rates."""
+    import torch
+    from io_aware_kv_amd import binding
+    from io_aware_kv_amd.workloads import SYNTH_VOCAB, decision_logits
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    stream = torch.cuda.current_stream()
+    V = SYNTH_VOCAB
+    res = {}
+    for rows in (1, 8, 32, 64, 128, 256, 512, 1024):
+        host = decision_logits(rows, V, seed=rows)
+        bufs = [host.to(dev) for _ in range(2)]
+        pred = torch.empty((rows,), dtype=torch.int32, device=dev)
+        conf = torch.empty((rows,), dtype=torch.float32, device=dev)
+        over = torch.empty((rows,), dtype=torch.uint8, device=dev)
+        for i in range(3):
+            binding.confidence(bufs[i % 2], 126, 0.9, pred, conf, over, stream=stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        iters = 50
+        e0.record(stream)
+        for i in range(iters):
+            binding.confidence(bufs[i % 2], 126, 0.9, pred, conf, over, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / iters * 1e3
+        nbytes = rows * V * 2 + rows * 9
+        res[str(rows)] = {"confidence_us": round(us, 3), "GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+        log("bench: decisions, %d rows: %.2f us (%.0f GB/s)" % (rows, us, nbytes / (us * 1e-6) / 1e9))
+        del bufs
+    print(json.dumps({"mode": "decisions", "vocab": V, "dtype": "bf16", "rows": res}))
+
+
 def run_stack(args):
     """The large-batch workload as a whole stack: --layers consecutive layers
     (32 by default), each with its own weights and its own K/V cache in HBM,
@@ -585,7 +624,7 @@ def main():
     ap.add_argument("--attn-splits", type=int, default=0)
     ap.add_argument("--gemm-splitk", type=int, default=0)
     ap.add_argument("--proj-tile", type=int, default=0, help="projection tile choice override (0: the library's)")
-    ap.add_argument("--mode", default="step", choices=["step", "copy", "stream", "probes", "stack"])
+    ap.add_argument("--mode", default="step", choices=["step", "copy", "stream", "probes", "stack", "decisions"])
     ap.add_argument("--layers", type=int, default=32, help="--mode stack: layers of the large-batch stack")
     ap.add_argument("--copy-bytes", type=int, default=1 << 30)
     args = ap.parse_args()
@@ -604,6 +643,8 @@ def main():
         return run_probes(args)
     if args.mode == "stack":
         return run_stack(args)
+    if args.mode == "decisions":
+        return run_decisions(args)
 
     from io_aware_kv_amd.workloads import make_workload
 
